@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Throughput of the folded multi-branch verify layer on one MI355X.
+
+A step is one complete verify layer (gate, provenance, packing, packed QKV GEMM, prefix
+and block attention with per-branch correction, O projection, packed SwiGLU FFN,
+combine) over the parent and all draft branches of one synthetic block, with every
+input already resident in HBM.  The default workload is the 7B-shaped layer (hidden
+3584, 28/4 heads x 128, FFN 18944, prefix 512, block 32, a 3-ary draft tree of
+1 + 15 nodes, tau = 0.05).  `value` is branch-tokens verified per second per layer
+(N*B slots per step); `us_per_verify_layer` is the same number as latency.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.  --report PATH writes
+the extended results (per-kernel times, tau sweep) as JSON."""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, public spec
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, public spec
+FP32_PEAK_TFLOPS = 157.3       # dense fp32
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t helpers from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so.7")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        assert self.h.hipEventRecord(ev, stream) == 0
+
+    def ms(self, a, b):
+        assert self.h.hipEventSynchronize(b) == 0
+        v = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(v), a, b) == 0
+        return v.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.h.hipEventDestroy(e)
+
+
+def algorithmic(cfg, K):
+    """Bytes and flops each kernel must move/compute per launch (weights read once, packed
+    rows only, prefix read once per KV head)."""
+    eb = 2 if cfg.dtype == "bf16" else 4
+    d, ff, dh, nq, nkv, S, P, B = (cfg.hidden, cfg.ffn, cfg.head_dim, cfg.n_q, cfg.n_kv,
+                                   cfg.slots, cfg.prefix, cfg.block)
+    qkvd = cfg.qkv_dim
+    g = nq // nkv
+    out = {
+        "gate": dict(bytes=2 * S * d * eb + S * 5, flops=4 * S * d),
+        "qkv": dict(bytes=qkvd * d * eb + K * d * eb + K * qkvd * eb, flops=2 * K * d * qkvd),
+        "attn_prefix": dict(bytes=2 * P * nkv * dh * eb + K * nq * dh * eb,
+                            flops=4 * K * nq * P * dh),
+        "attn_block": dict(bytes=K * qkvd * eb + S * nq * dh * eb, flops=4 * S * nq * B * dh),
+        "o_proj": dict(bytes=d * nq * dh * eb + 2 * S * d * eb + S * nq * dh * eb,
+                       flops=2 * S * nq * dh * d),
+        "ffn_gate_up": dict(bytes=2 * ff * d * eb + K * d * eb + K * ff * eb,
+                            flops=2 * K * d * 2 * ff),
+        "ffn_down": dict(bytes=d * ff * eb + K * ff * eb + K * d * eb, flops=2 * K * ff * d),
+        "combine": dict(bytes=3 * S * d * eb, flops=S * d),
+    }
+    return out
+
+
+def build_layer(cfg):
+    import numpy as np  # noqa: F401
+    from branch_folding_amd.runner import DeviceLayer
+    from synth import make_workload
+    t = time.time()
+    w = make_workload(cfg, layers=1)
+    log(f"[bench] workload {cfg.name} drawn in {time.time() - t:.1f}s")
+    dl = DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src)
+    return w, dl
+
+
+def time_layer(dl, tau, steps, warmup, ev, stream, probe_step=None):
+    """Returns (ms per step, list of probe-step durations in ms)."""
+    import torch
+    from branch_folding_amd import _lib as L
+    for _ in range(warmup):
+        dl.forward(tau, stream=stream)
+    t0, t1 = ev.create(2)
+    ps = ev.create(steps) if probe_step is not None else []
+    pe = ev.create(steps) if probe_step is not None else []
+    torch.cuda.synchronize()
+    ev.record(t0, stream)
+    for i in range(steps):
+        probe = None
+        if probe_step is not None:
+            probe = L.Probe(probe_step, ps[i], pe[i])
+        dl.forward(tau, stream=stream, probe=probe)
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    total = ev.ms(t0, t1)
+    per = [ev.ms(a, b) for a, b in zip(ps, pe)]
+    ev.destroy([t0, t1] + ps + pe)
+    return total / steps, per
+
+
+def kernel_breakdown(dl, tau, reps, ev, stream):
+    from branch_folding_amd import _lib as L
+    out = {}
+    for idx, name in enumerate(L.STEPS):
+        _, per = time_layer(dl, tau, reps, 2, ev, stream, probe_step=idx)
+        out[name] = sum(per) / len(per) * 1e3 if per else 0.0
+    return out
+
+
+def cpu_baseline(w, tau, budget_s):
+    """The oracle as it stands on the host cores, on whole verify layers of the same
+    workload, repeated until the time budget is used."""
+    from oracle import layer
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    cfg = w.cfg
+    pk, pv = w.prefix_kv(0)
+    runs, t0 = 0, time.time()
+    while True:
+        layer(w.weights[0], w.H, w.fold_src, tau, pk, pv, n_q=cfg.n_q, n_kv=cfg.n_kv,
+              eps=cfg.rms_eps)
+        runs += 1
+        el = time.time() - t0
+        if el >= budget_s:
+            break
+    return dict(value=cfg.slots * runs / el, unit="branch-tokens/s", cores=int(cores),
+                kind="oracle",
+                sample=f"{runs} whole {cfg.name} verify layers (tau={tau}), numpy float64 "
+                       f"oracle, {el:.1f}s wall, {os.cpu_count()} host CPUs visible")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 4],
+                    help="configuration id (1 = the 7B-shaped headline layer)")
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also run the tau sweep of config 2")
+    ap.add_argument("--report", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the folded verify layer is measured on one "
+              "MI355X (multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from branch_folding_amd import _lib as L
+    from synth import CONFIGS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    L.lib()
+    cfg = CONFIGS[args.workload]
+    tau = cfg.tau if args.tau is None else args.tau
+    w, dl = build_layer(cfg)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+
+    dl.forward(tau, stream=stream)
+    torch.cuda.synchronize()
+    K = dl.fold_state()["K"]
+    log(f"[bench] K={K} of S={cfg.slots} packed rows")
+
+    dom = L.STEPS.index("ffn_gate_up")
+    ms, per = time_layer(dl, tau, args.steps, args.warmup, ev, stream, probe_step=dom)
+    log(f"[bench] {ms * 1e3:.1f} us per verify layer")
+    dom_ms = sum(per) / len(per)
+    alg = algorithmic(cfg, K)
+    dom_bytes = alg["ffn_gate_up"]["bytes"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    kernels = kernel_breakdown(dl, tau, 20, ev, stream)
+    log("[bench] per-kernel us: " + ", ".join(f"{k}={v:.1f}" for k, v in kernels.items()))
+
+    result = {
+        "metric": "branch-tokens verified/s per layer (7B shape, 1+15 branches); us/verify-layer",
+        "value": cfg.slots / (ms * 1e-3),
+        "unit": "branch-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; random-init weights of the named shape)",
+        "config": {"workload": cfg.name, "nodes": cfg.num_nodes, "block": cfg.block,
+                   "hidden": cfg.hidden, "heads": f"{cfg.n_q}q/{cfg.n_kv}kv x {cfg.head_dim}",
+                   "ffn": cfg.ffn, "prefix": cfg.prefix, "tau": tau, "graph": cfg.graph},
+        "us_per_verify_layer": ms * 1e3,
+        "packed_rows": K,
+        "recompute_fraction": K / cfg.slots,
+        "kernels_us": kernels,
+        "roofline": {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "avg_us": dom_ms * 1e3,
+                     "algorithmic_bytes": dom_bytes},
+    }
+    report = {"main": result}
+    if args.sweep:
+        report["tau_sweep"] = tau_sweep(ev, stream, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(w, tau, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump(report, f, indent=1)
+    print(json.dumps(result), flush=True)
+
+
+def tau_sweep(ev, stream, steps, warmup):
+    """Recompute fraction and time of the 3B-shaped DAG layer across tau (dense first)."""
+    import torch
+    from synth import CONFIGS
+    cfg = CONFIGS[2]
+    w, dl = build_layer(cfg)
+    rows = []
+    for tau in (-1.0,) + tuple(cfg.taus):
+        dl.forward(tau, stream=stream)
+        torch.cuda.synchronize()
+        K = dl.fold_state()["K"]
+        ms, _ = time_layer(dl, tau, steps, warmup, ev, stream)
+        kern = kernel_breakdown(dl, tau, 10, ev, stream)
+        rows.append(dict(tau=tau, K=K, recompute_fraction=K / cfg.slots, us=ms * 1e3,
+                         kernels_us=kern))
+        log(f"[bench] sweep tau={tau}: K={K} ({K / cfg.slots:.3f}) {ms * 1e3:.1f} us")
+    return rows
+
+
+if __name__ == "__main__":
+    main()

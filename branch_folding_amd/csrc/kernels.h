@@ -1,0 +1,123 @@
+// Internal launchers of the folded verify-layer kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace specfold {
+
+// resolve_pack modes
+constexpr int kResolve = 1;
+constexpr int kPack = 2;
+
+template <typename T>
+hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
+                       float* ratio, uint8_t* recompute, hipStream_t st);
+size_t resolve_pack_lds_bytes(int S);
+hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,
+                               const int32_t* src_in, int N, int B, int mode, int32_t* src_out,
+                               int32_t* packed_slot, int32_t* slot_row, int32_t* count,
+                               hipStream_t st);
+template <typename T>
+hipError_t launch_rmsnorm_gather(const void* X, const int32_t* rows, const int32_t* count,
+                                 int cap, int S, int d, float eps, const void* g, void* out,
+                                 hipStream_t st);
+template <typename T>
+hipError_t launch_combine(const void* h, const void* F, const int32_t* slot_row,
+                          const int32_t* count, int cap, int S, int d, void* y, hipStream_t st);
+
+// ---------------------------------------------------------------------------------------
+// GEMM  C[M, N] = A[M, Kd] . W[N, Kd]^T  (both operands K-contiguous), M read on the
+// device.  Epilogues: plain store, + residual, SwiGLU (W = [gate; up], output [M, ff]).
+// ---------------------------------------------------------------------------------------
+enum GemmEpi { kEpiStore = 0, kEpiResidual = 1, kEpiSwiGLU = 2 };
+
+struct GemmParams {
+  const void* A;
+  long lda;
+  const void* W;
+  long ldw;
+  void* C;
+  long ldc;
+  const void* R;     // residual (kEpiResidual), [M, N] with leading dimension ldr
+  long ldr;
+  float* partial;    // split-K partial sums, [split][M][N] fp32
+  const int32_t* m_dev;  // device row count (nullptr: m_cap rows)
+  int m_cap;
+  int N;             // logical output columns (2*ff for SwiGLU)
+  int Kd;
+  int ff;            // SwiGLU only
+};
+
+constexpr int kGemmBM = 128;
+constexpr int kGemmBN = 128;
+constexpr int kGemmBKBytes = 128;
+constexpr int kGemmMaxSplit = 16;
+
+// Split-K factor chosen on the device from the tile count (the packed row count is only
+// known there); the reduction kernel recomputes it with the same function.
+__host__ __device__ inline int gemm_split(int tiles, int kiters) {
+  if (tiles <= 0) return 1;
+  if (tiles >= kPlanCUs) return 1;
+  int s = (kPlanCUs + tiles - 1) / tiles;
+  int smax = kiters / 4;
+  if (smax < 1) smax = 1;
+  if (s > smax) s = smax;
+  if (s > kGemmMaxSplit) s = kGemmMaxSplit;
+  return s;
+}
+
+template <typename T>
+hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st);
+// fp32 elements of split-K partial storage any GEMM with these bounds may use
+size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes);
+
+// ---------------------------------------------------------------------------------------
+// Attention.  Prefix phase: online-softmax partials of every packed row's queries over the
+// prefix view (split over key ranges).  Block phase: every slot's query against its own
+// branch's block keys, merged with the prefix partials of its packed row.
+// ---------------------------------------------------------------------------------------
+struct AttnParams {
+  const void* qkv;     // packed [K, (n_q + 2 n_kv) dh]
+  long ld_qkv;
+  int n_q, n_kv, dh;
+  const int32_t* count;  // K (device)
+  int cap;               // max K (= S)
+  const void* pk;
+  const void* pv;
+  long stride_tok, stride_head;
+  int P;
+  float scale_log2;
+  float* part_o;         // [nsplit][K][n_q][dh]  (K = device packed count)
+  float* part_lse;       // [nsplit][K][n_q]
+  int S;
+  const int32_t* slot_row;
+  int N, B;
+  void* out;             // [S, n_q dh]
+  long ld_out;
+};
+
+constexpr int kAttnMaxSplit = 32;
+__host__ __device__ inline int attn_splits(int K, int g, int n_kv, int P) {
+  if (P <= 0 || K <= 0) return 0;
+  const int qtiles = (K * g + 63) / 64;
+  const int units = n_kv * qtiles;
+  const int chunks = (P + 63) / 64;
+  int s = (2 * kPlanCUs + units - 1) / units;
+  int smax = chunks / 2;
+  if (smax < 1) smax = 1;
+  if (s > smax) s = smax;
+  if (s > kAttnMaxSplit) s = kAttnMaxSplit;
+  return s;
+}
+// largest nsplit * K over K in [1, S] (rows of partial storage)
+size_t attn_partial_rows(int S, int g, int n_kv, int P);
+
+template <typename T>
+hipError_t launch_attn_prefix(const AttnParams& p, int num_cu, hipStream_t st);
+template <typename T>
+hipError_t launch_attn_block(const AttnParams& p, int num_cu, hipStream_t st);
+
+}  // namespace specfold

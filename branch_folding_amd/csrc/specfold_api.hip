@@ -1,0 +1,401 @@
+// C ABI of the folded multi-branch verify layer: argument checks, workspace carving and
+// the launch sequence.  Everything is enqueued on the caller's stream; nothing here
+// synchronises, allocates device memory or keeps global mutable state besides a per-device
+// cache of the compute-unit count.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/specfold.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace specfold;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+specfold_status fail(specfold_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+specfold_status ok() {
+  g_last_error.clear();
+  return SPECFOLD_OK;
+}
+
+#define HIP_CHECK(expr)                                                                  \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(SPECFOLD_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));      \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(const specfold_shape* s) { return s->dtype == SPECFOLD_BF16 ? 2 : 4; }
+
+specfold_status check_graph_shape(const specfold_shape* s) {
+  if (!s) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->num_nodes < 1 || s->block < 1)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "num_nodes and block must be >= 1 (got %d, %d)",
+                s->num_nodes, s->block);
+  if (s->block > 1024)
+    return fail(SPECFOLD_ERR_UNSUPPORTED, "block %d > 1024 is not supported", s->block);
+  if ((long)s->num_nodes * s->block > 16384)
+    return fail(SPECFOLD_ERR_UNSUPPORTED, "num_nodes * block = %ld > 16384 is not supported",
+                (long)s->num_nodes * s->block);
+  return SPECFOLD_OK;
+}
+
+specfold_status check_shape(const specfold_shape* s, bool layer) {
+  specfold_status st = check_graph_shape(s);
+  if (st != SPECFOLD_OK) return st;
+  if (s->dtype != SPECFOLD_F32 && s->dtype != SPECFOLD_BF16)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "dtype %d is not a specfold_dtype", s->dtype);
+  if (s->hidden < 128 || s->hidden % 128 != 0)
+    return fail(SPECFOLD_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 128",
+                s->hidden);
+  if (!layer) return SPECFOLD_OK;
+  if (s->ffn < 128 || s->ffn % 128 != 0)
+    return fail(SPECFOLD_ERR_UNSUPPORTED, "ffn %d must be a positive multiple of 128", s->ffn);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(SPECFOLD_ERR_UNSUPPORTED, "head_dim %d must be 64 or 128", s->head_dim);
+  if (s->n_q_heads < 1 || s->n_kv_heads < 1)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "head counts must be >= 1");
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->prefix_len < 0) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "prefix_len < 0");
+  if (!(s->rms_eps >= 0.f)) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "rms_eps must be >= 0");
+  return SPECFOLD_OK;
+}
+
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kPlanCUs;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = kPlanCUs;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout of one layer.
+struct Layout {
+  size_t ratio, rec, src, packed, slot_row, count;
+  size_t a1, qkv, part_o, part_lse, attn, h, a2, G, F, gpart;
+  size_t total;
+};
+
+Layout layout_of(const specfold_shape* s) {
+  const size_t S = (size_t)s->num_nodes * s->block;
+  const size_t eb = elem_bytes(s);
+  const size_t d = s->hidden, ff = s->ffn, dh = s->head_dim;
+  const size_t qkvd = (size_t)(s->n_q_heads + 2 * s->n_kv_heads) * dh;
+  const size_t qd = (size_t)s->n_q_heads * dh;
+  const int g = s->n_q_heads / s->n_kv_heads;
+  const size_t prow = attn_partial_rows((int)S, g, s->n_kv_heads, s->prefix_len);
+  size_t gp = 0;
+  const int ebi = (int)eb;
+  gp = std::max(gp, gemm_partial_elems((int)S, (int)qkvd, (int)d, ebi));
+  gp = std::max(gp, gemm_partial_elems((int)S, (int)d, (int)qd, ebi));
+  gp = std::max(gp, gemm_partial_elems((int)S, (int)(2 * ff), (int)d, ebi));
+  gp = std::max(gp, gemm_partial_elems((int)S, (int)d, (int)ff, ebi));
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.ratio = take(S * 4);
+  L.rec = take(S);
+  L.src = take(S * 4);
+  L.packed = take(S * 4);
+  L.slot_row = take(S * 4);
+  L.count = take(256);
+  L.a1 = take(S * d * eb);
+  L.qkv = take(S * qkvd * eb);
+  L.part_o = take(prow * qd * 4);
+  L.part_lse = take(prow * (size_t)s->n_q_heads * 4);
+  L.attn = take(S * qd * eb);
+  L.h = take(S * d * eb);
+  L.a2 = take(S * d * eb);
+  L.G = take(S * ff * eb);
+  L.F = take(S * d * eb);
+  L.gpart = take(gp * 4);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights* w,
+                          const specfold_kv_view* prefix, const void* hin, void* hout,
+                          const int32_t* fold_src, float tau, float* ratio, uint8_t* rec,
+                          int32_t* src, int32_t* packed, int32_t* slot_row, int32_t* count,
+                          bool state_in, char* ws, const Layout& L, hipStream_t st,
+                          const specfold_probe* probe) {
+  const int N = s->num_nodes, B = s->block, S = N * B, d = s->hidden, ff = s->ffn;
+  const int dh = s->head_dim, nq = s->n_q_heads, nkv = s->n_kv_heads;
+  const int qkvd = (nq + 2 * nkv) * dh, qd = nq * dh;
+  const int cus = num_cus();
+  auto mark = [&](int step, bool begin) -> hipError_t {
+    if (!probe || probe->step != step) return hipSuccess;
+    void* ev = begin ? probe->start : probe->stop;
+    return ev ? hipEventRecord((hipEvent_t)ev, st) : hipSuccess;
+  };
+  if (!state_in) {
+    HIP_CHECK(mark(SPECFOLD_STEP_GATE, true));
+    HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, rec, st));
+    HIP_CHECK(mark(SPECFOLD_STEP_GATE, false));
+    HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, true));
+    HIP_CHECK(launch_resolve_pack(rec, fold_src, nullptr, N, B, kResolve | kPack, src, packed,
+                                  slot_row, count, st));
+    HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, false));
+  }
+  void* A1 = ws + L.a1;
+  void* QKV = ws + L.qkv;
+  void* ATT = ws + L.attn;
+  void* Hh = ws + L.h;
+  void* A2 = ws + L.a2;
+  void* G = ws + L.G;
+  void* F = ws + L.F;
+  float* gpart = (float*)(ws + L.gpart);
+
+  HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM1, true));
+  HIP_CHECK(launch_rmsnorm_gather<T>(hin, packed, count, S, S, d, s->rms_eps, w->rms1, A1, st));
+  HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM1, false));
+
+  GemmParams gp{};
+  gp.A = A1; gp.lda = d; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = qkvd;
+  gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = qkvd; gp.Kd = d;
+  HIP_CHECK(mark(SPECFOLD_STEP_QKV, true));
+  HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
+  HIP_CHECK(mark(SPECFOLD_STEP_QKV, false));
+
+  AttnParams ap{};
+  ap.qkv = QKV; ap.ld_qkv = qkvd; ap.n_q = nq; ap.n_kv = nkv; ap.dh = dh;
+  ap.count = count; ap.cap = S;
+  ap.pk = prefix ? prefix->k : nullptr; ap.pv = prefix ? prefix->v : nullptr;
+  ap.stride_tok = prefix ? prefix->stride_tok : 0; ap.stride_head = prefix ? prefix->stride_head : 0;
+  ap.P = s->prefix_len;
+  ap.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
+  ap.part_o = (float*)(ws + L.part_o); ap.part_lse = (float*)(ws + L.part_lse);
+  ap.S = S; ap.slot_row = slot_row; ap.N = N; ap.B = B; ap.out = ATT; ap.ld_out = qd;
+  HIP_CHECK(mark(SPECFOLD_STEP_ATTN_PREFIX, true));
+  HIP_CHECK(launch_attn_prefix<T>(ap, cus, st));
+  HIP_CHECK(mark(SPECFOLD_STEP_ATTN_PREFIX, false));
+  HIP_CHECK(mark(SPECFOLD_STEP_ATTN_BLOCK, true));
+  HIP_CHECK(launch_attn_block<T>(ap, cus, st));
+  HIP_CHECK(mark(SPECFOLD_STEP_ATTN_BLOCK, false));
+
+  gp = GemmParams{};
+  gp.A = ATT; gp.lda = qd; gp.W = w->w_o; gp.ldw = qd; gp.C = Hh; gp.ldc = d;
+  gp.R = hin; gp.ldr = d; gp.partial = gpart; gp.m_dev = nullptr; gp.m_cap = S; gp.N = d;
+  gp.Kd = qd;
+  HIP_CHECK(mark(SPECFOLD_STEP_O_PROJ, true));
+  HIP_CHECK(launch_gemm<T>(gp, kEpiResidual, cus, st));
+  HIP_CHECK(mark(SPECFOLD_STEP_O_PROJ, false));
+
+  HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM2, true));
+  HIP_CHECK(launch_rmsnorm_gather<T>(Hh, packed, count, S, S, d, s->rms_eps, w->rms2, A2, st));
+  HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM2, false));
+
+  gp = GemmParams{};
+  gp.A = A2; gp.lda = d; gp.W = w->w_gate_up; gp.ldw = d; gp.C = G; gp.ldc = ff;
+  gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = 2 * ff; gp.Kd = d; gp.ff = ff;
+  HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, true));
+  HIP_CHECK(launch_gemm<T>(gp, kEpiSwiGLU, cus, st));
+  HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, false));
+
+  gp = GemmParams{};
+  gp.A = G; gp.lda = ff; gp.W = w->w_down; gp.ldw = ff; gp.C = F; gp.ldc = d;
+  gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = d; gp.Kd = ff;
+  HIP_CHECK(mark(SPECFOLD_STEP_FFN_DOWN, true));
+  HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
+  HIP_CHECK(mark(SPECFOLD_STEP_FFN_DOWN, false));
+
+  HIP_CHECK(mark(SPECFOLD_STEP_COMBINE, true));
+  HIP_CHECK(launch_combine<T>(Hh, F, slot_row, count, S, S, d, hout, st));
+  HIP_CHECK(mark(SPECFOLD_STEP_COMBINE, false));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+specfold_status specfold_gate(const specfold_shape* shape, const void* hidden,
+                              const int32_t* fold_src, float tau, float* ratio,
+                              uint8_t* recompute, void* stream) {
+  specfold_status st = check_shape(shape, false);
+  if (st != SPECFOLD_OK) return st;
+  if (!hidden || !fold_src || !recompute)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden, fold_src and recompute are required");
+  if (!aligned16(hidden)) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden is not 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const specfold_shape* sh = shape;
+  if (sh->dtype == SPECFOLD_BF16) {
+    HIP_CHECK(launch_gate<bf16>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
+                                ratio, recompute, s));
+  } else {
+    HIP_CHECK(launch_gate<float>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
+                                 ratio, recompute, s));
+  }
+  return ok();
+}
+
+specfold_status specfold_resolve(const specfold_shape* shape, const uint8_t* recompute,
+                                 const int32_t* fold_src, int32_t* src_node, void* stream) {
+  specfold_status st = check_graph_shape(shape);
+  if (st != SPECFOLD_OK) return st;
+  if (!recompute || !fold_src || !src_node)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "recompute, fold_src and src_node are required");
+  HIP_CHECK(launch_resolve_pack(recompute, fold_src, nullptr, shape->num_nodes, shape->block,
+                                kResolve, src_node, nullptr, nullptr, nullptr,
+                                (hipStream_t)stream));
+  return ok();
+}
+
+specfold_status specfold_pack(const specfold_shape* shape, const uint8_t* recompute,
+                              const int32_t* src_node, int32_t* packed_slot,
+                              int32_t* slot_row, int32_t* packed_count, void* stream) {
+  specfold_status st = check_graph_shape(shape);
+  if (st != SPECFOLD_OK) return st;
+  if (!recompute || !src_node || !packed_slot || !slot_row || !packed_count)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
+                "recompute, src_node, packed_slot, slot_row and packed_count are required");
+  HIP_CHECK(launch_resolve_pack(recompute, nullptr, src_node, shape->num_nodes, shape->block,
+                                kPack, nullptr, packed_slot, slot_row, packed_count,
+                                (hipStream_t)stream));
+  return ok();
+}
+
+size_t specfold_layer_workspace_bytes(const specfold_shape* shape) {
+  if (check_shape(shape, true) != SPECFOLD_OK) return 0;
+  g_last_error.clear();
+  return layout_of(shape).total;
+}
+
+size_t specfold_workspace_offset(const specfold_shape* shape, int32_t which) {
+  if (check_shape(shape, true) != SPECFOLD_OK) return SIZE_MAX;
+  const Layout L = layout_of(shape);
+  switch (which) {
+    case SPECFOLD_T_QKV: return L.qkv;
+    case SPECFOLD_T_ATTN: return L.attn;
+    case SPECFOLD_T_H: return L.h;
+    case SPECFOLD_T_FFN: return L.F;
+    default:
+      fail(SPECFOLD_ERR_INVALID_ARGUMENT, "unknown tensor id %d", which);
+      return SIZE_MAX;
+  }
+}
+
+specfold_status specfold_layer_forward(const specfold_shape* shape,
+                                       const specfold_layer_weights* weights,
+                                       const specfold_kv_view* prefix, const void* hidden_in,
+                                       void* hidden_out, const int32_t* fold_src, float tau,
+                                       specfold_fold_state* state, uint32_t flags,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  return specfold_layer_forward_probed(shape, weights, prefix, hidden_in, hidden_out, fold_src,
+                                       tau, state, flags, workspace, workspace_bytes, stream,
+                                       nullptr);
+}
+
+specfold_status specfold_layer_forward_probed(const specfold_shape* shape,
+                                              const specfold_layer_weights* weights,
+                                              const specfold_kv_view* prefix,
+                                              const void* hidden_in, void* hidden_out,
+                                              const int32_t* fold_src, float tau,
+                                              specfold_fold_state* state, uint32_t flags,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream, const specfold_probe* probe) {
+  specfold_status st = check_shape(shape, true);
+  if (st != SPECFOLD_OK) return st;
+  const bool state_in = (flags & SPECFOLD_FLAG_FOLD_STATE_IN) != 0;
+  if (flags & ~SPECFOLD_FLAG_FOLD_STATE_IN)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  if (!weights || !weights->rms1 || !weights->w_qkv || !weights->w_o || !weights->rms2 ||
+      !weights->w_gate_up || !weights->w_down)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "every layer weight pointer is required");
+  const void* wp[6] = {weights->rms1, weights->w_qkv, weights->w_o, weights->rms2,
+                       weights->w_gate_up, weights->w_down};
+  for (int i = 0; i < 6; ++i)
+    if (!aligned16(wp[i]))
+      return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "weight pointer %d is not 16-byte aligned", i);
+  if (!hidden_in || !hidden_out)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden_in and hidden_out are required");
+  if (!aligned16(hidden_in) || !aligned16(hidden_out))
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden_in/hidden_out must be 16-byte aligned");
+  const size_t eb = elem_bytes(shape);
+  const size_t hbytes = (size_t)shape->num_nodes * shape->block * shape->hidden * eb;
+  {
+    const char* a = (const char*)hidden_in;
+    const char* b = (const char*)hidden_out;
+    if (a < b + hbytes && b < a + hbytes)
+      return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden_in and hidden_out overlap");
+  }
+  if (shape->prefix_len > 0) {
+    if (!prefix || !prefix->k || !prefix->v)
+      return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "prefix_len > 0 needs a prefix view");
+    if (!aligned16(prefix->k) || !aligned16(prefix->v) || prefix->stride_tok < 0 ||
+        prefix->stride_head < 0 || (prefix->stride_tok * (int64_t)eb) % 16 != 0 ||
+        (prefix->stride_head * (int64_t)eb) % 16 != 0)
+      return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
+                  "prefix view pointers and strides must keep rows 16-byte aligned");
+  }
+  if (!state_in && !fold_src)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "fold_src is required unless the fold state is an input");
+  if (state_in && (!state || !state->recompute || !state->src_node || !state->packed_slot ||
+                   !state->slot_row || !state->packed_count))
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
+                "SPECFOLD_FLAG_FOLD_STATE_IN needs every fold-state array except ratio");
+  const Layout L = layout_of(shape);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(SPECFOLD_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                workspace ? workspace_bytes : (size_t)0, L.total);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+
+  char* ws = (char*)workspace;
+  auto pick = [&](auto* user, size_t off) {
+    using P = decltype(user);
+    return user ? user : (P)(ws + off);
+  };
+  float* ratio = pick(state ? state->ratio : (float*)nullptr, L.ratio);
+  uint8_t* rec = pick(state ? state->recompute : (uint8_t*)nullptr, L.rec);
+  int32_t* src = pick(state ? state->src_node : (int32_t*)nullptr, L.src);
+  int32_t* packed = pick(state ? state->packed_slot : (int32_t*)nullptr, L.packed);
+  int32_t* slot_row = pick(state ? state->slot_row : (int32_t*)nullptr, L.slot_row);
+  int32_t* count = pick(state ? state->packed_count : (int32_t*)nullptr, L.count);
+  hipStream_t s = (hipStream_t)stream;
+  if (shape->dtype == SPECFOLD_BF16)
+    return run_layer<bf16>(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, ratio,
+                           rec, src, packed, slot_row, count, state_in, ws, L, s, probe);
+  return run_layer<float>(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, ratio,
+                          rec, src, packed, slot_row, count, state_in, ws, L, s, probe);
+}
+
+const char* specfold_last_error(void) { return g_last_error.c_str(); }
+
+int32_t specfold_version(void) { return 100; }
+
+}  // extern "C"

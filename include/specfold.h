@@ -1,0 +1,250 @@
+/*
+ * specfold.h -- C ABI of the folded multi-branch verify layer for AMD MI355X (gfx950).
+ *
+ * One verify step of a block-diffusion LLM runs a parent branch and its draft children
+ * (each revealing one or a few more masked positions of the same block) through a
+ * transformer layer together.  Most child positions barely differ from their parent, so
+ * the layer measures the per-position difference at its input, reuses the parent's
+ * projections and FFN output where the difference is small, packs the positions that
+ * must be recomputed from every branch into one batch, runs the heavy GEMMs once on
+ * that batch, and corrects each folded position's attention with its own branch's
+ * keys and values while the shared prefix cache is read once through a strided view.
+ *
+ * Sources (cited by page and section):
+ *   "SpecFold" explainer, blog.ontle.kr/blog/358: the paragraphs on measuring
+ *     ||H_child - H_parent|| / ||H_parent|| at the layer input, on reusing the parent
+ *     while keeping the child's own delta, on packing the recompute positions of all
+ *     branches into one bundle, on referencing the shared prefix cache without copies,
+ *     and the implementation memo (gate, provenance and streaming-attention kernels,
+ *     zero-copy strided view, GQA);
+ *   "SpecFold uskoryaet diffuzionnye yazykovye modeli do 1,99x", iitog.ru: the abstract
+ *     summary (token-level residual gating, folded attention and FFN);
+ *   Spiffy explainer, lifetechia.com/?p=5403: the directed draft graph.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or retains them beyond the call.  They must be 16-byte aligned.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Host-side argument checks run first and fail before anything is
+ *     enqueued; device faults surface at the caller's next synchronisation.
+ *   - Integer results (masks, provenance, packing) are exact; floating-point results are
+ *     deterministic (bit-identical between runs, no floating-point atomics).
+ *   - There is no global mutable state: calls on different streams are safe when they
+ *     use different output and workspace buffers.
+ *   - On failure a status other than SPECFOLD_OK is returned and specfold_last_error()
+ *     returns a message (per host thread).
+ *   - Device-side index inputs (fold_src, masks, provenance, packed rows) are clamped
+ *     before use, so malformed values give wrong results but never out-of-bounds access.
+ *
+ * Layouts (row-major, elements of `dtype` unless noted):
+ *   hidden states H      [N, B, d]         N = num_nodes (node 0 = parent/root), B = block
+ *   slot                 s = n * B + i     (node-major, position-minor), S = N * B
+ *   fold_src             int32 [N]         fold source (first parent) of each node;
+ *                                          fold_src[0] = -1 and 0 <= fold_src[n] < n
+ *                                          (nodes are numbered topologically)
+ *   w_qkv                [(n_q + 2 n_kv) dh, d]  rows: Q heads, then K heads, then V heads
+ *   w_o                  [d, n_q dh]
+ *   w_gate_up            [2 ffn, d]        rows: gate projection, then up projection
+ *   w_down               [d, ffn]
+ *   rms1, rms2           [d]               RMSNorm gains
+ *   prefix K/V           element (t, kvh, c) at ptr[t * stride_tok + kvh * stride_head + c]
+ */
+#ifndef SPECFOLD_H
+#define SPECFOLD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum specfold_status {
+  SPECFOLD_OK = 0,
+  SPECFOLD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned pointer      */
+  SPECFOLD_ERR_UNSUPPORTED = 2,      /* valid but unsupported shape (see below)         */
+  SPECFOLD_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required      */
+  SPECFOLD_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed      */
+} specfold_status;
+
+typedef enum specfold_dtype {
+  SPECFOLD_F32 = 0,   /* float32 storage and arithmetic                                 */
+  SPECFOLD_BF16 = 1   /* bfloat16 storage; fp32 accumulation, softmax and gate          */
+} specfold_dtype;
+
+/* Shape of one verify layer.  Supported: num_nodes >= 1, 1 <= block <= 1024,
+ * num_nodes * block <= 16384, hidden and ffn multiples of 128, head_dim 64 or 128,
+ * n_q_heads a multiple of n_kv_heads, prefix_len >= 0, rms_eps >= 0. */
+typedef struct specfold_shape {
+  int32_t num_nodes;
+  int32_t block;
+  int32_t hidden;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ffn;
+  int32_t prefix_len;
+  float rms_eps;
+  int32_t dtype;       /* specfold_dtype */
+} specfold_shape;
+
+/* Zero-copy strided view of the shared prefix cache (SpecFold explainer: the shared cache
+ * is referenced, never copied per branch).  Strides are in elements; the head_dim
+ * elements of one (token, head) are contiguous; strides must keep rows 16-byte aligned. */
+typedef struct specfold_kv_view {
+  const void* k;
+  const void* v;
+  int64_t stride_tok;
+  int64_t stride_head;
+} specfold_kv_view;
+
+typedef struct specfold_layer_weights {
+  const void* rms1;
+  const void* w_qkv;
+  const void* w_o;
+  const void* rms2;
+  const void* w_gate_up;
+  const void* w_down;
+} specfold_layer_weights;
+
+/* Fold state of one layer (device buffers, S = num_nodes * block entries each).
+ * Outputs of specfold_layer_forward, or inputs with SPECFOLD_FLAG_FOLD_STATE_IN.
+ * Any pointer may be NULL: the library then keeps that array in the workspace. */
+typedef struct specfold_fold_state {
+  float* ratio;          /* [S]  r = ||H_n - H_src|| / ||H_src|| (+inf for the root)  */
+  uint8_t* recompute;    /* [S]  1 = recompute, 0 = folded                             */
+  int32_t* src_node;     /* [S]  node whose computation the slot uses                  */
+  int32_t* packed_slot;  /* [S]  packed row k -> slot id (first packed_count valid)    */
+  int32_t* slot_row;     /* [S]  slot -> packed row of (src_node, position)            */
+  int32_t* packed_count; /* [1]  K = number of packed (recompute) rows                 */
+} specfold_fold_state;
+
+/* Skip gate/resolve/pack and read recompute, src_node, packed_slot, slot_row and
+ * packed_count from `state` (all five must be non-NULL and mutually consistent). */
+#define SPECFOLD_FLAG_FOLD_STATE_IN 1u
+
+/* Gate (SpecFold explainer, paragraph on measuring the relative difference at the layer
+ * input; iitog.ru summary, "token-level residual gating").
+ * For every child n >= 1 and position i:
+ *     r = ||H[n,i] - H[p,i]||_2 / ||H[p,i]||_2,  p = fold_src[n],
+ * accumulated in fp32; recompute = !(r <= tau), so tau < 0 folds nothing, tau = +inf
+ * folds every finite ratio, and NaN recomputes.  ||H[p,i]|| = 0 gives r = 0 when the
+ * rows are equal and +inf otherwise.  Root rows always recompute (r = +inf), and so
+ * does any node whose fold_src entry is not in [0, n).
+ *   hidden    [N, B, d] device, dtype = shape->dtype
+ *   fold_src  [N] int32 device
+ *   ratio     [N, B] float device, or NULL
+ *   recompute [N, B] uint8 device (required)                                          */
+specfold_status specfold_gate(const specfold_shape* shape, const void* hidden,
+                              const int32_t* fold_src, float tau, float* ratio,
+                              uint8_t* recompute, void* stream);
+
+/* Provenance (SpecFold explainer, implementation memo: follow fold chains so every
+ * folded position points at the ancestor state that actually computed it).
+ *     src_node[n,i] = n                        if slot (n,i) recomputes (or n = 0),
+ *                   = src_node[fold_src[n], i] otherwise.
+ *   recompute [N, B] uint8 device; fold_src [N] int32 device; src_node [N, B] int32 device */
+specfold_status specfold_resolve(const specfold_shape* shape, const uint8_t* recompute,
+                                 const int32_t* fold_src, int32_t* src_node, void* stream);
+
+/* Packing (SpecFold explainer: the recompute positions of all branches are compacted
+ * into one bundle so the heavy layer runs once on it).  Stable compaction of the
+ * recompute slots (root slots always count) in ascending slot id:
+ *     packed_slot[k] = slot id of the k-th recompute slot, k < K
+ *     slot_row[n,i]  = k such that packed_slot[k] = src_node[n,i] * B + i
+ *     packed_count[0] = K
+ *   recompute, src_node: [N, B] device inputs; packed_slot, slot_row: [N, B] int32
+ *   device outputs (packed_slot entries >= K are left unspecified); packed_count: [1]
+ *   int32 device output.  src_node must come from specfold_resolve on the same mask.  */
+specfold_status specfold_pack(const specfold_shape* shape, const uint8_t* recompute,
+                              const int32_t* src_node, int32_t* packed_slot,
+                              int32_t* slot_row, int32_t* packed_count, void* stream);
+
+/* Bytes of device workspace specfold_layer_forward needs for `shape` (0 if the shape is
+ * invalid or unsupported; see specfold_last_error). */
+size_t specfold_layer_workspace_bytes(const specfold_shape* shape);
+
+/* One folded verify layer (all steps of the SpecFold explainer's paragraphs on reuse,
+ * packing and streaming attention with per-branch correction):
+ *   1-3. gate, provenance and packing as above (skipped with SPECFOLD_FLAG_FOLD_STATE_IN);
+ *   4.   A = RMSNorm(H[packed rows]) * rms1;  [Q|K|V] = A w_qkv^T on the K packed rows;
+ *   5.   attention of every slot (n,i) and query head h (KV head h / (n_q/n_kv)):
+ *        query = Q[slot_row[n,i], h]; keys/values = the prefix view followed by branch
+ *        n's own block rows K/V[slot_row[n,j]], j < B; no mask; scale 1/sqrt(head_dim);
+ *        the prefix is streamed once per packed row and merged with each branch's block;
+ *   6.   h = H + o w_o^T for every slot;
+ *   7.   F = (SiLU(A2 w_gate^T) * (A2 w_up^T)) w_down^T, A2 = RMSNorm(h[packed rows]) * rms2;
+ *   8.   hidden_out[n,i] = h[n,i] + F[slot_row[n,i]].
+ * bf16: Q/K/V, attention output, h, the SwiGLU product, F and hidden_out are rounded to
+ * bf16; accumulation, softmax and normalisation statistics are fp32.
+ *   hidden_in, hidden_out: [N, B, d] device, no aliasing.
+ *   fold_src: [N] int32 device (may be NULL only with SPECFOLD_FLAG_FOLD_STATE_IN).
+ *   state: fold-state buffers (outputs, or inputs with the flag); may be NULL without it.
+ *   workspace: device buffer of at least specfold_layer_workspace_bytes(shape) bytes,
+ *   256-byte aligned; calls that overlap in time need distinct workspaces.             */
+specfold_status specfold_layer_forward(const specfold_shape* shape,
+                                       const specfold_layer_weights* weights,
+                                       const specfold_kv_view* prefix,
+                                       const void* hidden_in, void* hidden_out,
+                                       const int32_t* fold_src, float tau,
+                                       specfold_fold_state* state, uint32_t flags,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/* Launch steps of specfold_layer_forward, for timing probes. */
+typedef enum specfold_step {
+  SPECFOLD_STEP_GATE = 0,          /* gate                                            */
+  SPECFOLD_STEP_RESOLVE_PACK = 1,  /* provenance + packing                            */
+  SPECFOLD_STEP_RMSNORM1 = 2,      /* gathered RMSNorm of the packed rows             */
+  SPECFOLD_STEP_QKV = 3,           /* packed QKV GEMM (incl. its split-K reduction)   */
+  SPECFOLD_STEP_ATTN_PREFIX = 4,   /* prefix-phase attention                          */
+  SPECFOLD_STEP_ATTN_BLOCK = 5,    /* block-phase attention + merge                   */
+  SPECFOLD_STEP_O_PROJ = 6,        /* O projection + residual over all slots          */
+  SPECFOLD_STEP_RMSNORM2 = 7,      /* gathered RMSNorm before the FFN                 */
+  SPECFOLD_STEP_FFN_GATE_UP = 8,   /* packed gate/up GEMM with the SwiGLU product     */
+  SPECFOLD_STEP_FFN_DOWN = 9,      /* packed down GEMM                                */
+  SPECFOLD_STEP_COMBINE = 10       /* y = h + F[slot_row]                             */
+} specfold_step;
+
+/* A timing probe: `start` is recorded on the stream right before the first launch of
+ * step `step` and `stop` right after its last launch (both are hipEvent_t created by the
+ * caller).  Nothing is recorded for a step that the call skips. */
+typedef struct specfold_probe {
+  int32_t step;
+  void* start;
+  void* stop;
+} specfold_probe;
+
+/* specfold_layer_forward with an optional timing probe (probe may be NULL). */
+specfold_status specfold_layer_forward_probed(const specfold_shape* shape,
+                                              const specfold_layer_weights* weights,
+                                              const specfold_kv_view* prefix,
+                                              const void* hidden_in, void* hidden_out,
+                                              const int32_t* fold_src, float tau,
+                                              specfold_fold_state* state, uint32_t flags,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream, const specfold_probe* probe);
+
+/* Intermediates of the last specfold_layer_forward that are kept in the workspace, for
+ * inspection after the stream has synchronised.  Row k of a packed tensor is packed row
+ * k (k < K); slot tensors have S rows.  All are row-major in shape->dtype.            */
+typedef enum specfold_tensor {
+  SPECFOLD_T_QKV = 0,    /* [S cap, (n_q + 2 n_kv) dh] packed Q|K|V rows          */
+  SPECFOLD_T_ATTN = 1,   /* [S, n_q dh] attention output of every slot            */
+  SPECFOLD_T_H = 2,      /* [S, d]  h = H + attention projection                  */
+  SPECFOLD_T_FFN = 3     /* [S cap, d] packed FFN output rows                     */
+} specfold_tensor;
+
+/* Byte offset of tensor `which` inside the workspace (SIZE_MAX on invalid input). */
+size_t specfold_workspace_offset(const specfold_shape* shape, int32_t which);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* specfold_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t specfold_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECFOLD_H */

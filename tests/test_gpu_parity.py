@@ -1,0 +1,213 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Gate masks, provenance and packing must match bit for bit (slots whose ratio lies within
+1e-4 relative of tau are excluded from the mask comparison); layer outputs must agree to
+max|y - y_ref| / max|y_ref| <= 1e-3 (fp32) or 2e-2 (bf16).  When a tie-band slot decides
+differently, the layer is also compared with the oracle's own fold state fed to the GPU
+(SPECFOLD_FLAG_FOLD_STATE_IN), so the oracle never consumes a GPU result."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from parity_util import (TOL, assert_fold_state_equal, max_abs_rel, oracle_layer,
+                         oracle_state)
+from synth import CONFIGS, custom_config, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from branch_folding_amd import _lib as L
+    from branch_folding_amd.runner import DeviceLayer
+    L.lib()
+    return L, DeviceLayer
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+_WL = {}
+
+
+def _workload(cfg, **kw):
+    key = (cfg, tuple(sorted(kw.items())))
+    if key not in _WL:
+        _WL.clear()
+        _WL[key] = make_workload(cfg, **kw)
+    return _WL[key]
+
+
+# Small and edge-case shapes: ragged blocks (B not a multiple of 16, B > 64 so the block
+# phase spans two key tiles), ragged and empty prefixes, root-only graphs, MHA (g = 1),
+# GQA 7:1, head_dim 64/128, deep chains and DAGs.
+EDGE = [
+    custom_config(name="edge-root-only", num_nodes=1, block=7, hidden=128, n_q=2, n_kv=1,
+                  head_dim=64, ffn=128, prefix=5, dtype="f32", seed=31),
+    custom_config(name="edge-noprefix-mha", num_nodes=5, block=13, hidden=128, n_q=2, n_kv=2,
+                  head_dim=64, ffn=256, prefix=0, dtype="f32", graph="dag", reveal=(1, 2),
+                  seed=32),
+    custom_config(name="edge-ragged-bf16", num_nodes=9, block=70, hidden=256, n_q=7, n_kv=1,
+                  head_dim=128, ffn=384, prefix=100, dtype="bf16", graph="dag_deep",
+                  max_depth=6, reveal=(1, 4), seed=33),
+    custom_config(name="edge-chain-bf16", num_nodes=12, block=33, hidden=384, n_q=6, n_kv=2,
+                  head_dim=64, ffn=640, prefix=300, dtype="bf16", graph="chain",
+                  reveal=(1, 2), seed=34),
+    custom_config(name="edge-raggedN-bf16", num_nodes=3, block=9, hidden=128, n_q=3, n_kv=1,
+                  head_dim=64, ffn=128, prefix=65, dtype="bf16", graph="chain", seed=36),
+    custom_config(name="edge-star-f32", num_nodes=17, block=16, hidden=256, n_q=4, n_kv=4,
+                  head_dim=128, ffn=256, prefix=129, dtype="f32", graph="star",
+                  reveal=(1, 1), seed=35),
+]
+
+
+def _check_layer(cfg, w, tau, L, DeviceLayer, slots=None):
+    _say(f"[gpu] layer {cfg.name} tau={tau} S={cfg.slots}")
+    dl = DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src)
+    dl.forward(tau)
+    torch.cuda.synchronize()
+    gst = dl.fold_state()
+    ost = oracle_state(w, tau)
+    masks_agree = assert_fold_state_equal(gst, ost, tau)
+    y_gpu = dl.output_numpy()
+    tol = TOL[cfg.dtype]
+    if masks_agree:
+        ref = oracle_layer(w, tau, state=ost, slots=slots)
+        sel = np.ones(y_gpu.shape[:2], bool) if slots is None else _slot_mask(cfg, slots)
+        err = max_abs_rel(y_gpu[sel], ref["y"][sel])
+        _say(f"[gpu]   K={gst['K']} max-abs-rel={err:.3e} (tol {tol})")
+        assert err <= tol
+    # conditioned on the oracle's fold state
+    y_in = dl.forward(tau, state_in=dict(recompute=ost["recompute"], src_node=ost["src"],
+                                         packed_slot=np.pad(ost["packed_slot"],
+                                                            (0, cfg.slots - ost["K"])),
+                                         slot_row=ost["slot_row"],
+                                         packed_count=np.array([ost["K"]])))
+    torch.cuda.synchronize()
+    y_in = y_in.float().cpu().numpy().reshape(y_gpu.shape)
+    ref = oracle_layer(w, tau, state=ost, slots=slots)
+    sel = np.ones(y_gpu.shape[:2], bool) if slots is None else _slot_mask(cfg, slots)
+    err = max_abs_rel(y_in[sel], ref["y"][sel])
+    _say(f"[gpu]   state-in max-abs-rel={err:.3e}")
+    assert err <= tol
+    return dl, gst, ost
+
+
+def _slot_mask(cfg, slots):
+    m = np.zeros((cfg.num_nodes, cfg.block), bool)
+    for n, i in slots:
+        m[n, i] = True
+    return m
+
+
+@pytest.mark.parametrize("cfg", EDGE + [CONFIGS[0]], ids=lambda c: c.name)
+@pytest.mark.parametrize("tau", [-1.0, 0.05, 0.3, math.inf])
+def test_layer_small(cfg, tau):
+    L, DeviceLayer = _dev()
+    w = _workload(cfg)
+    _check_layer(cfg, w, tau, L, DeviceLayer)
+
+
+def test_fold_steps_individually():
+    """specfold_gate, specfold_resolve and specfold_pack called one by one."""
+    L, DeviceLayer = _dev()
+    from branch_folding_amd.runner import shape_of, to_device
+    for cfg in [CONFIGS[0], EDGE[2], CONFIGS[2].with_(hidden=256)]:
+        w = _workload(cfg, weights=False)
+        N, B, S = cfg.num_nodes, cfg.block, cfg.slots
+        sh = shape_of(cfg)
+        H = to_device(w.H.reshape(S, -1), torch.bfloat16 if cfg.dtype == "bf16" else torch.float32,
+                      "cuda")
+        fs = torch.from_numpy(w.fold_src).cuda()
+        for tau in (0.0, 0.02, 0.05, 0.1, -1.0, math.inf):
+            _say(f"[gpu] fold steps {cfg.name} tau={tau}")
+            ratio = torch.empty(S, device="cuda")
+            rec = torch.empty(S, dtype=torch.uint8, device="cuda")
+            src = torch.empty(S, dtype=torch.int32, device="cuda")
+            ps = torch.empty(S, dtype=torch.int32, device="cuda")
+            sr = torch.empty(S, dtype=torch.int32, device="cuda")
+            cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+            L.specfold_gate(sh, H, fs, tau, ratio, rec)
+            ost = oracle_state(w, tau)
+            # resolve/pack on the oracle's mask: bit-exact whatever the tie band did
+            rec_o = torch.from_numpy(ost["recompute"].reshape(-1).astype(np.uint8)).cuda()
+            L.specfold_resolve(sh, rec_o, fs, src)
+            L.specfold_pack(sh, rec_o, src, ps, sr, cnt)
+            torch.cuda.synchronize()
+            K = int(cnt.item())
+            assert K == ost["K"]
+            np.testing.assert_array_equal(src.cpu().numpy().reshape(N, B), ost["src"])
+            np.testing.assert_array_equal(ps.cpu().numpy()[:K], ost["packed_slot"])
+            np.testing.assert_array_equal(sr.cpu().numpy().reshape(N, B), ost["slot_row"])
+            gst = dict(ratio=ratio.cpu().numpy().reshape(N, B),
+                       recompute=rec.cpu().numpy().reshape(N, B) != 0,
+                       src=ost["src"], K=ost["K"], packed_slot=ost["packed_slot"],
+                       slot_row=ost["slot_row"])
+            assert_fold_state_equal(gst, ost, tau)
+
+
+def test_pack_maximum_slots():
+    """S = 16384 slots (the supported maximum) through resolve + pack."""
+    L, _ = _dev()
+    from branch_folding_amd.runner import shape_of
+    from oracle import pack, resolve
+    cfg = custom_config(num_nodes=256, block=64, hidden=128)
+    rng = np.random.default_rng(5)
+    fs = np.array([-1] + [int(rng.integers(0, n)) for n in range(1, 256)], dtype=np.int32)
+    rec = rng.random((256, 64)) < 0.3
+    rec[0] = True
+    sh = shape_of(cfg)
+    S = cfg.slots
+    src = torch.empty(S, dtype=torch.int32, device="cuda")
+    ps = torch.empty(S, dtype=torch.int32, device="cuda")
+    sr = torch.empty(S, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    rec_d = torch.from_numpy(rec.reshape(-1).astype(np.uint8)).cuda()
+    fs_d = torch.from_numpy(fs).cuda()
+    _say("[gpu] pack S=16384")
+    L.specfold_resolve(sh, rec_d, fs_d, src)
+    L.specfold_pack(sh, rec_d, src, ps, sr, cnt)
+    torch.cuda.synchronize()
+    src_o = resolve(rec, fs)
+    ps_o, sr_o, K = pack(rec, src_o)
+    assert int(cnt.item()) == K
+    np.testing.assert_array_equal(src.cpu().numpy().reshape(256, 64), src_o)
+    np.testing.assert_array_equal(ps.cpu().numpy()[:K], ps_o)
+    np.testing.assert_array_equal(sr.cpu().numpy().reshape(256, 64), sr_o)
+
+
+def test_cfg1_full_size():
+    """The 7B-shaped layer (1 + 15 branches, tau = 0.05) in the benchmark's launch
+    configuration, every output slot compared."""
+    L, DeviceLayer = _dev()
+    w = _workload(CONFIGS[1])
+    dl, gst, ost = _check_layer(CONFIGS[1], w, CONFIGS[1].tau, L, DeviceLayer)
+    # determinism: a second run is bit-identical
+    y1 = dl.forward(CONFIGS[1].tau).clone()
+    y2 = dl.forward(CONFIGS[1].tau).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.02, 0.05, 0.1])
+def test_cfg2_dag_tau_sweep(tau):
+    L, DeviceLayer = _dev()
+    _check_layer(CONFIGS[2], _workload(CONFIGS[2]), tau, L, DeviceLayer)
+
+
+def test_cfg4_stress_sampled():
+    """Stress layer (1 + 63 DAG, prefix 16384, block 64) at full size; outputs compared on
+    sampled slots that the oracle evaluates one by one (roots, deep fold chains, the last
+    slot)."""
+    L, DeviceLayer = _dev()
+    cfg = CONFIGS[4]
+    w = _workload(cfg)
+    rng = np.random.default_rng(0)
+    slots = [(0, 0), (0, cfg.block - 1), (cfg.num_nodes - 1, cfg.block - 1), (6, 5), (5, 40)]
+    slots += [(int(rng.integers(0, cfg.num_nodes)), int(rng.integers(0, cfg.block)))
+              for _ in range(27)]
+    _check_layer(cfg, w, cfg.tau, L, DeviceLayer, slots=slots)
