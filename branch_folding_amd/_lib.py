@@ -79,7 +79,8 @@ _SIGS = {
                                                      ctypes.c_float, ctypes.POINTER(FoldState),
                                                      ctypes.c_uint32, _P, ctypes.c_size_t, _P,
                                                      ctypes.POINTER(Probe)]),
-    "specfold_workspace_offset": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32]),
+    "specfold_workspace_offset": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32,
+                                                     ctypes.POINTER(ctypes.c_int64)]),
     "specfold_last_error": (ctypes.c_char_p, []),
     "specfold_version": (ctypes.c_int32, []),
 }
@@ -164,11 +165,13 @@ def specfold_layer_workspace_bytes(shape: Shape) -> int:
     return n
 
 
-def specfold_workspace_offset(shape: Shape, which: int) -> int:
-    off = int(lib().specfold_workspace_offset(ctypes.byref(shape), int(which)))
+def specfold_workspace_offset(shape: Shape, which: int):
+    """(byte offset, row stride in elements) of a workspace intermediate."""
+    ld = ctypes.c_int64(0)
+    off = int(lib().specfold_workspace_offset(ctypes.byref(shape), int(which), ctypes.byref(ld)))
     if off == ctypes.c_size_t(-1).value:
         raise SpecFoldError(SPECFOLD_ERR_INVALID_ARGUMENT, last_error())
-    return off
+    return off, int(ld.value)
 
 
 def specfold_layer_forward(shape: Shape, weights: dict, prefix, hidden_in, hidden_out,

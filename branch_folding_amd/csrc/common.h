@@ -66,6 +66,13 @@ __device__ __forceinline__ uint4 pack16(const float (&f)[4], float) {
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
+// Streaming load: data read exactly once (weights), marked non-temporal so it does not
+// displace reused data (the shared activation tile) from the caches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ void st16(void* p, const uint4& v) {
   *reinterpret_cast<uint4*>(p) = v;
 }

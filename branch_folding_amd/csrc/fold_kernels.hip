@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(kPackThreads) resolve_pack_kernel(
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_gather_kernel(
     const T* __restrict__ X, const int32_t* __restrict__ rows, const int32_t* __restrict__ count,
-    int cap, int S, int d, float eps, const T* __restrict__ g, T* __restrict__ out) {
+    int cap, int S, int d, float eps, const T* __restrict__ g, T* __restrict__ out, int ld_out) {
   const int lane = threadIdx.x & 63;
   const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int K = imin(*count, cap);
@@ -199,7 +199,7 @@ __global__ void __launch_bounds__(256) rmsnorm_gather_kernel(
   }
   ss = wave_sum(ss);
   const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
-  T* o = out + (size_t)k * d;
+  T* o = out + (size_t)k * ld_out;
   for (int ch = lane; ch < chunks; ch += 64) {
     float f[VE], w[VE];
     unpack16(ld16(x + ch * VE), f, T());
@@ -271,9 +271,9 @@ hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src
 template <typename T>
 hipError_t launch_rmsnorm_gather(const void* X, const int32_t* rows, const int32_t* count,
                                  int cap, int S, int d, float eps, const void* g, void* out,
-                                 hipStream_t st) {
+                                 int ld_out, hipStream_t st) {
   rmsnorm_gather_kernel<T><<<ceil_div(cap, 4), 256, 0, st>>>(
-      (const T*)X, rows, count, cap, S, d, eps, (const T*)g, (T*)out);
+      (const T*)X, rows, count, cap, S, d, eps, (const T*)g, (T*)out, ld_out);
   return hipGetLastError();
 }
 
@@ -293,9 +293,11 @@ template hipError_t launch_gate<float>(const void*, const int32_t*, int, int, in
 template hipError_t launch_gate<bf16>(const void*, const int32_t*, int, int, int, float, float*,
                                       uint8_t*, hipStream_t);
 template hipError_t launch_rmsnorm_gather<float>(const void*, const int32_t*, const int32_t*, int,
-                                                 int, int, float, const void*, void*, hipStream_t);
+                                                 int, int, float, const void*, void*, int,
+                                                 hipStream_t);
 template hipError_t launch_rmsnorm_gather<bf16>(const void*, const int32_t*, const int32_t*, int,
-                                                int, int, float, const void*, void*, hipStream_t);
+                                                int, int, float, const void*, void*, int,
+                                                hipStream_t);
 template hipError_t launch_combine<float>(const void*, const void*, const int32_t*, const int32_t*,
                                           int, int, int, void*, hipStream_t);
 template hipError_t launch_combine<bf16>(const void*, const void*, const int32_t*, const int32_t*,

@@ -3,12 +3,22 @@
 //
 //   C[M, N] = A[M, Kd] . W[N, Kd]^T     A = packed activations, W = [out, in] weights
 //
-// M (the packed row count) is known only on the device, so the kernel is persistent: a
-// fixed grid reads M, derives the tile count and a split-K factor, and walks the work
-// units.  Units are laid out so that each XCD owns a contiguous range (the M tiles of one
-// weight tile run side by side on one XCD and share it through that XCD's L2).
-// Workgroup tile 128 x 128 x 128 bytes of K, 4 waves (2 x 2), each wave 64 x 64 with
-// 16x16 MFMA tiles; operands staged through double-buffered, padded LDS.
+// With few packed rows these GEMMs stream the weights from HBM, so the kernel is shaped by
+// how the CU memory pipeline behaves on MI355X:
+//   * weight and activation tiles are fetched with fully coalesced 16-byte loads (8 lanes
+//     cover one 128-byte row segment), staged through padded LDS and read back in MFMA
+//     operand layout -- loading straight into operand layout (16 rows x 64 bytes per
+//     instruction) measured ~20% slower for the same bytes;
+//   * every workgroup re-reads the whole (small) activation tile from L2, and those hits
+//     occupy the same L1 request slots as the weight misses, so wide-N GEMMs use 256-column
+//     tiles (8 waves) to halve that traffic;
+//   * M (the packed row count) is known only on the device, so the kernel is persistent: a
+//     fixed grid reads M, derives the tile count and a split-K factor, and walks the work
+//     units, XCD-major so the M tiles of one weight tile share an XCD's L2.
+// Split-K partial sums (fp32) are reduced by a separate kernel in split order, so results
+// are deterministic and no device-scope fences are needed.
+// Wave tile 64 x 64 (4 x 4 MFMA 16x16 tiles); a k-iteration is 128 bytes of K; loads run
+// two k-iterations ahead through a register ring, staged into double-buffered LDS.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,42 +28,52 @@ template <typename T>
 struct GemmTile {
   static constexpr int VE = 16 / sizeof(T);               // elements per 16 bytes
   static constexpr int BK = kGemmBKBytes / sizeof(T);     // elements per k-iteration
-  static constexpr int LDR = BK + VE;                     // LDS row stride (16-byte pad)
-  static constexpr int kRowChunks = kGemmBKBytes / 16;    // 16-byte chunks per tile row
+  // LDS row stride: 32 bytes of padding make the 16-byte operand reads of 16 rows x 2 lane
+  // groups conflict-free on gfx950's LDS (16 bytes of padding measured ~2.9 conflict
+  // cycles per LDS instruction).
+  static constexpr int LDR = BK + 2 * VE;
 };
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
 
 // W row feeding logical tile column c.  SwiGLU interleaves 16-column blocks of the gate
 // and up projections so one lane ends up holding both halves of an output element.
-template <int EPI>
+template <int EPI, int BN>
 __device__ __forceinline__ int w_row_of(int c, int N, int ff) {
   if (EPI == kEpiSwiGLU) {
-    const int t = c / kGemmBN, cc = c % kGemmBN, blk = cc / 16;
-    const int j = t * (kGemmBN / 2) + (blk / 2) * 16 + (cc % 16);
+    const int t = c / BN, cc = c % BN, blk = cc / 16;
+    const int j = t * (BN / 2) + (blk / 2) * 16 + (cc % 16);
     return (blk & 1) ? ff + j : j;
   }
   return c < N ? c : N - 1;
 }
 
-template <typename T, int EPI>
-__global__ void __launch_bounds__(256, 2) gemm_kernel(GemmParams p) {
+// k-iterations in flight in registers per thread (ring slots).
+template <int BN> struct GemmDepth { static constexpr int PD = 2; };
+
+template <typename T, int EPI, int BN>
+__global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
   using G = GemmTile<T>;
-  constexpr int VE = G::VE, BK = G::BK, LDR = G::LDR;
+  constexpr int VE = G::VE, LDR = G::LDR;
+  constexpr int NT = BN * 2;                 // threads
+  constexpr int WN = BN / 64;                // waves along N
+  constexpr int AJ = kGemmBM * 8 / NT;       // 16-byte A chunks per thread per k-iteration
+  constexpr int WJ = BN * 8 / NT;            // 16-byte W chunks per thread per k-iteration
+  constexpr int RSTEP = NT / 8;              // rows covered by one pass of the loader
   __shared__ __attribute__((aligned(16))) T As[2][kGemmBM * LDR];
-  __shared__ __attribute__((aligned(16))) T Ws[2][kGemmBN * LDR];
+  __shared__ __attribute__((aligned(16))) T Ws[2][BN * LDR];
 
   const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
   if (M <= 0) return;
-  const int mb = ceil_div(M, kGemmBM), nt = ceil_div(p.N, kGemmBN);
-  const int kiters = p.Kd / BK;
+  const int mb = ceil_div(M, kGemmBM), nt = ceil_div(p.N, BN);
+  const int kiters = p.Kd / G::BK;
   const int tiles = mb * nt;
   const int split = gemm_split(tiles, kiters);
   const int units = tiles * split;
   const int per_xcd = ceil_div(units, 8);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int g4 = lane >> 4, l16 = lane & 15;
   const char* Ab = (const char*)p.A;
   const char* Wb = (const char*)p.W;
@@ -63,37 +83,39 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmParams p) {
     if (v >= units) continue;
     const int tile = v / split, s = v - tile * split;
     const int mt = tile % mb, ntile = tile / mb;
-    const int m0 = mt * kGemmBM, n0 = ntile * kGemmBN;
+    const int m0 = mt * kGemmBM, n0 = ntile * BN;
     const int kb = (int)((long)s * kiters / split), ke = (int)((long)(s + 1) * kiters / split);
 
-    // loader: thread handles 16-byte chunks (row = tid/8 + 32 j, chunk col = tid%8)
-    const char* a_src[4];
-    const char* w_src[4];
     const int lrow = tid >> 3, lcol = tid & 7;
+    const char* a_src[AJ];
+    const char* w_src[WJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = lrow + 32 * j;
-      const int ar = imin(m0 + r, M - 1);
+    for (int j = 0; j < AJ; ++j) {
+      const int ar = imin(m0 + lrow + RSTEP * j, M - 1);
       a_src[j] = Ab + ((size_t)ar * p.lda + (size_t)lcol * VE) * sizeof(T);
-      const int wr = w_row_of<EPI>(n0 + r, p.N, p.ff);
+    }
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      const int wr = w_row_of<EPI, BN>(n0 + lrow + RSTEP * j, p.N, p.ff);
       w_src[j] = Wb + ((size_t)wr * p.ldw + (size_t)lcol * VE) * sizeof(T);
     }
-    uint4 ra[4], rw[4];
-    auto gload = [&](int it) {
-      const size_t off = (size_t)it * kGemmBKBytes;
+    constexpr int PD = GemmDepth<BN>::PD;
+    uint4 ra[PD][AJ], rw[PD][WJ];
+    // loads past the unit's last k-iteration are clamped to it (cache hits, unused)
+    auto gload = [&](int slot, int it) {
+      const size_t off = (size_t)imin(it, ke - 1) * kGemmBKBytes;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ra[j] = ld16(a_src[j] + off);
-        rw[j] = ld16(w_src[j] + off);
-      }
+      for (int j = 0; j < WJ; ++j) rw[slot][j] = ld16(w_src[j] + off);
+#pragma unroll
+      for (int j = 0; j < AJ; ++j) ra[slot][j] = ld16(a_src[j] + off);
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf, int slot) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = lrow + 32 * j;
-        *reinterpret_cast<uint4*>(&As[buf][r * LDR + lcol * VE]) = ra[j];
-        *reinterpret_cast<uint4*>(&Ws[buf][r * LDR + lcol * VE]) = rw[j];
-      }
+      for (int j = 0; j < AJ; ++j)
+        *reinterpret_cast<uint4*>(&As[buf][(lrow + RSTEP * j) * LDR + lcol * VE]) = ra[slot][j];
+#pragma unroll
+      for (int j = 0; j < WJ; ++j)
+        *reinterpret_cast<uint4*>(&Ws[buf][(lrow + RSTEP * j) * LDR + lcol * VE]) = rw[slot][j];
     };
 
     f32x4 acc[4][4];
@@ -101,13 +123,10 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmParams p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool rows_live = (m0 + wm * 64) < M;
 
-    gload(kb);
-    lstore(0);
-    __syncthreads();
-    for (int it = kb; it < ke; ++it) {
-      const int cur = (it - kb) & 1;
-      if (it + 1 < ke) gload(it + 1);
+    auto compute = [&](int cur) {
+      if (!rows_live) return;
       const T* as = As[cur];
       const T* ws = Ws[cur];
 #pragma unroll
@@ -125,9 +144,29 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmParams p) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = mma_kstep(af[i], bfr[j], acc[i][j], T());
       }
-      if (it + 1 < ke) lstore(cur ^ 1);
+    };
+    // One k-iteration: refill the register slot whose data is already in LDS, run the
+    // MFMAs, stage the next iteration into the other LDS buffer.  Whole ring turns run
+    // without per-iteration conditions so the wait counts stay PD - 1 iterations deep.
+    // LDS buffer parity is relative to the unit's first k-iteration (staged into buffer 0)
+    auto step = [&](int q, int it) {
+      gload(q, it + PD);
+      compute((it - kb) & 1);
+      lstore((it - kb + 1) & 1, (q + 1) % PD);
       __syncthreads();
+    };
+#pragma unroll
+    for (int q = 0; q < PD; ++q) gload(q, kb + q);
+    lstore(0, 0);
+    __syncthreads();
+    int it = kb;
+    for (; it + PD <= ke; it += PD) {
+#pragma unroll
+      for (int q = 0; q < PD; ++q) step(q, it + q);
     }
+#pragma unroll
+    for (int q = 0; q < PD - 1; ++q)
+      if (it + q < ke) step(q, it + q);
 
     // epilogue: lane holds rows (g4*4 + r) and column l16 of every 16x16 tile
     if (split == 1) {
@@ -137,7 +176,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmParams p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
-            const int col = ntile * (kGemmBN / 2) + (wn * 2 + jj) * 16 + l16;
+            const int col = ntile * (BN / 2) + (wn * 2 + jj) * 16 + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int row = m0 + wm * 64 + i * 16 + g4 * 4 + r;
@@ -158,9 +197,9 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmParams p) {
             for (int r = 0; r < 4; ++r) {
               const int row = m0 + wm * 64 + i * 16 + g4 * 4 + r;
               if (row < M && col < p.N) {
-                float v = acc[i][j][r];
-                if (EPI == kEpiResidual) v += to_f32(R[(size_t)row * p.ldr + col]);
-                C[(size_t)row * p.ldc + col] = from_f32<T>(v);
+                float x = acc[i][j][r];
+                if (EPI == kEpiResidual) x += to_f32(R[(size_t)row * p.ldr + col]);
+                C[(size_t)row * p.ldc + col] = from_f32<T>(x);
               }
             }
           }
@@ -182,44 +221,64 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmParams p) {
   }
 }
 
-// Sums the split-K partials in split order and applies the epilogue.
-template <typename T, int EPI>
+// Sums the split-K partials in split order and applies the epilogue (4 outputs / thread).
+template <typename T, int EPI, int BN>
 __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
   const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
   if (M <= 0) return;
-  const int mb = ceil_div(M, kGemmBM), nt = ceil_div(p.N, kGemmBN);
+  const int mb = ceil_div(M, kGemmBM), nt = ceil_div(p.N, BN);
   const int kiters = p.Kd / (kGemmBKBytes / (int)sizeof(T));
   const int split = gemm_split(mb * nt, kiters);
   if (split == 1) return;
   const int Nout = (EPI == kEpiSwiGLU) ? p.ff : p.N;
-  const long total = (long)M * Nout;
+  const int q4 = Nout / 4;                      // Nout is a multiple of 64
+  const long total = (long)M * q4;
   const size_t plane = (size_t)M * p.N;
   T* C = (T*)p.C;
   for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (long)gridDim.x * blockDim.x) {
-    const int row = (int)(idx / Nout), col = (int)(idx - (long)row * Nout);
-    float v;
+    const int row = (int)(idx / q4), col = (int)(idx - (long)row * q4) * 4;
+    float v[4];
     if (EPI == kEpiSwiGLU) {
-      const int t = col / (kGemmBN / 2), cc = col % (kGemmBN / 2);
-      const int lg = t * kGemmBN + (cc / 16) * 32 + (cc % 16);
-      float gs = 0.f, us = 0.f;
+      // 4 consecutive outputs share a 16-column block: gate at lg, up at lg + 16
+      const int t = col / (BN / 2), cc = col % (BN / 2);
+      const int lg = t * BN + (cc / 16) * 32 + (cc % 16);
+      float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
       for (int s = 0; s < split; ++s) {
-        gs += p.partial[s * plane + (size_t)row * p.N + lg];
-        us += p.partial[s * plane + (size_t)row * p.N + lg + 16];
+        const float* ps = p.partial + s * plane + (size_t)row * p.N;
+        const float4 a = *reinterpret_cast<const float4*>(ps + lg);
+        const float4 b = *reinterpret_cast<const float4*>(ps + lg + 16);
+        gs.x += a.x; gs.y += a.y; gs.z += a.z; gs.w += a.w;
+        us.x += b.x; us.y += b.y; us.z += b.z; us.w += b.w;
       }
-      v = silu_f(gs) * us;
+      v[0] = silu_f(gs.x) * us.x; v[1] = silu_f(gs.y) * us.y;
+      v[2] = silu_f(gs.z) * us.z; v[3] = silu_f(gs.w) * us.w;
     } else {
-      v = 0.f;
-      for (int s = 0; s < split; ++s) v += p.partial[s * plane + (size_t)row * p.N + col];
-      if (EPI == kEpiResidual) v += to_f32(((const T*)p.R)[(size_t)row * p.ldr + col]);
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = 0; s < split; ++s) {
+        const float4 b = *reinterpret_cast<const float4*>(p.partial + s * plane +
+                                                          (size_t)row * p.N + col);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      if (EPI == kEpiResidual) {
+        const T* R = (const T*)p.R + (size_t)row * p.ldr + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += to_f32(R[e]);
+      }
     }
-    C[(size_t)row * p.ldc + col] = from_f32<T>(v);
+    T* out = C + (size_t)row * p.ldc + col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = from_f32<T>(v[e]);
   }
 }
 
+int gemm_tile_n(int N) { return (N / 256 >= kGemmMinTiles) ? 256 : 128; }
+
 size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes) {
+  const int BN = gemm_tile_n(N);
   const int kiters = Kd / (kGemmBKBytes / elem_bytes);
-  const int nt = ceil_div(N, kGemmBN);
+  const int nt = ceil_div(N, BN);
   size_t best = 0;
   for (int mb = 1; mb <= ceil_div(m_cap, kGemmBM); ++mb) {
     const int split = gemm_split(mb * nt, kiters);
@@ -231,29 +290,34 @@ size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes) {
   return best;
 }
 
-template <typename T>
-hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st) {
-  const int grid = 2 * num_cu;
-  const int Nout = (epi == kEpiSwiGLU) ? p.ff : p.N;
-  const long total = (long)p.m_cap * Nout;
-  const int rgrid = (int)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
-  switch (epi) {
-    case kEpiStore:
-      gemm_kernel<T, kEpiStore><<<grid, 256, 0, st>>>(p);
-      gemm_reduce_kernel<T, kEpiStore><<<rgrid, 256, 0, st>>>(p);
-      break;
-    case kEpiResidual:
-      gemm_kernel<T, kEpiResidual><<<grid, 256, 0, st>>>(p);
-      gemm_reduce_kernel<T, kEpiResidual><<<rgrid, 256, 0, st>>>(p);
-      break;
-    case kEpiSwiGLU:
-      gemm_kernel<T, kEpiSwiGLU><<<grid, 256, 0, st>>>(p);
-      gemm_reduce_kernel<T, kEpiSwiGLU><<<rgrid, 256, 0, st>>>(p);
-      break;
-    default:
-      return hipErrorInvalidValue;
+template <typename T, int EPI, int BN>
+static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st) {
+  const int grid = (BN == 256 ? 1 : 2) * num_cu;
+  gemm_kernel<T, EPI, BN><<<grid, BN * 2, 0, st>>>(p);
+  // the reduction only runs when some row count could make the device choose split > 1
+  if (ceil_div(p.N, BN) < kGemmMinTiles) {
+    const int Nout = (EPI == kEpiSwiGLU) ? p.ff : p.N;
+    const long total = (long)p.m_cap * (Nout / 4);
+    const int rgrid = (int)((total + 255) / 256 < 2048 ? (total + 255) / 256 : 2048);
+    gemm_reduce_kernel<T, EPI, BN><<<rgrid, 256, 0, st>>>(p);
   }
   return hipGetLastError();
+}
+
+template <typename T, int EPI>
+static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t st) {
+  return gemm_tile_n(p.N) == 256 ? launch_gemm_bn<T, EPI, 256>(p, num_cu, st)
+                                 : launch_gemm_bn<T, EPI, 128>(p, num_cu, st);
+}
+
+template <typename T>
+hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st) {
+  switch (epi) {
+    case kEpiStore: return launch_gemm_epi<T, kEpiStore>(p, num_cu, st);
+    case kEpiResidual: return launch_gemm_epi<T, kEpiResidual>(p, num_cu, st);
+    case kEpiSwiGLU: return launch_gemm_epi<T, kEpiSwiGLU>(p, num_cu, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template hipError_t launch_gemm<float>(const GemmParams&, int, int, hipStream_t);

@@ -23,7 +23,7 @@ hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src
 template <typename T>
 hipError_t launch_rmsnorm_gather(const void* X, const int32_t* rows, const int32_t* count,
                                  int cap, int S, int d, float eps, const void* g, void* out,
-                                 hipStream_t st);
+                                 int ld_out, hipStream_t st);
 template <typename T>
 hipError_t launch_combine(const void* h, const void* F, const int32_t* slot_row,
                           const int32_t* count, int cap, int S, int d, void* y, hipStream_t st);
@@ -52,15 +52,16 @@ struct GemmParams {
 };
 
 constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;
 constexpr int kGemmBKBytes = 128;
 constexpr int kGemmMaxSplit = 16;
+// Tile counts at or above this keep every CU streaming without splitting K.
+constexpr int kGemmMinTiles = 128;
 
 // Split-K factor chosen on the device from the tile count (the packed row count is only
-// known there); the reduction kernel recomputes it with the same function.
+// known there); kiters = number of 128-byte k-iterations.
 __host__ __device__ inline int gemm_split(int tiles, int kiters) {
   if (tiles <= 0) return 1;
-  if (tiles >= kPlanCUs) return 1;
+  if (tiles >= kGemmMinTiles) return 1;
   int s = (kPlanCUs + tiles - 1) / tiles;
   int smax = kiters / 4;
   if (smax < 1) smax = 1;
@@ -73,6 +74,8 @@ template <typename T>
 hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st);
 // fp32 elements of split-K partial storage any GEMM with these bounds may use
 size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes);
+// N-tile width used for a GEMM with N output columns (256 for wide, 128 otherwise)
+int gemm_tile_n(int N);
 
 // ---------------------------------------------------------------------------------------
 // Attention.  Prefix phase: online-softmax partials of every packed row's queries over the

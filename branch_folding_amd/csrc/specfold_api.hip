@@ -98,11 +98,17 @@ int num_cus() {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Row stride (elements) of a workspace activation matrix with `cols` columns: one extra
+// 128-byte cache line per row, so rows that many workgroups read at the same column do not
+// all map to the same few L2 channels.
+size_t padded_ld(size_t cols, size_t eb) { return cols + 128 / eb; }
+
 // Workspace layout of one layer.
 struct Layout {
   size_t ratio, rec, src, packed, slot_row, count;
   size_t a1, qkv, part_o, part_lse, attn, h, a2, G, F, gpart;
   size_t total;
+  size_t ld_d, ld_qkv, ld_q, ld_ff;   // padded row strides (elements)
 };
 
 Layout layout_of(const specfold_shape* s) {
@@ -120,6 +126,10 @@ Layout layout_of(const specfold_shape* s) {
   gp = std::max(gp, gemm_partial_elems((int)S, (int)(2 * ff), (int)d, ebi));
   gp = std::max(gp, gemm_partial_elems((int)S, (int)d, (int)ff, ebi));
   Layout L;
+  L.ld_d = padded_ld(d, eb);
+  L.ld_qkv = padded_ld(qkvd, eb);
+  L.ld_q = padded_ld(qd, eb);
+  L.ld_ff = padded_ld(ff, eb);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -132,14 +142,14 @@ Layout layout_of(const specfold_shape* s) {
   L.packed = take(S * 4);
   L.slot_row = take(S * 4);
   L.count = take(256);
-  L.a1 = take(S * d * eb);
-  L.qkv = take(S * qkvd * eb);
+  L.a1 = take(S * L.ld_d * eb);
+  L.qkv = take(S * L.ld_qkv * eb);
   L.part_o = take(prow * qd * 4);
   L.part_lse = take(prow * (size_t)s->n_q_heads * 4);
-  L.attn = take(S * qd * eb);
+  L.attn = take(S * L.ld_q * eb);
   L.h = take(S * d * eb);
-  L.a2 = take(S * d * eb);
-  L.G = take(S * ff * eb);
+  L.a2 = take(S * L.ld_d * eb);
+  L.G = take(S * L.ld_ff * eb);
   L.F = take(S * d * eb);
   L.gpart = take(gp * 4);
   L.total = off;
@@ -181,25 +191,26 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   float* gpart = (float*)(ws + L.gpart);
 
   HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM1, true));
-  HIP_CHECK(launch_rmsnorm_gather<T>(hin, packed, count, S, S, d, s->rms_eps, w->rms1, A1, st));
+  HIP_CHECK(launch_rmsnorm_gather<T>(hin, packed, count, S, S, d, s->rms_eps, w->rms1, A1,
+                                     (int)L.ld_d, st));
   HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM1, false));
 
   GemmParams gp{};
-  gp.A = A1; gp.lda = d; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = qkvd;
+  gp.A = A1; gp.lda = L.ld_d; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = L.ld_qkv;
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = qkvd; gp.Kd = d;
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, false));
 
   AttnParams ap{};
-  ap.qkv = QKV; ap.ld_qkv = qkvd; ap.n_q = nq; ap.n_kv = nkv; ap.dh = dh;
+  ap.qkv = QKV; ap.ld_qkv = L.ld_qkv; ap.n_q = nq; ap.n_kv = nkv; ap.dh = dh;
   ap.count = count; ap.cap = S;
   ap.pk = prefix ? prefix->k : nullptr; ap.pv = prefix ? prefix->v : nullptr;
   ap.stride_tok = prefix ? prefix->stride_tok : 0; ap.stride_head = prefix ? prefix->stride_head : 0;
   ap.P = s->prefix_len;
   ap.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
   ap.part_o = (float*)(ws + L.part_o); ap.part_lse = (float*)(ws + L.part_lse);
-  ap.S = S; ap.slot_row = slot_row; ap.N = N; ap.B = B; ap.out = ATT; ap.ld_out = qd;
+  ap.S = S; ap.slot_row = slot_row; ap.N = N; ap.B = B; ap.out = ATT; ap.ld_out = L.ld_q;
   HIP_CHECK(mark(SPECFOLD_STEP_ATTN_PREFIX, true));
   HIP_CHECK(launch_attn_prefix<T>(ap, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_ATTN_PREFIX, false));
@@ -208,7 +219,7 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   HIP_CHECK(mark(SPECFOLD_STEP_ATTN_BLOCK, false));
 
   gp = GemmParams{};
-  gp.A = ATT; gp.lda = qd; gp.W = w->w_o; gp.ldw = qd; gp.C = Hh; gp.ldc = d;
+  gp.A = ATT; gp.lda = L.ld_q; gp.W = w->w_o; gp.ldw = qd; gp.C = Hh; gp.ldc = d;
   gp.R = hin; gp.ldr = d; gp.partial = gpart; gp.m_dev = nullptr; gp.m_cap = S; gp.N = d;
   gp.Kd = qd;
   HIP_CHECK(mark(SPECFOLD_STEP_O_PROJ, true));
@@ -216,18 +227,19 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   HIP_CHECK(mark(SPECFOLD_STEP_O_PROJ, false));
 
   HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM2, true));
-  HIP_CHECK(launch_rmsnorm_gather<T>(Hh, packed, count, S, S, d, s->rms_eps, w->rms2, A2, st));
+  HIP_CHECK(launch_rmsnorm_gather<T>(Hh, packed, count, S, S, d, s->rms_eps, w->rms2, A2,
+                                     (int)L.ld_d, st));
   HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM2, false));
 
   gp = GemmParams{};
-  gp.A = A2; gp.lda = d; gp.W = w->w_gate_up; gp.ldw = d; gp.C = G; gp.ldc = ff;
+  gp.A = A2; gp.lda = L.ld_d; gp.W = w->w_gate_up; gp.ldw = d; gp.C = G; gp.ldc = L.ld_ff;
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = 2 * ff; gp.Kd = d; gp.ff = ff;
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiSwiGLU, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, false));
 
   gp = GemmParams{};
-  gp.A = G; gp.lda = ff; gp.W = w->w_down; gp.ldw = ff; gp.C = F; gp.ldc = d;
+  gp.A = G; gp.lda = L.ld_ff; gp.W = w->w_down; gp.ldw = ff; gp.C = F; gp.ldc = d;
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = d; gp.Kd = ff;
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_DOWN, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
@@ -295,14 +307,16 @@ size_t specfold_layer_workspace_bytes(const specfold_shape* shape) {
   return layout_of(shape).total;
 }
 
-size_t specfold_workspace_offset(const specfold_shape* shape, int32_t which) {
+size_t specfold_workspace_offset(const specfold_shape* shape, int32_t which, int64_t* ld) {
   if (check_shape(shape, true) != SPECFOLD_OK) return SIZE_MAX;
   const Layout L = layout_of(shape);
+  int64_t dummy;
+  if (!ld) ld = &dummy;
   switch (which) {
-    case SPECFOLD_T_QKV: return L.qkv;
-    case SPECFOLD_T_ATTN: return L.attn;
-    case SPECFOLD_T_H: return L.h;
-    case SPECFOLD_T_FFN: return L.F;
+    case SPECFOLD_T_QKV: *ld = (int64_t)L.ld_qkv; return L.qkv;
+    case SPECFOLD_T_ATTN: *ld = (int64_t)L.ld_q; return L.attn;
+    case SPECFOLD_T_H: *ld = shape->hidden; return L.h;
+    case SPECFOLD_T_FFN: *ld = shape->hidden; return L.F;
     default:
       fail(SPECFOLD_ERR_INVALID_ARGUMENT, "unknown tensor id %d", which);
       return SIZE_MAX;

@@ -90,12 +90,12 @@ class DeviceLayer:
     def intermediate(self, which: int) -> torch.Tensor:
         """View of a workspace tensor after the stream has synchronised."""
         cfg = self.cfg
-        off = L.specfold_workspace_offset(self.shape, which)
+        off, ld = L.specfold_workspace_offset(self.shape, which)
         S = cfg.slots
         cols = {L.SPECFOLD_T_QKV: cfg.qkv_dim, L.SPECFOLD_T_ATTN: cfg.n_q * cfg.head_dim,
                 L.SPECFOLD_T_H: cfg.hidden, L.SPECFOLD_T_FFN: cfg.hidden}[which]
         es = torch.tensor([], dtype=self.dt).element_size()
-        return self.ws[off: off + S * cols * es].view(self.dt).view(S, cols)
+        return self.ws[off: off + S * ld * es].view(self.dt).view(S, ld)[:, :cols]
 
     def output_numpy(self) -> np.ndarray:
         cfg = self.cfg

@@ -227,7 +227,9 @@ specfold_status specfold_layer_forward_probed(const specfold_shape* shape,
 
 /* Intermediates of the last specfold_layer_forward that are kept in the workspace, for
  * inspection after the stream has synchronised.  Row k of a packed tensor is packed row
- * k (k < K); slot tensors have S rows.  All are row-major in shape->dtype.            */
+ * k (k < K); slot tensors have S rows.  All are row-major in shape->dtype with the row
+ * stride returned by specfold_workspace_offset (packed activations carry one extra
+ * 128-byte line per row).                                                              */
 typedef enum specfold_tensor {
   SPECFOLD_T_QKV = 0,    /* [S cap, (n_q + 2 n_kv) dh] packed Q|K|V rows          */
   SPECFOLD_T_ATTN = 1,   /* [S, n_q dh] attention output of every slot            */
@@ -235,8 +237,9 @@ typedef enum specfold_tensor {
   SPECFOLD_T_FFN = 3     /* [S cap, d] packed FFN output rows                     */
 } specfold_tensor;
 
-/* Byte offset of tensor `which` inside the workspace (SIZE_MAX on invalid input). */
-size_t specfold_workspace_offset(const specfold_shape* shape, int32_t which);
+/* Byte offset of tensor `which` inside the workspace (SIZE_MAX on invalid input); the row
+ * stride in elements is stored to *ld_elems when ld_elems is non-NULL. */
+size_t specfold_workspace_offset(const specfold_shape* shape, int32_t which, int64_t* ld_elems);
 
 /* Message of the last failed call on this host thread ("" if none). */
 const char* specfold_last_error(void);

@@ -43,8 +43,8 @@ def test_workspace_sizes():
         eb = 2 if cfg.dtype == "bf16" else 4
         assert n >= S * cfg.ffn * eb + 4 * S * cfg.hidden * eb
         for which in range(4):
-            off = L.specfold_workspace_offset(sh, which)
-            assert off % 256 == 0 and off < n
+            off, ld = L.specfold_workspace_offset(sh, which)
+            assert off % 256 == 0 and off < n and ld >= cfg.hidden
     assert L.specfold_layer_workspace_bytes(shape_of(CONFIGS[1], prefix_len=0)) > 0
 
 
