@@ -55,9 +55,12 @@ class HipEvents:
         assert self.h.hipEventRecord(ev, stream) == 0
 
     def ms(self, a, b):
+        """Elapsed ms between two recorded events (None if the pair was never recorded)."""
         assert self.h.hipEventSynchronize(b) == 0
         v = ctypes.c_float()
-        assert self.h.hipEventElapsedTime(ctypes.byref(v), a, b) == 0
+        if self.h.hipEventElapsedTime(ctypes.byref(v), a, b) != 0:
+            self.h.hipGetLastError()          # clear: the pair was never recorded
+            return None
         return v.value
 
     def destroy(self, evs):
@@ -119,7 +122,7 @@ def time_layer(dl, tau, steps, warmup, ev, stream, probe_step=None):
     ev.record(t1, stream)
     torch.cuda.synchronize()
     total = ev.ms(t0, t1)
-    per = [ev.ms(a, b) for a, b in zip(ps, pe)]
+    per = [x for x in (ev.ms(a, b) for a, b in zip(ps, pe)) if x is not None]
     ev.destroy([t0, t1] + ps + pe)
     return total / steps, per
 
@@ -129,7 +132,8 @@ def kernel_breakdown(dl, tau, reps, ev, stream):
     out = {}
     for idx, name in enumerate(L.STEPS):
         _, per = time_layer(dl, tau, reps, 2, ev, stream, probe_step=idx)
-        out[name] = sum(per) / len(per) * 1e3 if per else 0.0
+        if per:                      # steps fused into another launch record nothing
+            out[name] = sum(per) / len(per) * 1e3
     return out
 
 

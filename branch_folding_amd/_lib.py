@@ -53,7 +53,7 @@ class Probe(ctypes.Structure):
 
 
 STEPS = ["gate", "resolve_pack", "rmsnorm1", "qkv", "attn_prefix", "attn_block", "o_proj",
-         "rmsnorm2", "ffn_gate_up", "ffn_down", "combine"]
+         "o_finish", "ffn_gate_up", "ffn_down", "combine"]
 
 
 class FoldState(ctypes.Structure):

@@ -9,25 +9,29 @@ namespace specfold {
 // ------------------------------------------------------------------------------------
 // Gate (SpecFold explainer, paragraph on measuring ||H_child - H_parent|| / ||H_parent||
 // at the layer input).  One wave per slot; fp32 sums of squares; fold iff r <= tau.
+// The same pass yields the row's RMSNorm scale 1/sqrt(mean(H^2) + eps), which the QKV
+// GEMM applies while gathering the packed rows.
 // ------------------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
                                                    const int32_t* __restrict__ fold_src,
                                                    int N, int B, int d, float tau,
                                                    float* __restrict__ ratio,
-                                                   uint8_t* __restrict__ recompute) {
+                                                   uint8_t* __restrict__ recompute,
+                                                   float* __restrict__ rstd, float eps,
+                                                   int stats_only) {
   const int lane = threadIdx.x & 63;
   const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (slot >= N * B) return;
   const int n = slot / B, i = slot - n * B;
   int p = -1;
-  if (n > 0) p = fold_src[n];
+  if (n > 0 && !stats_only) p = fold_src[n];   // stats only: fold_src may be absent
   const bool has_parent = (n > 0) && (p >= 0) && (p < n);
   const T* c = H + (size_t)slot * d;
   const T* q = has_parent ? H + ((size_t)p * B + i) * d : c;
   constexpr int VE = Pack16<T>::kElems;
   const int chunks = d / VE;
-  float sd = 0.f, sp = 0.f;
+  float sd = 0.f, sp = 0.f, sc = 0.f;
   for (int ch = lane; ch < chunks; ch += 64) {
     float fc[VE], fp[VE];
     unpack16(ld16(c + ch * VE), fc, T());
@@ -37,11 +41,14 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
       const float df = fc[e] - fp[e];
       sd = fmaf(df, df, sd);
       sp = fmaf(fp[e], fp[e], sp);
+      sc = fmaf(fc[e], fc[e], sc);
     }
   }
   sd = wave_sum(sd);
   sp = wave_sum(sp);
-  if (lane == 0) {
+  sc = wave_sum(sc);
+  if (lane == 0 && rstd) rstd[slot] = 1.0f / sqrtf(sc / (float)d + eps);
+  if (lane == 0 && !stats_only) {
     float r;
     bool rec;
     if (!has_parent) {
@@ -211,6 +218,56 @@ __global__ void __launch_bounds__(256) rmsnorm_gather_kernel(
 }
 
 // ------------------------------------------------------------------------------------
+// O-projection finish: h = H + sum of the split-K partials, then the FFN's RMSNorm for the
+// rows that are packed.  One wave per slot; pass 2 re-reads the row this lane just wrote.
+// ------------------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) oproj_finish_kernel(
+    const float* __restrict__ partial, int split, const T* __restrict__ H, T* __restrict__ h,
+    int S, int d, const int32_t* __restrict__ slot_row, const int32_t* __restrict__ packed_slot,
+    const int32_t* __restrict__ count, const T* __restrict__ g, float eps, T* __restrict__ A2,
+    int ld_a2) {
+  const int lane = threadIdx.x & 63;
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= S) return;
+  constexpr int VE = Pack16<T>::kElems;
+  const int chunks = d / VE;
+  const size_t plane = (size_t)S * d;
+  float ss = 0.f;
+  for (int ch = lane; ch < chunks; ch += 64) {
+    float x[VE];
+    unpack16(ld16(H + (size_t)s * d + ch * VE), x, T());
+    for (int q = 0; q < split; ++q) {
+      const float* pp = partial + q * plane + (size_t)s * d + ch * VE;
+#pragma unroll
+      for (int e = 0; e < VE; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(pp + e);
+        x[e] += v.x; x[e + 1] += v.y; x[e + 2] += v.z; x[e + 3] += v.w;
+      }
+    }
+    const uint4 hv = pack16(x, T());
+    st16(h + (size_t)s * d + ch * VE, hv);
+    float r[VE];
+    unpack16(hv, r, T());                       // statistics of the rounded h
+#pragma unroll
+    for (int e = 0; e < VE; ++e) ss = fmaf(r[e], r[e], ss);
+  }
+  ss = wave_sum(ss);
+  const int K = imin(*count, S);
+  const int k = imin(imax(slot_row[s], 0), imax(K - 1, 0));
+  if (K <= 0 || packed_slot[k] != s) return;     // not a packed row: no FFN input
+  const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int ch = lane; ch < chunks; ch += 64) {
+    float x[VE], w[VE];
+    unpack16(ld16(h + (size_t)s * d + ch * VE), x, T());
+    unpack16(ld16(g + ch * VE), w, T());
+#pragma unroll
+    for (int e = 0; e < VE; ++e) x[e] = x[e] * rstd * w[e];
+    st16(A2 + (size_t)k * ld_a2 + ch * VE, pack16(x, T()));
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Combine: y[s] = h[s] + F[slot_row[s]] (a folded slot keeps its own residual stream and
 // adds its source's FFN output).
 // ------------------------------------------------------------------------------------
@@ -244,10 +301,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ h,
 // ------------------------------------------------------------------------------------
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
-                       float* ratio, uint8_t* recompute, hipStream_t st) {
+                       float* ratio, uint8_t* recompute, float* rstd, float eps, bool stats_only,
+                       hipStream_t st) {
   const int S = N * B;
   gate_kernel<T><<<ceil_div(S, 4), 256, 0, st>>>((const T*)H, fold_src, N, B, d, tau, ratio,
-                                                 recompute);
+                                                 recompute, rstd, eps, stats_only ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -288,10 +346,27 @@ hipError_t launch_combine(const void* h, const void* F, const int32_t* slot_row,
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_oproj_finish(const float* partial, int split, const void* H, void* h, int S,
+                               int d, const int32_t* slot_row, const int32_t* packed_slot,
+                               const int32_t* count, const void* g, float eps, void* A2,
+                               int ld_a2, hipStream_t st) {
+  oproj_finish_kernel<T><<<ceil_div(S, 4), 256, 0, st>>>(partial, split, (const T*)H, (T*)h, S, d,
+                                                          slot_row, packed_slot, count,
+                                                          (const T*)g, eps, (T*)A2, ld_a2);
+  return hipGetLastError();
+}
+template hipError_t launch_oproj_finish<float>(const float*, int, const void*, void*, int, int,
+                                               const int32_t*, const int32_t*, const int32_t*,
+                                               const void*, float, void*, int, hipStream_t);
+template hipError_t launch_oproj_finish<bf16>(const float*, int, const void*, void*, int, int,
+                                              const int32_t*, const int32_t*, const int32_t*,
+                                              const void*, float, void*, int, hipStream_t);
+
 template hipError_t launch_gate<float>(const void*, const int32_t*, int, int, int, float, float*,
-                                       uint8_t*, hipStream_t);
+                                       uint8_t*, float*, float, bool, hipStream_t);
 template hipError_t launch_gate<bf16>(const void*, const int32_t*, int, int, int, float, float*,
-                                      uint8_t*, hipStream_t);
+                                      uint8_t*, float*, float, bool, hipStream_t);
 template hipError_t launch_rmsnorm_gather<float>(const void*, const int32_t*, const int32_t*, int,
                                                  int, int, float, const void*, void*, int,
                                                  hipStream_t);

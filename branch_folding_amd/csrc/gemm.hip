@@ -51,7 +51,9 @@ __device__ __forceinline__ int w_row_of(int c, int N, int ff) {
 // k-iterations in flight in registers per thread (ring slots).
 template <int BN> struct GemmDepth { static constexpr int PD = 2; };
 
-template <typename T, int EPI, int BN>
+// NORMA: the A operand is gathered through p.a_rows and RMS-normalised on its way into LDS
+// (row scale p.a_scale, column gain p.a_gain), which fuses the pre-attention RMSNorm.
+template <typename T, int EPI, int BN, bool NORMA>
 __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
   using G = GemmTile<T>;
   constexpr int VE = G::VE, LDR = G::LDR;
@@ -89,18 +91,24 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
     const int lrow = tid >> 3, lcol = tid & 7;
     const char* a_src[AJ];
     const char* w_src[WJ];
+    float a_sc[AJ];
 #pragma unroll
     for (int j = 0; j < AJ; ++j) {
-      const int ar = imin(m0 + lrow + RSTEP * j, M - 1);
+      int ar = imin(m0 + lrow + RSTEP * j, M - 1);
+      if (NORMA) {
+        ar = imin(imax(p.a_rows[ar], 0), p.a_rows_cap - 1);
+        a_sc[j] = p.a_scale[ar];
+      }
       a_src[j] = Ab + ((size_t)ar * p.lda + (size_t)lcol * VE) * sizeof(T);
     }
+    const char* g_src = NORMA ? (const char*)p.a_gain + (size_t)lcol * VE * sizeof(T) : nullptr;
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
       const int wr = w_row_of<EPI, BN>(n0 + lrow + RSTEP * j, p.N, p.ff);
       w_src[j] = Wb + ((size_t)wr * p.ldw + (size_t)lcol * VE) * sizeof(T);
     }
     constexpr int PD = GemmDepth<BN>::PD;
-    uint4 ra[PD][AJ], rw[PD][WJ];
+    uint4 ra[PD][AJ], rw[PD][WJ], rg[PD];
     // loads past the unit's last k-iteration are clamped to it (cache hits, unused)
     auto gload = [&](int slot, int it) {
       const size_t off = (size_t)imin(it, ke - 1) * kGemmBKBytes;
@@ -108,11 +116,22 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
       for (int j = 0; j < WJ; ++j) rw[slot][j] = ld16(w_src[j] + off);
 #pragma unroll
       for (int j = 0; j < AJ; ++j) ra[slot][j] = ld16(a_src[j] + off);
+      if (NORMA) rg[slot] = ld16(g_src + off);
     };
     auto lstore = [&](int buf, int slot) {
 #pragma unroll
-      for (int j = 0; j < AJ; ++j)
-        *reinterpret_cast<uint4*>(&As[buf][(lrow + RSTEP * j) * LDR + lcol * VE]) = ra[slot][j];
+      for (int j = 0; j < AJ; ++j) {
+        uint4 av = ra[slot][j];
+        if (NORMA) {
+          float x[VE], gv[VE];
+          unpack16(av, x, T());
+          unpack16(rg[slot], gv, T());
+#pragma unroll
+          for (int e = 0; e < VE; ++e) x[e] = x[e] * a_sc[j] * gv[e];
+          av = pack16(x, T());
+        }
+        *reinterpret_cast<uint4*>(&As[buf][(lrow + RSTEP * j) * LDR + lcol * VE]) = av;
+      }
 #pragma unroll
       for (int j = 0; j < WJ; ++j)
         *reinterpret_cast<uint4*>(&Ws[buf][(lrow + RSTEP * j) * LDR + lcol * VE]) = rw[slot][j];
@@ -169,7 +188,7 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
       if (it + q < ke) step(q, it + q);
 
     // epilogue: lane holds rows (g4*4 + r) and column l16 of every 16x16 tile
-    if (split == 1) {
+    if (split == 1 && EPI != kEpiPartial) {
       T* C = (T*)p.C;
       if (EPI == kEpiSwiGLU) {
 #pragma unroll
@@ -273,16 +292,21 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
   }
 }
 
-int gemm_tile_n(int N) { return (N / 256 >= kGemmMinTiles) ? 256 : 128; }
+int gemm_tile_n(int N) { return N >= 256 ? 256 : 128; }
 
-size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes) {
+int gemm_host_split(int M, int N, int Kd, int elem_bytes) {
+  const int BN = gemm_tile_n(N);
+  return gemm_split(ceil_div(M, kGemmBM) * ceil_div(N, BN), Kd / (kGemmBKBytes / elem_bytes));
+}
+
+size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always) {
   const int BN = gemm_tile_n(N);
   const int kiters = Kd / (kGemmBKBytes / elem_bytes);
   const int nt = ceil_div(N, BN);
   size_t best = 0;
   for (int mb = 1; mb <= ceil_div(m_cap, kGemmBM); ++mb) {
     const int split = gemm_split(mb * nt, kiters);
-    if (split > 1) {
+    if (split > 1 || always) {
       const size_t e = (size_t)split * (size_t)(mb * kGemmBM < m_cap ? mb * kGemmBM : m_cap) * N;
       if (e > best) best = e;
     }
@@ -293,9 +317,12 @@ size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes) {
 template <typename T, int EPI, int BN>
 static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st) {
   const int grid = (BN == 256 ? 1 : 2) * num_cu;
-  gemm_kernel<T, EPI, BN><<<grid, BN * 2, 0, st>>>(p);
+  if (p.a_rows)
+    gemm_kernel<T, EPI, BN, true><<<grid, BN * 2, 0, st>>>(p);
+  else
+    gemm_kernel<T, EPI, BN, false><<<grid, BN * 2, 0, st>>>(p);
   // the reduction only runs when some row count could make the device choose split > 1
-  if (ceil_div(p.N, BN) < kGemmMinTiles) {
+  if (EPI != kEpiPartial && ceil_div(p.N, BN) < kGemmMinTiles) {
     const int Nout = (EPI == kEpiSwiGLU) ? p.ff : p.N;
     const long total = (long)p.m_cap * (Nout / 4);
     const int rgrid = (int)((total + 255) / 256 < 2048 ? (total + 255) / 256 : 2048);
@@ -316,6 +343,7 @@ hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st)
     case kEpiStore: return launch_gemm_epi<T, kEpiStore>(p, num_cu, st);
     case kEpiResidual: return launch_gemm_epi<T, kEpiResidual>(p, num_cu, st);
     case kEpiSwiGLU: return launch_gemm_epi<T, kEpiSwiGLU>(p, num_cu, st);
+    case kEpiPartial: return launch_gemm_epi<T, kEpiPartial>(p, num_cu, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,9 +12,12 @@ namespace specfold {
 constexpr int kResolve = 1;
 constexpr int kPack = 2;
 
+// Gate; also writes rstd[slot] = 1/sqrt(mean(H[slot]^2) + eps) when rstd is non-null.
+// stats_only: write rstd only (fold state supplied by the caller).
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
-                       float* ratio, uint8_t* recompute, hipStream_t st);
+                       float* ratio, uint8_t* recompute, float* rstd, float eps, bool stats_only,
+                       hipStream_t st);
 size_t resolve_pack_lds_bytes(int S);
 hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,
                                const int32_t* src_in, int N, int B, int mode, int32_t* src_out,
@@ -32,7 +35,9 @@ hipError_t launch_combine(const void* h, const void* F, const int32_t* slot_row,
 // GEMM  C[M, N] = A[M, Kd] . W[N, Kd]^T  (both operands K-contiguous), M read on the
 // device.  Epilogues: plain store, + residual, SwiGLU (W = [gate; up], output [M, ff]).
 // ---------------------------------------------------------------------------------------
-enum GemmEpi { kEpiStore = 0, kEpiResidual = 1, kEpiSwiGLU = 2 };
+// kEpiPartial: always write fp32 partial sums (plane s of p.partial), even without split-K;
+// a row-wise finishing kernel applies the epilogue.
+enum GemmEpi { kEpiStore = 0, kEpiResidual = 1, kEpiSwiGLU = 2, kEpiPartial = 3 };
 
 struct GemmParams {
   const void* A;
@@ -49,6 +54,12 @@ struct GemmParams {
   int N;             // logical output columns (2*ff for SwiGLU)
   int Kd;
   int ff;            // SwiGLU only
+  // Optional fused RMSNorm on the A operand: row m of A is row a_rows[m] of `A` (clamped to
+  // [0, a_rows_cap)), multiplied by a_scale[that row] and by a_gain[k] before rounding.
+  const int32_t* a_rows;
+  int a_rows_cap;
+  const float* a_scale;
+  const void* a_gain;
 };
 
 constexpr int kGemmBM = 128;
@@ -59,10 +70,13 @@ constexpr int kGemmMinTiles = 128;
 
 // Split-K factor chosen on the device from the tile count (the packed row count is only
 // known there); kiters = number of 128-byte k-iterations.
+// Split-K targets about this many work units: with 256-column tiles each unit keeps one CU
+// streaming, and fewer, longer units keep the split-K partial traffic small.
+constexpr int kGemmTargetUnits = 144;
 __host__ __device__ inline int gemm_split(int tiles, int kiters) {
   if (tiles <= 0) return 1;
   if (tiles >= kGemmMinTiles) return 1;
-  int s = (kPlanCUs + tiles - 1) / tiles;
+  int s = (kGemmTargetUnits + tiles - 1) / tiles;
   int smax = kiters / 4;
   if (smax < 1) smax = 1;
   if (s > smax) s = smax;
@@ -72,8 +86,20 @@ __host__ __device__ inline int gemm_split(int tiles, int kiters) {
 
 template <typename T>
 hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st);
+// split-K factor the GEMM uses when the row count M is known on the host
+int gemm_host_split(int M, int N, int Kd, int elem_bytes);
+
+// Finish of the O projection: h[s] = H[s] + sum of `split` partial planes (rounded to T),
+// and for every packed slot s (packed_slot[slot_row[s]] == s) the FFN input
+// A2[slot_row[s]] = h[s] / sqrt(mean(h[s]^2) + eps) * g.  One wave per slot.
+template <typename T>
+hipError_t launch_oproj_finish(const float* partial, int split, const void* H, void* h, int S,
+                               int d, const int32_t* slot_row, const int32_t* packed_slot,
+                               const int32_t* count, const void* g, float eps, void* A2,
+                               int ld_a2, hipStream_t st);
 // fp32 elements of split-K partial storage any GEMM with these bounds may use
-size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes);
+// (always: the GEMM writes partial planes even without split-K, as kEpiPartial does)
+size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always = false);
 // N-tile width used for a GEMM with N output columns (256 for wide, 128 otherwise)
 int gemm_tile_n(int N);
 

@@ -106,7 +106,7 @@ size_t padded_ld(size_t cols, size_t eb) { return cols + 128 / eb; }
 // Workspace layout of one layer.
 struct Layout {
   size_t ratio, rec, src, packed, slot_row, count;
-  size_t a1, qkv, part_o, part_lse, attn, h, a2, G, F, gpart;
+  size_t rstd, qkv, part_o, part_lse, attn, h, a2, G, F, gpart;
   size_t total;
   size_t ld_d, ld_qkv, ld_q, ld_ff;   // padded row strides (elements)
 };
@@ -122,7 +122,7 @@ Layout layout_of(const specfold_shape* s) {
   size_t gp = 0;
   const int ebi = (int)eb;
   gp = std::max(gp, gemm_partial_elems((int)S, (int)qkvd, (int)d, ebi));
-  gp = std::max(gp, gemm_partial_elems((int)S, (int)d, (int)qd, ebi));
+  gp = std::max(gp, gemm_partial_elems((int)S, (int)d, (int)qd, ebi, true));
   gp = std::max(gp, gemm_partial_elems((int)S, (int)(2 * ff), (int)d, ebi));
   gp = std::max(gp, gemm_partial_elems((int)S, (int)d, (int)ff, ebi));
   Layout L;
@@ -142,7 +142,7 @@ Layout layout_of(const specfold_shape* s) {
   L.packed = take(S * 4);
   L.slot_row = take(S * 4);
   L.count = take(256);
-  L.a1 = take(S * L.ld_d * eb);
+  L.rstd = take(S * 4);
   L.qkv = take(S * L.ld_qkv * eb);
   L.part_o = take(prow * qd * 4);
   L.part_lse = take(prow * (size_t)s->n_q_heads * 4);
@@ -167,21 +167,26 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   const int dh = s->head_dim, nq = s->n_q_heads, nkv = s->n_kv_heads;
   const int qkvd = (nq + 2 * nkv) * dh, qd = nq * dh;
   const int cus = num_cus();
+  // a failure left behind by some earlier, unrelated HIP call on this thread must not be
+  // reported as a failure of these launches
+  (void)hipGetLastError();
   auto mark = [&](int step, bool begin) -> hipError_t {
     if (!probe || probe->step != step) return hipSuccess;
     void* ev = begin ? probe->start : probe->stop;
     return ev ? hipEventRecord((hipEvent_t)ev, st) : hipSuccess;
   };
+  float* rstd = (float*)(ws + L.rstd);
+  // the gate pass also yields every row's RMSNorm scale (stats only with a given state)
+  HIP_CHECK(mark(SPECFOLD_STEP_GATE, true));
+  HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, rec, rstd, s->rms_eps, state_in,
+                           st));
+  HIP_CHECK(mark(SPECFOLD_STEP_GATE, false));
   if (!state_in) {
-    HIP_CHECK(mark(SPECFOLD_STEP_GATE, true));
-    HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, rec, st));
-    HIP_CHECK(mark(SPECFOLD_STEP_GATE, false));
     HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, true));
     HIP_CHECK(launch_resolve_pack(rec, fold_src, nullptr, N, B, kResolve | kPack, src, packed,
                                   slot_row, count, st));
     HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, false));
   }
-  void* A1 = ws + L.a1;
   void* QKV = ws + L.qkv;
   void* ATT = ws + L.attn;
   void* Hh = ws + L.h;
@@ -190,13 +195,11 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   void* F = ws + L.F;
   float* gpart = (float*)(ws + L.gpart);
 
-  HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM1, true));
-  HIP_CHECK(launch_rmsnorm_gather<T>(hin, packed, count, S, S, d, s->rms_eps, w->rms1, A1,
-                                     (int)L.ld_d, st));
-  HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM1, false));
 
   GemmParams gp{};
-  gp.A = A1; gp.lda = L.ld_d; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = L.ld_qkv;
+  // RMSNorm of the packed rows is applied inside the GEMM's A loader
+  gp.A = hin; gp.lda = d; gp.a_rows = packed; gp.a_rows_cap = S; gp.a_scale = rstd;
+  gp.a_gain = w->rms1; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = L.ld_qkv;
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = qkvd; gp.Kd = d;
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
@@ -218,17 +221,18 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   HIP_CHECK(launch_attn_block<T>(ap, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_ATTN_BLOCK, false));
 
+  // O projection over every slot: fp32 partials, then one row pass adds the residual and
+  // computes the FFN's RMSNorm for the packed rows
   gp = GemmParams{};
-  gp.A = ATT; gp.lda = L.ld_q; gp.W = w->w_o; gp.ldw = qd; gp.C = Hh; gp.ldc = d;
-  gp.R = hin; gp.ldr = d; gp.partial = gpart; gp.m_dev = nullptr; gp.m_cap = S; gp.N = d;
-  gp.Kd = qd;
+  gp.A = ATT; gp.lda = L.ld_q; gp.W = w->w_o; gp.ldw = qd; gp.C = nullptr; gp.ldc = d;
+  gp.partial = gpart; gp.m_dev = nullptr; gp.m_cap = S; gp.N = d; gp.Kd = qd;
   HIP_CHECK(mark(SPECFOLD_STEP_O_PROJ, true));
-  HIP_CHECK(launch_gemm<T>(gp, kEpiResidual, cus, st));
+  HIP_CHECK(launch_gemm<T>(gp, kEpiPartial, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_O_PROJ, false));
-
   HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM2, true));
-  HIP_CHECK(launch_rmsnorm_gather<T>(Hh, packed, count, S, S, d, s->rms_eps, w->rms2, A2,
-                                     (int)L.ld_d, st));
+  HIP_CHECK(launch_oproj_finish<T>(gpart, gemm_host_split(S, d, qd, (int)sizeof(T)), hin, Hh, S, d,
+                                   slot_row, packed, count, w->rms2, s->rms_eps, A2,
+                                   (int)L.ld_d, st));
   HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM2, false));
 
   gp = GemmParams{};
@@ -265,12 +269,13 @@ specfold_status specfold_gate(const specfold_shape* shape, const void* hidden,
   if (!aligned16(hidden)) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden is not 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   const specfold_shape* sh = shape;
+  (void)hipGetLastError();   // do not report an earlier, unrelated failure
   if (sh->dtype == SPECFOLD_BF16) {
     HIP_CHECK(launch_gate<bf16>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
-                                ratio, recompute, s));
+                                ratio, recompute, nullptr, 0.f, false, s));
   } else {
     HIP_CHECK(launch_gate<float>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
-                                 ratio, recompute, s));
+                                 ratio, recompute, nullptr, 0.f, false, s));
   }
   return ok();
 }
@@ -281,6 +286,7 @@ specfold_status specfold_resolve(const specfold_shape* shape, const uint8_t* rec
   if (st != SPECFOLD_OK) return st;
   if (!recompute || !fold_src || !src_node)
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "recompute, fold_src and src_node are required");
+  (void)hipGetLastError();
   HIP_CHECK(launch_resolve_pack(recompute, fold_src, nullptr, shape->num_nodes, shape->block,
                                 kResolve, src_node, nullptr, nullptr, nullptr,
                                 (hipStream_t)stream));
@@ -295,6 +301,7 @@ specfold_status specfold_pack(const specfold_shape* shape, const uint8_t* recomp
   if (!recompute || !src_node || !packed_slot || !slot_row || !packed_count)
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
                 "recompute, src_node, packed_slot, slot_row and packed_count are required");
+  (void)hipGetLastError();
   HIP_CHECK(launch_resolve_pack(recompute, nullptr, src_node, shape->num_nodes, shape->block,
                                 kPack, nullptr, packed_slot, slot_row, packed_count,
                                 (hipStream_t)stream));

@@ -32,7 +32,8 @@
  *   - There is no global mutable state: calls on different streams are safe when they
  *     use different output and workspace buffers.
  *   - On failure a status other than SPECFOLD_OK is returned and specfold_last_error()
- *     returns a message (per host thread).
+ *     returns a message (per host thread).  A HIP error left pending by an earlier,
+ *     unrelated HIP call on the calling thread is cleared on entry, not reported.
  *   - Device-side index inputs (fold_src, masks, provenance, packed rows) are clamped
  *     before use, so malformed values give wrong results but never out-of-bounds access.
  *
@@ -193,14 +194,14 @@ specfold_status specfold_layer_forward(const specfold_shape* shape,
 
 /* Launch steps of specfold_layer_forward, for timing probes. */
 typedef enum specfold_step {
-  SPECFOLD_STEP_GATE = 0,          /* gate                                            */
+  SPECFOLD_STEP_GATE = 0,          /* gate (also every row's RMSNorm scale)           */
   SPECFOLD_STEP_RESOLVE_PACK = 1,  /* provenance + packing                            */
-  SPECFOLD_STEP_RMSNORM1 = 2,      /* gathered RMSNorm of the packed rows             */
+  SPECFOLD_STEP_RMSNORM1 = 2,      /* fused into the QKV GEMM's loader: not recorded  */
   SPECFOLD_STEP_QKV = 3,           /* packed QKV GEMM (incl. its split-K reduction)   */
   SPECFOLD_STEP_ATTN_PREFIX = 4,   /* prefix-phase attention                          */
   SPECFOLD_STEP_ATTN_BLOCK = 5,    /* block-phase attention + merge                   */
-  SPECFOLD_STEP_O_PROJ = 6,        /* O projection + residual over all slots          */
-  SPECFOLD_STEP_RMSNORM2 = 7,      /* gathered RMSNorm before the FFN                 */
+  SPECFOLD_STEP_O_PROJ = 6,        /* O projection over all slots (fp32 partials)     */
+  SPECFOLD_STEP_RMSNORM2 = 7,      /* O finish: residual add + FFN RMSNorm of packed  */
   SPECFOLD_STEP_FFN_GATE_UP = 8,   /* packed gate/up GEMM with the SwiGLU product     */
   SPECFOLD_STEP_FFN_DOWN = 9,      /* packed down GEMM                                */
   SPECFOLD_STEP_COMBINE = 10       /* y = h + F[slot_row]                             */
