@@ -23,6 +23,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, public spec
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "ffn_gate_up_7b_layer_traffic.json")
+COPY_BYTES = 256 << 20         # calibration copy: bytes read (and written) per launch
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, public spec
 FP32_PEAK_TFLOPS = 157.3       # dense fp32
 
@@ -137,6 +139,33 @@ def kernel_breakdown(dl, tau, reps, ev, stream):
     return out
 
 
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    record, or None when the GEMM source has changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except (OSError, ValueError):
+        return None
+    src = os.path.join(ROOT, rec.get("source", ""))
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return rec.get("hbm_bytes_per_launch") if sha == rec.get("source_sha256") else None
+
+
+def calibration_copy(reps=3):
+    """A plain device-to-device copy of known size; its FETCH_SIZE / WRITE_SIZE readings
+    scale the counters of the other kernels to bytes."""
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(w, tau, budget_s):
     """The oracle as it stands on the host cores, on whole verify layers of the same
     workload, repeated until the time budget is used."""
@@ -174,6 +203,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also run the tau sweep of config 2")
     ap.add_argument("--report", default=None)
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel probes")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help=f"also run a {COPY_BYTES >> 20} MiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the folded verify layer is measured on one "
@@ -204,8 +236,11 @@ def main():
     alg = algorithmic(cfg, K)
     dom_bytes = alg["ffn_gate_up"]["bytes"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    kernels = kernel_breakdown(dl, tau, 20, ev, stream)
-    log("[bench] per-kernel us: " + ", ".join(f"{k}={v:.1f}" for k, v in kernels.items()))
+    kernels = {} if args.no_breakdown else kernel_breakdown(dl, tau, 20, ev, stream)
+    if kernels:
+        log("[bench] per-kernel us: " + ", ".join(f"{k}={v:.1f}" for k, v in kernels.items()))
+    if args.calibrate_copy:
+        calibration_copy()
 
     result = {
         "metric": "branch-tokens verified/s per layer (7B shape, 1+15 branches); us/verify-layer",
@@ -229,7 +264,7 @@ def main():
         "kernels_us": kernels,
         "roofline": {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "avg_us": dom_ms * 1e3,
+                     "traffic": measured_traffic(), "avg_us": dom_ms * 1e3,
                      "algorithmic_bytes": dom_bytes},
     }
     report = {"main": result}
