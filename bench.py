@@ -79,18 +79,40 @@ def algorithmic(cfg, K):
     qkvd = cfg.qkv_dim
     g = nq // nkv
     out = {
-        "gate": dict(bytes=2 * S * d * eb + S * 5, flops=4 * S * d),
+        "gate": dict(bytes=2 * S * d * eb + S * 9, flops=4 * S * d),
+        "resolve_pack": dict(bytes=S * 1 + cfg.num_nodes * 4 + 3 * S * 4 + 4, flops=0),
         "qkv": dict(bytes=qkvd * d * eb + K * d * eb + K * qkvd * eb, flops=2 * K * d * qkvd),
         "attn_prefix": dict(bytes=2 * P * nkv * dh * eb + K * nq * dh * eb,
                             flops=4 * K * nq * P * dh),
         "attn_block": dict(bytes=K * qkvd * eb + S * nq * dh * eb, flops=4 * S * nq * B * dh),
-        "o_proj": dict(bytes=d * nq * dh * eb + 2 * S * d * eb + S * nq * dh * eb,
-                       flops=2 * S * nq * dh * d),
+        # O projection and its finish (residual add, FFN RMSNorm of the packed rows)
+        "o_proj+o_finish": dict(bytes=d * nq * dh * eb + S * nq * dh * eb + 2 * S * d * eb
+                                + K * d * eb, flops=2 * S * nq * dh * d),
         "ffn_gate_up": dict(bytes=2 * ff * d * eb + K * d * eb + K * ff * eb,
                             flops=2 * K * d * 2 * ff),
         "ffn_down": dict(bytes=d * ff * eb + K * ff * eb + K * d * eb, flops=2 * K * ff * d),
-        "combine": dict(bytes=3 * S * d * eb, flops=S * d),
+        "combine": dict(bytes=2 * S * d * eb + K * d * eb, flops=S * d),
     }
+    return out
+
+
+def kernel_rooflines(cfg, K, kernels):
+    """Per-kernel achieved HBM rate and MFMA rate from the probe times and the
+    algorithmic bytes/flops, as fractions of MI355X peak."""
+    alg = algorithmic(cfg, K)
+    times = dict(kernels)
+    if "o_proj" in times and "o_finish" in times:
+        times["o_proj+o_finish"] = times["o_proj"] + times["o_finish"]
+    peak_tf = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
+    out = {}
+    for name, a in alg.items():
+        us = times.get(name)
+        if not us:
+            continue
+        gbs = a["bytes"] / (us * 1e-6) / 1e9
+        tfs = a["flops"] / (us * 1e-6) / 1e12
+        out[name] = dict(us=us, GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS, TFLOPs=tfs,
+                         mfma_frac=tfs / peak_tf, bytes=a["bytes"], flops=a["flops"])
     return out
 
 
@@ -202,6 +224,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also run the tau sweep of config 2")
+    ap.add_argument("--stack", action="store_true",
+                    help="also time the 28-layer stack (config 3) end to end")
+    ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--report", default=None)
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel probes")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -262,6 +287,7 @@ def main():
         "packed_rows": K,
         "recompute_fraction": K / cfg.slots,
         "kernels_us": kernels,
+        "kernels_roofline": kernel_rooflines(cfg, K, kernels) if kernels else {},
         "roofline": {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(), "avg_us": dom_ms * 1e3,
@@ -270,6 +296,13 @@ def main():
     report = {"main": result}
     if args.sweep:
         report["tau_sweep"] = tau_sweep(ev, stream, args.steps, args.warmup)
+    if args.stack:
+        del dl
+        torch.cuda.empty_cache()
+        report["stack"] = stack_bench(ev, stream, args.stack_steps, 3)
+        result["stack"] = {k: report["stack"][k] for k in
+                           ("workload", "layers", "us_per_verify_step", "us_per_layer",
+                            "packed_rows_per_layer")}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(w, tau, args.cpu_seconds)
@@ -298,6 +331,44 @@ def tau_sweep(ev, stream, steps, warmup):
                          kernels_us=kern))
         log(f"[bench] sweep tau={tau}: K={K} ({K / cfg.slots:.3f}) {ms * 1e3:.1f} us")
     return rows
+
+
+def stack_bench(ev, stream, steps, warmup):
+    """End-to-end time of one verify step through the 28-layer 7B-shaped stack (1+31
+    branches, prefix 4096): every layer gates, packs and runs on the previous layer's
+    output inside one specfold_stack_forward call."""
+    import torch
+    from branch_folding_amd.runner import DeviceStack
+    from synth import CONFIGS, iter_layers, make_workload
+    cfg = CONFIGS[3]
+    t = time.time()
+    base = make_workload(cfg, layers=1, weights=False)
+    ds = DeviceStack(cfg, ((w, c) for _, w, c in iter_layers(cfg, workers=8)), base.H,
+                     base.fold_src)
+    log(f"[bench] stack {cfg.name}: {ds.num_layers} layers drawn and uploaded in "
+        f"{time.time() - t:.1f}s")
+    ds.forward(cfg.tau, stream=stream)
+    torch.cuda.synchronize()
+    Ks = [s["K"] for s in ds.fold_states()]
+    for _ in range(warmup):
+        ds.forward(cfg.tau, stream=stream, record_states=False)
+    t0, t1 = ev.create(2)
+    torch.cuda.synchronize()
+    ev.record(t0, stream)
+    for _ in range(steps):
+        ds.forward(cfg.tau, stream=stream, record_states=False)
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    ev.destroy([t0, t1])
+    log(f"[bench] stack: {ms * 1e3:.0f} us per verify step ({ms * 1e3 / ds.num_layers:.1f} "
+        f"us per layer), K per layer {Ks}")
+    res = dict(workload=cfg.name, layers=ds.num_layers, tau=cfg.tau, us_per_verify_step=ms * 1e3,
+               us_per_layer=ms * 1e3 / ds.num_layers, packed_rows_per_layer=Ks,
+               slots=cfg.slots, branch_tokens_per_s=cfg.slots / (ms * 1e-3))
+    del ds
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

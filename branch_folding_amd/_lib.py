@@ -81,6 +81,12 @@ _SIGS = {
                                                      ctypes.POINTER(Probe)]),
     "specfold_workspace_offset": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32,
                                                      ctypes.POINTER(ctypes.c_int64)]),
+    "specfold_stack_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
+    "specfold_stack_forward": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32,
+                                              ctypes.POINTER(LayerWeights),
+                                              ctypes.POINTER(KVView), _P, _P, _P,
+                                              ctypes.c_float, ctypes.POINTER(FoldState),
+                                              ctypes.c_uint32, _P, ctypes.c_size_t, _P]),
     "specfold_last_error": (ctypes.c_char_p, []),
     "specfold_version": (ctypes.c_int32, []),
 }
@@ -174,6 +180,24 @@ def specfold_workspace_offset(shape: Shape, which: int):
     return off, int(ld.value)
 
 
+_WEIGHT_KEYS = ("rms1", "w_qkv", "w_o", "rms2", "w_gate_up", "w_down")
+_STATE_KEYS = ("ratio", "recompute", "src_node", "packed_slot", "slot_row", "packed_count")
+
+
+def _weights(weights: dict) -> LayerWeights:
+    return LayerWeights(*[_ptr(weights[k]) for k in _WEIGHT_KEYS])
+
+
+def _kv(prefix) -> KVView:
+    if prefix is None:
+        return KVView(None, None, 0, 0)
+    return KVView(_ptr(prefix[0]), _ptr(prefix[1]), int(prefix[2]), int(prefix[3]))
+
+
+def _state(state: dict) -> FoldState:
+    return FoldState(*[_ptr(state.get(k)) for k in _STATE_KEYS])
+
+
 def specfold_layer_forward(shape: Shape, weights: dict, prefix, hidden_in, hidden_out,
                            fold_src, tau: float, state: Optional[dict] = None, flags: int = 0,
                            workspace=None, workspace_bytes: Optional[int] = None, stream=None,
@@ -181,15 +205,9 @@ def specfold_layer_forward(shape: Shape, weights: dict, prefix, hidden_in, hidde
     """weights: dict of device tensors rms1, w_qkv, w_o, rms2, w_gate_up, w_down.
     prefix: (k_ptr_or_tensor, v_ptr_or_tensor, stride_tok, stride_head) or None.
     state: dict with any of ratio, recompute, src_node, packed_slot, slot_row, packed_count."""
-    lw = LayerWeights(*[_ptr(weights[k]) for k in
-                        ("rms1", "w_qkv", "w_o", "rms2", "w_gate_up", "w_down")])
-    kv = KVView(None, None, 0, 0) if prefix is None else KVView(
-        _ptr(prefix[0]), _ptr(prefix[1]), int(prefix[2]), int(prefix[3]))
-    st = None
-    if state is not None:
-        st = FoldState(*[_ptr(state.get(k)) for k in
-                         ("ratio", "recompute", "src_node", "packed_slot", "slot_row",
-                          "packed_count")])
+    lw = _weights(weights)
+    kv = _kv(prefix)
+    st = None if state is None else _state(state)
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (ctypes.byref(shape), ctypes.byref(lw), ctypes.byref(kv), _ptr(hidden_in),
@@ -200,3 +218,32 @@ def specfold_layer_forward(shape: Shape, weights: dict, prefix, hidden_in, hidde
         _check(lib().specfold_layer_forward(*args))
     else:
         _check(lib().specfold_layer_forward_probed(*args, ctypes.byref(probe)))
+
+
+def specfold_stack_workspace_bytes(shape: Shape) -> int:
+    n = int(lib().specfold_stack_workspace_bytes(ctypes.byref(shape)))
+    if n == 0:
+        raise SpecFoldError(SPECFOLD_ERR_INVALID_ARGUMENT, last_error())
+    return n
+
+
+def specfold_stack_forward(shape: Shape, weights: list, prefix, hidden_in, hidden_out,
+                           fold_src, tau: float, states: Optional[list] = None,
+                           flags: int = 0, workspace=None,
+                           workspace_bytes: Optional[int] = None, stream=None,
+                           num_layers: Optional[int] = None):
+    """weights: list of per-layer weight dicts (as specfold_layer_forward's); prefix: list
+    of per-layer views or None; states: list of per-layer state dicts or None."""
+    nl = len(weights) if num_layers is None else int(num_layers)
+    wa = (LayerWeights * max(len(weights), 1))(*[_weights(w) for w in weights])
+    pa = None
+    if prefix is not None:
+        pa = (KVView * max(len(prefix), 1))(*[_kv(p) for p in prefix])
+    sa = None
+    if states is not None:
+        sa = (FoldState * max(len(states), 1))(*[_state(st) for st in states])
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().specfold_stack_forward(
+        ctypes.byref(shape), nl, wa, pa, _ptr(hidden_in), _ptr(hidden_out), _ptr(fold_src),
+        float(tau), sa, int(flags), _ptr(workspace), int(workspace_bytes), _stream(stream)))

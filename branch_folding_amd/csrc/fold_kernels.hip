@@ -18,14 +18,15 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
                                                    int N, int B, int d, float tau,
                                                    float* __restrict__ ratio,
                                                    uint8_t* __restrict__ recompute,
-                                                   float* __restrict__ rstd, float eps,
-                                                   int stats_only) {
+                                                   float* __restrict__ rstd, float eps) {
   const int lane = threadIdx.x & 63;
   const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (slot >= N * B) return;
   const int n = slot / B, i = slot - n * B;
+  // ratio and mask are each optional (a given fold state needs only rstd, perhaps ratios)
+  const bool decide = (ratio != nullptr) || (recompute != nullptr);
   int p = -1;
-  if (n > 0 && !stats_only) p = fold_src[n];   // stats only: fold_src may be absent
+  if (n > 0 && decide && fold_src) p = fold_src[n];
   const bool has_parent = (n > 0) && (p >= 0) && (p < n);
   const T* c = H + (size_t)slot * d;
   const T* q = has_parent ? H + ((size_t)p * B + i) * d : c;
@@ -48,7 +49,7 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
   sp = wave_sum(sp);
   sc = wave_sum(sc);
   if (lane == 0 && rstd) rstd[slot] = 1.0f / sqrtf(sc / (float)d + eps);
-  if (lane == 0 && !stats_only) {
+  if (lane == 0 && decide) {
     float r;
     bool rec;
     if (!has_parent) {
@@ -60,7 +61,7 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
       rec = !(r <= tau);
     }
     if (ratio) ratio[slot] = r;
-    recompute[slot] = rec ? 1 : 0;
+    if (recompute) recompute[slot] = rec ? 1 : 0;
   }
 }
 
@@ -301,11 +302,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ h,
 // ------------------------------------------------------------------------------------
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
-                       float* ratio, uint8_t* recompute, float* rstd, float eps, bool stats_only,
+                       float* ratio, uint8_t* recompute, float* rstd, float eps,
                        hipStream_t st) {
   const int S = N * B;
   gate_kernel<T><<<ceil_div(S, 4), 256, 0, st>>>((const T*)H, fold_src, N, B, d, tau, ratio,
-                                                 recompute, rstd, eps, stats_only ? 1 : 0);
+                                                 recompute, rstd, eps);
   return hipGetLastError();
 }
 
@@ -364,9 +365,9 @@ template hipError_t launch_oproj_finish<bf16>(const float*, int, const void*, vo
                                               const void*, float, void*, int, hipStream_t);
 
 template hipError_t launch_gate<float>(const void*, const int32_t*, int, int, int, float, float*,
-                                       uint8_t*, float*, float, bool, hipStream_t);
+                                       uint8_t*, float*, float, hipStream_t);
 template hipError_t launch_gate<bf16>(const void*, const int32_t*, int, int, int, float, float*,
-                                      uint8_t*, float*, float, bool, hipStream_t);
+                                      uint8_t*, float*, float, hipStream_t);
 template hipError_t launch_rmsnorm_gather<float>(const void*, const int32_t*, const int32_t*, int,
                                                  int, int, float, const void*, void*, int,
                                                  hipStream_t);

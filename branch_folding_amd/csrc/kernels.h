@@ -12,11 +12,11 @@ namespace specfold {
 constexpr int kResolve = 1;
 constexpr int kPack = 2;
 
-// Gate; also writes rstd[slot] = 1/sqrt(mean(H[slot]^2) + eps) when rstd is non-null.
-// stats_only: write rstd only (fold state supplied by the caller).
+// Gate: writes ratio[slot] and recompute[slot] where those pointers are non-null (the
+// ratio needs fold_src), and rstd[slot] = 1/sqrt(mean(H[slot]^2) + eps) when rstd is.
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
-                       float* ratio, uint8_t* recompute, float* rstd, float eps, bool stats_only,
+                       float* ratio, uint8_t* recompute, float* rstd, float eps,
                        hipStream_t st);
 size_t resolve_pack_lds_bytes(int S);
 hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,

@@ -176,10 +176,11 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
     return ev ? hipEventRecord((hipEvent_t)ev, st) : hipSuccess;
   };
   float* rstd = (float*)(ws + L.rstd);
-  // the gate pass also yields every row's RMSNorm scale (stats only with a given state)
+  // the gate pass also yields every row's RMSNorm scale; with a given fold state it
+  // writes no mask, and ratios only into a caller's ratio buffer
   HIP_CHECK(mark(SPECFOLD_STEP_GATE, true));
-  HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, rec, rstd, s->rms_eps, state_in,
-                           st));
+  HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, state_in ? nullptr : rec, rstd,
+                           s->rms_eps, st));
   HIP_CHECK(mark(SPECFOLD_STEP_GATE, false));
   if (!state_in) {
     HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, true));
@@ -255,6 +256,102 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   return ok();
 }
 
+specfold_status check_flags(uint32_t flags) {
+  if (flags & ~SPECFOLD_FLAG_FOLD_STATE_IN)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  return SPECFOLD_OK;
+}
+
+size_t hidden_bytes(const specfold_shape* s) {
+  return (size_t)s->num_nodes * s->block * s->hidden * elem_bytes(s);
+}
+
+// Weights and prefix view of one layer (`layer` < 0: a single-layer call).
+specfold_status check_layer_params(const specfold_shape* shape,
+                                   const specfold_layer_weights* weights,
+                                   const specfold_kv_view* prefix, int layer) {
+  char at[32] = "";
+  if (layer >= 0) snprintf(at, sizeof at, " (layer %d)", layer);
+  if (!weights || !weights->rms1 || !weights->w_qkv || !weights->w_o || !weights->rms2 ||
+      !weights->w_gate_up || !weights->w_down)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "every layer weight pointer is required%s", at);
+  const void* wp[6] = {weights->rms1, weights->w_qkv, weights->w_o, weights->rms2,
+                       weights->w_gate_up, weights->w_down};
+  for (int i = 0; i < 6; ++i)
+    if (!aligned16(wp[i]))
+      return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "weight pointer %d is not 16-byte aligned%s", i,
+                  at);
+  const int64_t eb = elem_bytes(shape);
+  if (shape->prefix_len > 0) {
+    if (!prefix || !prefix->k || !prefix->v)
+      return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "prefix_len > 0 needs a prefix view%s", at);
+    if (!aligned16(prefix->k) || !aligned16(prefix->v) || prefix->stride_tok < 0 ||
+        prefix->stride_head < 0 || (prefix->stride_tok * eb) % 16 != 0 ||
+        (prefix->stride_head * eb) % 16 != 0)
+      return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
+                  "prefix view pointers and strides must keep rows 16-byte aligned%s", at);
+  }
+  return SPECFOLD_OK;
+}
+
+specfold_status check_hidden(const specfold_shape* shape, const void* hidden_in,
+                             const void* hidden_out) {
+  if (!hidden_in || !hidden_out)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden_in and hidden_out are required");
+  if (!aligned16(hidden_in) || !aligned16(hidden_out))
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden_in/hidden_out must be 16-byte aligned");
+  const size_t hb = hidden_bytes(shape);
+  const char* a = (const char*)hidden_in;
+  const char* b = (const char*)hidden_out;
+  if (a < b + hb && b < a + hb)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden_in and hidden_out overlap");
+  return SPECFOLD_OK;
+}
+
+specfold_status check_state_in(const specfold_fold_state* state, int layer) {
+  char at[32] = "";
+  if (layer >= 0) snprintf(at, sizeof at, " (layer %d)", layer);
+  if (!state || !state->recompute || !state->src_node || !state->packed_slot ||
+      !state->slot_row || !state->packed_count)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
+                "SPECFOLD_FLAG_FOLD_STATE_IN needs every fold-state array except ratio%s", at);
+  return SPECFOLD_OK;
+}
+
+specfold_status check_workspace(void* workspace, size_t workspace_bytes, size_t need) {
+  if (!workspace || workspace_bytes < need)
+    return fail(SPECFOLD_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                workspace ? workspace_bytes : (size_t)0, need);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  return SPECFOLD_OK;
+}
+
+// Fold-state buffers of one call (caller's where given, else the workspace's) and the
+// launch sequence in the layer's dtype.
+specfold_status launch_layer(const specfold_shape* shape, const specfold_layer_weights* weights,
+                             const specfold_kv_view* prefix, const void* hidden_in,
+                             void* hidden_out, const int32_t* fold_src, float tau,
+                             specfold_fold_state* state, bool state_in, char* ws,
+                             const Layout& L, hipStream_t s, const specfold_probe* probe) {
+  auto pick = [&](auto* user, size_t off) {
+    using P = decltype(user);
+    return user ? user : (P)(ws + off);
+  };
+  float* ratio = pick(state ? state->ratio : (float*)nullptr, L.ratio);
+  if (state_in && !(state && state->ratio && fold_src)) ratio = nullptr;
+  uint8_t* rec = pick(state ? state->recompute : (uint8_t*)nullptr, L.rec);
+  int32_t* src = pick(state ? state->src_node : (int32_t*)nullptr, L.src);
+  int32_t* packed = pick(state ? state->packed_slot : (int32_t*)nullptr, L.packed);
+  int32_t* slot_row = pick(state ? state->slot_row : (int32_t*)nullptr, L.slot_row);
+  int32_t* count = pick(state ? state->packed_count : (int32_t*)nullptr, L.count);
+  if (shape->dtype == SPECFOLD_BF16)
+    return run_layer<bf16>(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, ratio,
+                           rec, src, packed, slot_row, count, state_in, ws, L, s, probe);
+  return run_layer<float>(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, ratio,
+                          rec, src, packed, slot_row, count, state_in, ws, L, s, probe);
+}
+
 }  // namespace
 
 extern "C" {
@@ -272,10 +369,10 @@ specfold_status specfold_gate(const specfold_shape* shape, const void* hidden,
   (void)hipGetLastError();   // do not report an earlier, unrelated failure
   if (sh->dtype == SPECFOLD_BF16) {
     HIP_CHECK(launch_gate<bf16>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
-                                ratio, recompute, nullptr, 0.f, false, s));
+                                ratio, recompute, nullptr, 0.f, s));
   } else {
     HIP_CHECK(launch_gate<float>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
-                                 ratio, recompute, nullptr, 0.f, false, s));
+                                 ratio, recompute, nullptr, 0.f, s));
   }
   return ok();
 }
@@ -351,72 +448,79 @@ specfold_status specfold_layer_forward_probed(const specfold_shape* shape,
                                               void* stream, const specfold_probe* probe) {
   specfold_status st = check_shape(shape, true);
   if (st != SPECFOLD_OK) return st;
+  if ((st = check_flags(flags)) != SPECFOLD_OK) return st;
   const bool state_in = (flags & SPECFOLD_FLAG_FOLD_STATE_IN) != 0;
-  if (flags & ~SPECFOLD_FLAG_FOLD_STATE_IN)
-    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
-  if (!weights || !weights->rms1 || !weights->w_qkv || !weights->w_o || !weights->rms2 ||
-      !weights->w_gate_up || !weights->w_down)
-    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "every layer weight pointer is required");
-  const void* wp[6] = {weights->rms1, weights->w_qkv, weights->w_o, weights->rms2,
-                       weights->w_gate_up, weights->w_down};
-  for (int i = 0; i < 6; ++i)
-    if (!aligned16(wp[i]))
-      return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "weight pointer %d is not 16-byte aligned", i);
-  if (!hidden_in || !hidden_out)
-    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden_in and hidden_out are required");
-  if (!aligned16(hidden_in) || !aligned16(hidden_out))
-    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden_in/hidden_out must be 16-byte aligned");
-  const size_t eb = elem_bytes(shape);
-  const size_t hbytes = (size_t)shape->num_nodes * shape->block * shape->hidden * eb;
-  {
-    const char* a = (const char*)hidden_in;
-    const char* b = (const char*)hidden_out;
-    if (a < b + hbytes && b < a + hbytes)
-      return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden_in and hidden_out overlap");
-  }
-  if (shape->prefix_len > 0) {
-    if (!prefix || !prefix->k || !prefix->v)
-      return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "prefix_len > 0 needs a prefix view");
-    if (!aligned16(prefix->k) || !aligned16(prefix->v) || prefix->stride_tok < 0 ||
-        prefix->stride_head < 0 || (prefix->stride_tok * (int64_t)eb) % 16 != 0 ||
-        (prefix->stride_head * (int64_t)eb) % 16 != 0)
-      return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
-                  "prefix view pointers and strides must keep rows 16-byte aligned");
-  }
+  if ((st = check_layer_params(shape, weights, prefix, -1)) != SPECFOLD_OK) return st;
+  if ((st = check_hidden(shape, hidden_in, hidden_out)) != SPECFOLD_OK) return st;
   if (!state_in && !fold_src)
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "fold_src is required unless the fold state is an input");
-  if (state_in && (!state || !state->recompute || !state->src_node || !state->packed_slot ||
-                   !state->slot_row || !state->packed_count))
-    return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
-                "SPECFOLD_FLAG_FOLD_STATE_IN needs every fold-state array except ratio");
+  if (state_in && (st = check_state_in(state, -1)) != SPECFOLD_OK) return st;
   const Layout L = layout_of(shape);
-  if (!workspace || workspace_bytes < L.total)
-    return fail(SPECFOLD_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
-                workspace ? workspace_bytes : (size_t)0, L.total);
-  if (((uintptr_t)workspace & 255u) != 0)
-    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SPECFOLD_OK) return st;
+  return launch_layer(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, state,
+                      state_in, (char*)workspace, L, (hipStream_t)stream, probe);
+}
 
+size_t specfold_stack_workspace_bytes(const specfold_shape* shape) {
+  if (check_shape(shape, true) != SPECFOLD_OK) return 0;
+  g_last_error.clear();
+  return layout_of(shape).total + hidden_bytes(shape);
+}
+
+specfold_status specfold_stack_forward(const specfold_shape* shape, int32_t num_layers,
+                                       const specfold_layer_weights* weights,
+                                       const specfold_kv_view* prefix, const void* hidden_in,
+                                       void* hidden_out, const int32_t* fold_src, float tau,
+                                       specfold_fold_state* states, uint32_t flags,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  specfold_status st = check_shape(shape, true);
+  if (st != SPECFOLD_OK) return st;
+  if ((st = check_flags(flags)) != SPECFOLD_OK) return st;
+  const bool state_in = (flags & SPECFOLD_FLAG_FOLD_STATE_IN) != 0;
+  if (num_layers < 1) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "num_layers must be >= 1");
+  if (!weights) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "weights array is NULL");
+  if (shape->prefix_len > 0 && !prefix)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "prefix_len > 0 needs an array of prefix views");
+  for (int l = 0; l < num_layers; ++l) {
+    if ((st = check_layer_params(shape, &weights[l], prefix ? &prefix[l] : nullptr, l)) !=
+        SPECFOLD_OK)
+      return st;
+    if (state_in && (st = check_state_in(states ? &states[l] : nullptr, l)) != SPECFOLD_OK)
+      return st;
+  }
+  if ((st = check_hidden(shape, hidden_in, hidden_out)) != SPECFOLD_OK) return st;
+  if (!state_in && !fold_src)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "fold_src is required unless the fold states are inputs");
+  const Layout L = layout_of(shape);
+  const size_t hb = hidden_bytes(shape);
+  if ((st = check_workspace(workspace, workspace_bytes, L.total + hb)) != SPECFOLD_OK) return st;
   char* ws = (char*)workspace;
-  auto pick = [&](auto* user, size_t off) {
-    using P = decltype(user);
-    return user ? user : (P)(ws + off);
-  };
-  float* ratio = pick(state ? state->ratio : (float*)nullptr, L.ratio);
-  uint8_t* rec = pick(state ? state->recompute : (uint8_t*)nullptr, L.rec);
-  int32_t* src = pick(state ? state->src_node : (int32_t*)nullptr, L.src);
-  int32_t* packed = pick(state ? state->packed_slot : (int32_t*)nullptr, L.packed);
-  int32_t* slot_row = pick(state ? state->slot_row : (int32_t*)nullptr, L.slot_row);
-  int32_t* count = pick(state ? state->packed_count : (int32_t*)nullptr, L.count);
-  hipStream_t s = (hipStream_t)stream;
-  if (shape->dtype == SPECFOLD_BF16)
-    return run_layer<bf16>(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, ratio,
-                           rec, src, packed, slot_row, count, state_in, ws, L, s, probe);
-  return run_layer<float>(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, ratio,
-                          rec, src, packed, slot_row, count, state_in, ws, L, s, probe);
+  char* pong = ws + L.total;
+  {
+    // the caller's activations must not live inside the workspace
+    const char* w0 = ws;
+    const char* w1 = ws + L.total + hb;
+    const char* a = (const char*)hidden_in;
+    const char* b = (const char*)hidden_out;
+    if ((a < w1 && w0 < a + hb) || (b < w1 && w0 < b + hb))
+      return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "hidden_in/hidden_out overlap the workspace");
+  }
+  // layer l writes hidden_out when (num_layers - 1 - l) is even, else the workspace's
+  // spare hidden buffer, so consecutive layers never alias and the last writes hidden_out
+  const void* x = hidden_in;
+  for (int l = 0; l < num_layers; ++l) {
+    void* y = ((num_layers - 1 - l) % 2 == 0) ? hidden_out : (void*)pong;
+    st = launch_layer(shape, &weights[l], prefix ? &prefix[l] : nullptr, x, y, fold_src, tau,
+                      states ? &states[l] : nullptr, state_in, ws, L, (hipStream_t)stream,
+                      nullptr);
+    if (st != SPECFOLD_OK) return st;
+    x = y;
+  }
+  return ok();
 }
 
 const char* specfold_last_error(void) { return g_last_error.c_str(); }
 
-int32_t specfold_version(void) { return 100; }
+int32_t specfold_version(void) { return 200; }
 
 }  // extern "C"

@@ -100,3 +100,75 @@ class DeviceLayer:
     def output_numpy(self) -> np.ndarray:
         cfg = self.cfg
         return self.out.float().cpu().numpy().reshape(cfg.num_nodes, cfg.block, cfg.hidden)
+
+
+class DeviceStack:
+    """A stack of verify layers resident in HBM: per-layer weights and prefix caches, the
+    input hidden states, per-layer fold-state buffers and the stack workspace."""
+
+    def __init__(self, cfg, layers, H: np.ndarray, fold_src: np.ndarray, device="cuda:0"):
+        """layers: iterable of (weights dict, interleaved prefix cache) per layer; each is
+        uploaded as it is produced, so host memory holds one layer at a time."""
+        self.cfg = cfg
+        self.device = torch.device(device)
+        dt = torch_dtype(cfg)
+        self.dt = dt
+        self.shape = shape_of(cfg)
+        self.w, self.caches, self.prefix = [], [], []
+        n_kv, dh = cfg.n_kv, cfg.head_dim
+        for weights, cache in layers:
+            self.w.append({k: to_device(v, dt, self.device) for k, v in weights.items()})
+            c = to_device(cache, dt, self.device)
+            self.caches.append(c)
+            self.prefix.append((c[0, 0].data_ptr(), c[0, 1].data_ptr(), 2 * n_kv * dh, dh))
+        self.num_layers = len(self.w)
+        S, d = cfg.slots, cfg.hidden
+        self.H = to_device(H.reshape(S, d), dt, self.device)
+        self.out = torch.empty((S, d), dtype=dt, device=self.device)
+        self.fold_src = torch.from_numpy(np.asarray(fold_src, dtype=np.int32)).to(self.device)
+        self.states = []
+        for _ in range(self.num_layers):
+            self.states.append({
+                "ratio": torch.empty(S, dtype=torch.float32, device=self.device),
+                "recompute": torch.empty(S, dtype=torch.uint8, device=self.device),
+                "src_node": torch.empty(S, dtype=torch.int32, device=self.device),
+                "packed_slot": torch.empty(S, dtype=torch.int32, device=self.device),
+                "slot_row": torch.empty(S, dtype=torch.int32, device=self.device),
+                "packed_count": torch.zeros(1, dtype=torch.int32, device=self.device),
+            })
+        self.ws_bytes = L.specfold_stack_workspace_bytes(self.shape)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+
+    def load_states(self, states) -> None:
+        """Copy per-layer fold states (recompute, src_node, packed_slot, slot_row,
+        packed_count as host arrays) into the device buffers."""
+        for dev, st in zip(self.states, states):
+            for k in ("recompute", "src_node", "packed_slot", "slot_row", "packed_count"):
+                v = np.asarray(st[k]).reshape(-1)
+                v = v.astype(np.uint8 if k == "recompute" else np.int32)
+                dev[k][: v.size].copy_(torch.from_numpy(v).to(self.device))
+
+    def forward(self, tau: float, stream=None, state_in: bool = False,
+                record_states: bool = True) -> torch.Tensor:
+        flags = L.SPECFOLD_FLAG_FOLD_STATE_IN if state_in else 0
+        L.specfold_stack_forward(self.shape, self.w, self.prefix if self.cfg.prefix else None,
+                                 self.H, self.out, self.fold_src, tau,
+                                 self.states if (record_states or state_in) else None, flags,
+                                 self.ws, self.ws_bytes, stream)
+        return self.out
+
+    def fold_states(self):
+        N, B = self.cfg.num_nodes, self.cfg.block
+        res = []
+        for dev in self.states:
+            st = {k: v.cpu().numpy() for k, v in dev.items()}
+            K = int(st["packed_count"][0])
+            res.append(dict(ratio=st["ratio"].reshape(N, B),
+                            recompute=st["recompute"].reshape(N, B) != 0,
+                            src=st["src_node"].reshape(N, B), packed_slot=st["packed_slot"][:K],
+                            slot_row=st["slot_row"].reshape(N, B), K=K))
+        return res
+
+    def output_numpy(self) -> np.ndarray:
+        cfg = self.cfg
+        return self.out.float().cpu().numpy().reshape(cfg.num_nodes, cfg.block, cfg.hidden)

@@ -120,8 +120,11 @@ typedef struct specfold_fold_state {
   int32_t* packed_count; /* [1]  K = number of packed (recompute) rows                 */
 } specfold_fold_state;
 
-/* Skip gate/resolve/pack and read recompute, src_node, packed_slot, slot_row and
- * packed_count from `state` (all five must be non-NULL and mutually consistent). */
+/* Skip the fold decision, provenance and packing, and read recompute, src_node,
+ * packed_slot, slot_row and packed_count from `state` (all five must be non-NULL and
+ * mutually consistent).  If state->ratio and fold_src are both non-NULL, the gate's
+ * ratios on this call's input are still written to state->ratio (for inspection; they
+ * decide nothing). */
 #define SPECFOLD_FLAG_FOLD_STATE_IN 1u
 
 /* Gate (SpecFold explainer, paragraph on measuring the relative difference at the layer
@@ -189,6 +192,38 @@ specfold_status specfold_layer_forward(const specfold_shape* shape,
                                        const void* hidden_in, void* hidden_out,
                                        const int32_t* fold_src, float tau,
                                        specfold_fold_state* state, uint32_t flags,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/* Bytes of device workspace specfold_stack_forward needs for `shape`: one layer's
+ * workspace followed by one spare [N, B, d] hidden-state buffer (0 if the shape is
+ * invalid or unsupported).  The layer part has the layout that specfold_workspace_offset
+ * describes, and holds the last layer's intermediates after the call. */
+size_t specfold_stack_workspace_bytes(const specfold_shape* shape);
+
+/* A stack of folded verify layers (SpecFold explainer: the residual ripple grows through
+ * the layers and the fold decision is taken again at every layer, so a position folded
+ * at one layer can be recomputed at a later one).  Layer l runs specfold_layer_forward's
+ * steps on layer l-1's output (layer 0 on hidden_in) with its own weights, prefix view
+ * and gate; the residual stream between layers is stored in shape->dtype.
+ *   num_layers >= 1.
+ *   weights: host array [num_layers] of device weight sets.
+ *   prefix:  host array [num_layers] of views (may be NULL when prefix_len == 0).
+ *   hidden_in, hidden_out: [N, B, d] device, no aliasing with each other or the workspace;
+ *   hidden_out receives the last layer's output.
+ *   fold_src: [N] int32 device, the same draft graph for every layer (may be NULL only
+ *   with SPECFOLD_FLAG_FOLD_STATE_IN).
+ *   states: NULL, or host array [num_layers] of fold-state buffer sets: outputs of each
+ *   layer's gate/provenance/packing (NULL members fall back to the workspace), or with
+ *   SPECFOLD_FLAG_FOLD_STATE_IN every layer's complete input state.
+ *   workspace: at least specfold_stack_workspace_bytes(shape) bytes, 256-byte aligned.
+ * All arguments of all layers are checked before the first launch. */
+specfold_status specfold_stack_forward(const specfold_shape* shape, int32_t num_layers,
+                                       const specfold_layer_weights* weights,
+                                       const specfold_kv_view* prefix,
+                                       const void* hidden_in, void* hidden_out,
+                                       const int32_t* fold_src, float tau,
+                                       specfold_fold_state* states, uint32_t flags,
                                        void* workspace, size_t workspace_bytes,
                                        void* stream);
 

@@ -33,7 +33,9 @@ Readings where the pages are silent (each one is listed in the design notes):
     h uses KV head h // (n_q / n_kv); a folded slot's query is its source's, its keys and
     values are its own branch's block rows, so the O projection runs for every slot;
   * RMSNorm(x) = x / sqrt(mean(x^2) + eps) * g; SwiGLU FFN = (SiLU(a Wg^T) * (a Wu^T)) Wd^T;
-    no biases, no rotary embedding.
+    no biases, no rotary embedding;
+  * in a stack the gate runs again at every layer on the carried residual stream; for
+    bf16 models that stream is handed from layer to layer in bf16.
 """
 from __future__ import annotations
 
@@ -44,7 +46,7 @@ import numpy as np
 
 __all__ = [
     "gate", "resolve", "pack", "rms_norm", "silu", "layer", "serial_layer",
-    "bruteforce_provenance", "FoldState", "fold_state",
+    "bruteforce_provenance", "FoldState", "fold_state", "round_to_bf16", "stack",
 ]
 
 
@@ -327,3 +329,53 @@ def serial_layer(weights: Dict[str, np.ndarray], H: np.ndarray, fold_src: np.nda
         f_cache[n] = Fb
         y[n] = hb + Fb
     return y
+
+
+# ---------------------------------------------------------------------------------------
+# Stack of layers ([SF] the paragraph on the residual ripple spreading through the layers
+# and the fold decision taken per layer; reading: the gate runs again at every layer on
+# the carried residual stream, so a row folded at one layer may be recomputed later).
+# ---------------------------------------------------------------------------------------
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value of every element (8 significant bits, ties to even), returned
+    as float64.  x = m * 2**e with 0.5 <= |m| < 1, so m * 256 rounded to an integer keeps
+    8 bits; np.rint rounds halves to even.  Covers the normal range (the values handed
+    between layers are O(1)); zero, inf and NaN pass through."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def stack(layer_params: Iterable[Tuple[Dict[str, np.ndarray], np.ndarray, np.ndarray]],
+          H: np.ndarray, fold_src: np.ndarray, tau: float, *, n_q: int, n_kv: int,
+          eps: float = 1e-6, dtype=np.float64, carry: Optional[str] = None,
+          states: Optional[Sequence[FoldState]] = None, keep_inputs: bool = False
+          ) -> Dict[str, object]:
+    """Run folded verify layers one after another on the same draft graph.
+
+    layer_params yields (weights, prefix_k, prefix_v) for layer 0, 1, ... in order (a
+    generator keeps one layer's weights in memory at a time).  Layer l takes layer l-1's
+    output as its input and makes its own fold decisions on it.
+    carry: None hands the output on in `dtype`; "bf16" rounds every layer's output to
+    bf16 first (the residual stream stored in the model's bf16 format).
+    states: per-layer fold states to use instead of each layer's gate.
+    Returns dict(y=last output, states=[per-layer fold state], K=[per-layer K],
+    inputs=[per-layer input] when keep_inputs)."""
+    if carry not in (None, "bf16"):
+        raise ValueError(f"carry must be None or 'bf16', got {carry!r}")
+    x = np.asarray(H, dtype=dtype)
+    got_states, Ks, inputs = [], [], []
+    for l, (weights, pk, pv) in enumerate(layer_params):
+        if keep_inputs:
+            inputs.append(x)
+        st = None if states is None else states[l]
+        out = layer(weights, x, fold_src, tau, pk, pv, n_q=n_q, n_kv=n_kv, eps=eps,
+                    dtype=dtype, state=st)
+        got_states.append(FoldState({k: out[k] for k in
+                                     ("r32", "r64", "recompute", "src", "packed_slot",
+                                      "slot_row", "K") if k in out}))
+        Ks.append(int(out["K"]))
+        y = out["y"]
+        if carry == "bf16":
+            y = round_to_bf16(y).astype(dtype)
+        x = y
+    return dict(y=x, states=got_states, K=Ks, inputs=inputs)

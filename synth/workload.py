@@ -22,6 +22,7 @@ representable fp32 values, so both consumers see bit-identical inputs.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
 from typing import Dict, List, Optional, Tuple
@@ -31,7 +32,7 @@ import numpy as np
 __all__ = [
     "Config", "CONFIGS", "Workload", "make_workload", "make_layer_weights",
     "round_bf16", "bf16_bits", "draft_graph", "hidden_states", "prefix_cache",
-    "custom_config", "graph_depth", "layer_weights_of", "layer_cache_of",
+    "custom_config", "graph_depth", "layer_weights_of", "layer_cache_of", "iter_layers",
 ]
 
 
@@ -58,6 +59,7 @@ class Config:
     taus: Tuple[float, ...] = ()
     rms_eps: float = 1e-6
     max_depth: int = 0      # dag_deep only
+    weight_std: float = 0.02  # std of the linear weights
 
     @property
     def slots(self) -> int:
@@ -217,12 +219,13 @@ def hidden_states(cfg: Config, fold_src: np.ndarray, rng: np.random.Generator
 # Weights and the shared prefix cache.
 # ----------------------------------------------------------------------------------------
 def make_layer_weights(cfg: Config, rng: np.random.Generator) -> Dict[str, np.ndarray]:
-    """Row-major [out, in] linear weights ~ N(0, 0.02^2); RMSNorm gains = 1.
+    """Row-major [out, in] linear weights ~ N(0, weight_std^2) (0.02 in the benchmark
+    configurations); RMSNorm gains = 1.
 
     w_qkv rows are the Q heads, then the K heads, then the V heads; w_gate_up rows are
     the gate projection then the up projection."""
     d, f, dh = cfg.hidden, cfg.ffn, cfg.head_dim
-    std = np.float32(0.02)
+    std = np.float32(cfg.weight_std)
 
     def lin(o, i):
         return _storage(cfg, rng.standard_normal((o, i), dtype=np.float32) * std)
@@ -303,3 +306,27 @@ def layer_cache_of(cfg: Config, layer: int) -> np.ndarray:
     """Prefix cache of one layer, regenerated from the seed."""
     cs = _streams(cfg)[2].spawn(layer + 1)[layer]
     return prefix_cache(cfg, np.random.Generator(np.random.PCG64(cs)))
+
+
+def iter_layers(cfg: Config, layers: Optional[int] = None, workers: int = 4):
+    """Yield (layer, weights, prefix cache) for layers 0, 1, ... in order, drawing up to
+    `workers` layers ahead on threads (numpy's generators release the GIL).  Every layer
+    has its own sub-stream, so the values equal layer_weights_of / layer_cache_of."""
+    nl = cfg.layers if layers is None else layers
+    s_prefix, s_weights = _streams(cfg)[2:4]
+    c_seeds, w_seeds = s_prefix.spawn(nl), s_weights.spawn(nl)
+
+    def draw(l):
+        w = make_layer_weights(cfg, np.random.Generator(np.random.PCG64(w_seeds[l])))
+        c = prefix_cache(cfg, np.random.Generator(np.random.PCG64(c_seeds[l])))
+        return l, w, c
+
+    with concurrent.futures.ThreadPoolExecutor(max(1, workers)) as ex:
+        pending = [ex.submit(draw, l) for l in range(min(nl, workers))]
+        nxt = len(pending)
+        while pending:
+            res = pending.pop(0).result()
+            if nxt < nl:
+                pending.append(ex.submit(draw, nxt))
+                nxt += 1
+            yield res

@@ -122,3 +122,55 @@ def test_fold_step_argument_errors():
     bad = shape_of(custom_config(block=0))
     with pytest.raises(L.SpecFoldError):
         L.specfold_pack(bad, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+
+
+def _stack(sh, n=3, **kw):
+    args = dict(weights=[_weights() for _ in range(n)],
+                prefix=[(FAKE, FAKE, 1024, 128) for _ in range(n)], hidden_in=FAKE,
+                hidden_out=FAKE + (1 << 32), fold_src=FAKE, tau=0.05, states=None, flags=0,
+                workspace=FAKE + (1 << 34), workspace_bytes=1 << 40, num_layers=None)
+    args.update(kw)
+    with pytest.raises(L.SpecFoldError) as e:
+        L.specfold_stack_forward(sh, args["weights"], args["prefix"], args["hidden_in"],
+                                 args["hidden_out"], args["fold_src"], args["tau"],
+                                 args["states"], args["flags"], args["workspace"],
+                                 args["workspace_bytes"], stream=0,
+                                 num_layers=args["num_layers"])
+    return e.value.status, str(e.value)
+
+
+def test_stack_workspace_holds_a_layer_and_a_hidden_buffer():
+    for cfg in CONFIGS.values():
+        sh = shape_of(cfg)
+        eb = 2 if cfg.dtype == "bf16" else 4
+        assert (L.specfold_stack_workspace_bytes(sh)
+                == L.specfold_layer_workspace_bytes(sh) + cfg.slots * cfg.hidden * eb)
+
+
+def test_stack_argument_errors():
+    sh = shape_of(CONFIGS[3])
+    need = L.specfold_stack_workspace_bytes(sh)
+    assert _stack(sh, weights=[])[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT        # 0 layers
+    w = [_weights() for _ in range(3)]
+    w[2]["w_qkv"] = None
+    st, msg = _stack(sh, weights=w)
+    assert st == L.SPECFOLD_ERR_INVALID_ARGUMENT and "layer 2" in msg
+    p = [(FAKE, FAKE, 1024, 128)] * 3
+    p[1] = (FAKE, FAKE + 2, 1024, 128)                                          # misaligned
+    st, msg = _stack(sh, prefix=p)
+    assert st == L.SPECFOLD_ERR_INVALID_ARGUMENT and "layer 1" in msg
+    assert _stack(sh, prefix=None)[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
+    assert _stack(sh, hidden_out=FAKE)[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
+    assert _stack(sh, fold_src=None)[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
+    assert _stack(sh, flags=L.SPECFOLD_FLAG_FOLD_STATE_IN)[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
+    full = {k: FAKE for k in ("recompute", "src_node", "packed_slot", "slot_row", "packed_count")}
+    st, msg = _stack(sh, flags=L.SPECFOLD_FLAG_FOLD_STATE_IN,
+                     states=[full, full, {"recompute": FAKE}])
+    assert st == L.SPECFOLD_ERR_INVALID_ARGUMENT and "layer 2" in msg
+    assert _stack(sh, workspace_bytes=need - 1)[0] == L.SPECFOLD_ERR_WORKSPACE
+    # hidden buffers inside the workspace
+    assert _stack(sh, hidden_in=FAKE + (1 << 34) + 4096)[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
+    assert _stack(sh, hidden_out=FAKE + (1 << 34) + need - 256)[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
+    # no prefix views needed without a prefix
+    sh0 = shape_of(CONFIGS[3], prefix_len=0)
+    assert _stack(sh0, prefix=None, workspace_bytes=0)[0] == L.SPECFOLD_ERR_WORKSPACE
