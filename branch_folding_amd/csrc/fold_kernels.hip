@@ -9,47 +9,42 @@ namespace specfold {
 // ------------------------------------------------------------------------------------
 // Gate (SpecFold explainer, paragraph on measuring ||H_child - H_parent|| / ||H_parent||
 // at the layer input).  One wave per slot; fp32 sums of squares; fold iff r <= tau.
-// The same pass yields the row's RMSNorm scale 1/sqrt(mean(H^2) + eps), which the QKV
-// GEMM applies while gathering the packed rows.
+// ratio and recompute are each optional (a caller-given fold state needs ratios only).
 // ------------------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
                                                    const int32_t* __restrict__ fold_src,
                                                    int N, int B, int d, float tau,
                                                    float* __restrict__ ratio,
-                                                   uint8_t* __restrict__ recompute,
-                                                   float* __restrict__ rstd, float eps) {
+                                                   uint8_t* __restrict__ recompute) {
   const int lane = threadIdx.x & 63;
   const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (slot >= N * B) return;
   const int n = slot / B, i = slot - n * B;
-  // ratio and mask are each optional (a given fold state needs only rstd, perhaps ratios)
-  const bool decide = (ratio != nullptr) || (recompute != nullptr);
   int p = -1;
-  if (n > 0 && decide && fold_src) p = fold_src[n];
+  if (n > 0 && fold_src) p = fold_src[n];
   const bool has_parent = (n > 0) && (p >= 0) && (p < n);
   const T* c = H + (size_t)slot * d;
   const T* q = has_parent ? H + ((size_t)p * B + i) * d : c;
   constexpr int VE = Pack16<T>::kElems;
   const int chunks = d / VE;
-  float sd = 0.f, sp = 0.f, sc = 0.f;
-  for (int ch = lane; ch < chunks; ch += 64) {
-    float fc[VE], fp[VE];
-    unpack16(ld16(c + ch * VE), fc, T());
-    unpack16(ld16(q + ch * VE), fp, T());
+  float sd = 0.f, sp = 0.f;
+  if (has_parent) {
+    for (int ch = lane; ch < chunks; ch += 64) {
+      float fc[VE], fp[VE];
+      unpack16(ld16(c + ch * VE), fc, T());
+      unpack16(ld16(q + ch * VE), fp, T());
 #pragma unroll
-    for (int e = 0; e < VE; ++e) {
-      const float df = fc[e] - fp[e];
-      sd = fmaf(df, df, sd);
-      sp = fmaf(fp[e], fp[e], sp);
-      sc = fmaf(fc[e], fc[e], sc);
+      for (int e = 0; e < VE; ++e) {
+        const float df = fc[e] - fp[e];
+        sd = fmaf(df, df, sd);
+        sp = fmaf(fp[e], fp[e], sp);
+      }
     }
+    sd = wave_sum(sd);
+    sp = wave_sum(sp);
   }
-  sd = wave_sum(sd);
-  sp = wave_sum(sp);
-  sc = wave_sum(sc);
-  if (lane == 0 && rstd) rstd[slot] = 1.0f / sqrtf(sc / (float)d + eps);
-  if (lane == 0 && decide) {
+  if (lane == 0) {
     float r;
     bool rec;
     if (!has_parent) {
@@ -302,11 +297,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ h,
 // ------------------------------------------------------------------------------------
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
-                       float* ratio, uint8_t* recompute, float* rstd, float eps,
-                       hipStream_t st) {
+                       float* ratio, uint8_t* recompute, hipStream_t st) {
   const int S = N * B;
   gate_kernel<T><<<ceil_div(S, 4), 256, 0, st>>>((const T*)H, fold_src, N, B, d, tau, ratio,
-                                                 recompute, rstd, eps);
+                                                 recompute);
   return hipGetLastError();
 }
 
@@ -365,9 +359,9 @@ template hipError_t launch_oproj_finish<bf16>(const float*, int, const void*, vo
                                               const void*, float, void*, int, hipStream_t);
 
 template hipError_t launch_gate<float>(const void*, const int32_t*, int, int, int, float, float*,
-                                       uint8_t*, float*, float, hipStream_t);
+                                       uint8_t*, hipStream_t);
 template hipError_t launch_gate<bf16>(const void*, const int32_t*, int, int, int, float, float*,
-                                      uint8_t*, float*, float, hipStream_t);
+                                      uint8_t*, hipStream_t);
 template hipError_t launch_rmsnorm_gather<float>(const void*, const int32_t*, const int32_t*, int,
                                                  int, int, float, const void*, void*, int,
                                                  hipStream_t);

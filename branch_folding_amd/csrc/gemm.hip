@@ -3,35 +3,37 @@
 //
 //   C[M, N] = A[M, Kd] . W[N, Kd]^T     A = packed activations, W = [out, in] weights
 //
-// With few packed rows these GEMMs stream the weights from HBM, so the kernel is shaped by
-// how the CU memory pipeline behaves on MI355X:
-//   * weight and activation tiles are fetched with fully coalesced 16-byte loads (8 lanes
-//     cover one 128-byte row segment), staged through padded LDS and read back in MFMA
-//     operand layout -- loading straight into operand layout (16 rows x 64 bytes per
-//     instruction) measured ~20% slower for the same bytes;
-//   * every workgroup re-reads the whole (small) activation tile from L2, and those hits
-//     occupy the same L1 request slots as the weight misses, so wide-N GEMMs use 256-column
-//     tiles (8 waves) to halve that traffic;
+// With few packed rows these GEMMs stream the weights from HBM while every tile's MFMA,
+// LDS and load work competes inside one CU, so the main loop is built to let those three
+// overlap instead of running in lock-step:
+//   * A and W tiles go global -> LDS with direct-to-LDS loads (global_load_lds_dwordx4):
+//     no VGPR staging, no ds_write instructions, nothing for the wave to wait on until the
+//     stage is consumed;
+//   * a ring of three LDS stages (separate arrays, so the compiler can see that the loads
+//     into one stage never alias the reads of another) keeps two k-iterations in flight;
+//     one s_waitcnt vmcnt + s_barrier per k-iteration publishes the oldest stage;
+//   * each load instruction writes 8 rows x 128 bytes contiguously; the 16-byte chunks of
+//     a row are XOR-swizzled by (row >> 1) & 7, so the loads stay fully coalesced (8 lanes
+//     per 128-byte row segment) and the MFMA operand reads (16 rows at one k chunk) hit 16
+//     distinct bank groups;
 //   * M (the packed row count) is known only on the device, so the kernel is persistent: a
 //     fixed grid reads M, derives the tile count and a split-K factor, and walks the work
 //     units, XCD-major so the M tiles of one weight tile share an XCD's L2.
 // Split-K partial sums (fp32) are reduced by a separate kernel in split order, so results
 // are deterministic and no device-scope fences are needed.
-// Wave tile 64 x 64 (4 x 4 MFMA 16x16 tiles); a k-iteration is 128 bytes of K; loads run
-// two k-iterations ahead through a register ring, staged into double-buffered LDS.
+// Wave tile 64 x 64 (4 x 4 MFMA 16x16 tiles); a k-iteration is 128 bytes of K.
 #include "common.h"
 #include "kernels.h"
 
 namespace specfold {
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
 template <typename T>
 struct GemmTile {
   static constexpr int VE = 16 / sizeof(T);               // elements per 16 bytes
   static constexpr int BK = kGemmBKBytes / sizeof(T);     // elements per k-iteration
-  // LDS row stride: 32 bytes of padding make the 16-byte operand reads of 16 rows x 2 lane
-  // groups conflict-free on gfx950's LDS (16 bytes of padding measured ~2.9 conflict
-  // cycles per LDS instruction).
-  static constexpr int LDR = BK + 2 * VE;
 };
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
@@ -48,22 +50,31 @@ __device__ __forceinline__ int w_row_of(int c, int N, int ff) {
   return c < N ? c : N - 1;
 }
 
-// k-iterations in flight in registers per thread (ring slots).
-template <int BN> struct GemmDepth { static constexpr int PD = 2; };
+// Byte offset of logical 16-byte chunk c of tile row r inside an LDS stage.
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * kGemmBKBytes + ((c ^ ((r >> 1) & 7)) << 4);
+}
 
-// NORMA: the A operand is gathered through p.a_rows and RMS-normalised on its way into LDS
-// (row scale p.a_scale, column gain p.a_gain), which fuses the pre-attention RMSNorm.
-template <typename T, int EPI, int BN, bool NORMA>
+// s_waitcnt immediate that waits until at most n vector-memory operations are pending
+// (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt left at "no wait").
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+constexpr int kGemmStages = 3;
+
+template <typename T, int EPI, int BN>
 __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
   using G = GemmTile<T>;
-  constexpr int VE = G::VE, LDR = G::LDR;
   constexpr int NT = BN * 2;                 // threads
+  constexpr int NW = NT / 64;                // waves
   constexpr int WN = BN / 64;                // waves along N
-  constexpr int AJ = kGemmBM * 8 / NT;       // 16-byte A chunks per thread per k-iteration
-  constexpr int WJ = BN * 8 / NT;            // 16-byte W chunks per thread per k-iteration
-  constexpr int RSTEP = NT / 8;              // rows covered by one pass of the loader
-  __shared__ __attribute__((aligned(16))) T As[2][kGemmBM * LDR];
-  __shared__ __attribute__((aligned(16))) T Ws[2][BN * LDR];
+  constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
+  constexpr int W_BYTES = BN * kGemmBKBytes;
+  constexpr int AQ = A_BYTES / 1024 / NW;    // A load instructions per wave per k-iteration
+  constexpr int WQ = W_BYTES / 1024 / NW;    // W load instructions per wave per k-iteration
+  constexpr int LPI = AQ + WQ;               // vector-memory ops per wave per k-iteration
+  static_assert(AQ >= 1 && WQ >= 1 && A_BYTES % (1024 * NW) == 0, "tile/loader mismatch");
+  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
 
   const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
   if (M <= 0) return;
@@ -79,6 +90,9 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
   const int g4 = lane >> 4, l16 = lane & 15;
   const char* Ab = (const char*)p.A;
   const char* Wb = (const char*)p.W;
+  // loader geometry: instruction q of this wave fills rows 8*blk .. 8*blk+7 of a stage;
+  // lane i carries row 8*blk + i/8, physical chunk i%8 (logical chunk swizzled back)
+  const int lr = lane >> 3, lpc = lane & 7;
 
   for (int u = blockIdx.x; u < per_xcd * 8; u += gridDim.x) {
     const int v = (u & 7) * per_xcd + (u >> 3);       // XCD u%8 owns a contiguous range
@@ -88,53 +102,33 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
     const int m0 = mt * kGemmBM, n0 = ntile * BN;
     const int kb = (int)((long)s * kiters / split), ke = (int)((long)(s + 1) * kiters / split);
 
-    const int lrow = tid >> 3, lcol = tid & 7;
-    const char* a_src[AJ];
-    const char* w_src[WJ];
-    float a_sc[AJ];
+    const char* a_src[AQ];
+    const char* w_src[WQ];
 #pragma unroll
-    for (int j = 0; j < AJ; ++j) {
-      int ar = imin(m0 + lrow + RSTEP * j, M - 1);
-      if (NORMA) {
-        ar = imin(imax(p.a_rows[ar], 0), p.a_rows_cap - 1);
-        a_sc[j] = p.a_scale[ar];
-      }
-      a_src[j] = Ab + ((size_t)ar * p.lda + (size_t)lcol * VE) * sizeof(T);
+    for (int q = 0; q < AQ; ++q) {
+      const int r = (wave * AQ + q) * 8 + lr;
+      const int c = lpc ^ ((r >> 1) & 7);
+      const int ar = imin(m0 + r, M - 1);
+      a_src[q] = Ab + (size_t)ar * p.lda * sizeof(T) + c * 16;
     }
-    const char* g_src = NORMA ? (const char*)p.a_gain + (size_t)lcol * VE * sizeof(T) : nullptr;
 #pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-      const int wr = w_row_of<EPI, BN>(n0 + lrow + RSTEP * j, p.N, p.ff);
-      w_src[j] = Wb + ((size_t)wr * p.ldw + (size_t)lcol * VE) * sizeof(T);
+    for (int q = 0; q < WQ; ++q) {
+      const int r = (wave * WQ + q) * 8 + lr;
+      const int c = lpc ^ ((r >> 1) & 7);
+      const int wr = w_row_of<EPI, BN>(n0 + r, p.N, p.ff);
+      w_src[q] = Wb + (size_t)wr * p.ldw * sizeof(T) + c * 16;
     }
-    constexpr int PD = GemmDepth<BN>::PD;
-    uint4 ra[PD][AJ], rw[PD][WJ], rg[PD];
-    // loads past the unit's last k-iteration are clamped to it (cache hits, unused)
-    auto gload = [&](int slot, int it) {
+    // Stage loads of k-iteration `it` (clamped to the unit's last one: cache hits, unused).
+    auto issue = [&](char* as, char* ws, int it) {
       const size_t off = (size_t)imin(it, ke - 1) * kGemmBKBytes;
 #pragma unroll
-      for (int j = 0; j < WJ; ++j) rw[slot][j] = ld16(w_src[j] + off);
+      for (int q = 0; q < WQ; ++q)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(w_src[q] + off),
+                                         (lds_void_t*)(ws + (wave * WQ + q) * 1024), 16, 0, 0);
 #pragma unroll
-      for (int j = 0; j < AJ; ++j) ra[slot][j] = ld16(a_src[j] + off);
-      if (NORMA) rg[slot] = ld16(g_src + off);
-    };
-    auto lstore = [&](int buf, int slot) {
-#pragma unroll
-      for (int j = 0; j < AJ; ++j) {
-        uint4 av = ra[slot][j];
-        if (NORMA) {
-          float x[VE], gv[VE];
-          unpack16(av, x, T());
-          unpack16(rg[slot], gv, T());
-#pragma unroll
-          for (int e = 0; e < VE; ++e) x[e] = x[e] * a_sc[j] * gv[e];
-          av = pack16(x, T());
-        }
-        *reinterpret_cast<uint4*>(&As[buf][(lrow + RSTEP * j) * LDR + lcol * VE]) = av;
-      }
-#pragma unroll
-      for (int j = 0; j < WJ; ++j)
-        *reinterpret_cast<uint4*>(&Ws[buf][(lrow + RSTEP * j) * LDR + lcol * VE]) = rw[slot][j];
+      for (int q = 0; q < AQ; ++q)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[q] + off),
+                                         (lds_void_t*)(as + (wave * AQ + q) * 1024), 16, 0, 0);
     };
 
     f32x4 acc[4][4];
@@ -144,48 +138,45 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool rows_live = (m0 + wm * 64) < M;
 
-    auto compute = [&](int cur) {
+    auto compute = [&](const char* as, const char* ws) {
       if (!rows_live) return;
-      const T* as = As[cur];
-      const T* ws = Ws[cur];
 #pragma unroll
       for (int ks = 0; ks < kGemmBKBytes / 64; ++ks) {
         uint4 af[4], bfr[4];
-        const int koff = ks * 4 * VE + g4 * VE;
+        const int c = ks * 4 + g4;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const uint4*>(&as[(wm * 64 + i * 16 + l16) * LDR + koff]);
+          af[i] = *reinterpret_cast<const uint4*>(as + swz(wm * 64 + i * 16 + l16, c));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          bfr[j] = *reinterpret_cast<const uint4*>(&ws[(wn * 64 + j * 16 + l16) * LDR + koff]);
+          bfr[j] = *reinterpret_cast<const uint4*>(ws + swz(wn * 64 + j * 16 + l16, c));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = mma_kstep(af[i], bfr[j], acc[i][j], T());
       }
     };
-    // One k-iteration: refill the register slot whose data is already in LDS, run the
-    // MFMAs, stage the next iteration into the other LDS buffer.  Whole ring turns run
-    // without per-iteration conditions so the wait counts stay PD - 1 iterations deep.
-    // LDS buffer parity is relative to the unit's first k-iteration (staged into buffer 0)
-    auto step = [&](int q, int it) {
-      gload(q, it + PD);
-      compute((it - kb) & 1);
-      lstore((it - kb + 1) & 1, (q + 1) % PD);
-      __syncthreads();
+    // k-iteration i on stage (as, ws): once this wave's loads of i have landed (only the
+    // LPI loads of i + 1 may still be pending) and every wave has passed the barrier --
+    // so all loads of i are visible and nobody still reads the stage that held i - 1 --
+    // the loads of i + 2 go into that freed stage and the MFMAs run on stage i.
+    auto body = [&](char* as, char* ws, char* as2, char* ws2, int i) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPI));
+      __builtin_amdgcn_s_barrier();
+      issue(as2, ws2, i + 2);
+      if (i < ke) compute(as, ws);
     };
-#pragma unroll
-    for (int q = 0; q < PD; ++q) gload(q, kb + q);
-    lstore(0, 0);
-    __syncthreads();
-    int it = kb;
-    for (; it + PD <= ke; it += PD) {
-#pragma unroll
-      for (int q = 0; q < PD; ++q) step(q, it + q);
+
+    // every wave is done with the previous unit's stages and its loads have landed
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    issue(As0, Ws0, kb);
+    issue(As1, Ws1, kb + 1);
+    for (int it = kb; it < ke; it += kGemmStages) {
+      body(As0, Ws0, As2, Ws2, it);
+      body(As1, Ws1, As0, Ws0, it + 1);
+      body(As2, Ws2, As1, Ws1, it + 2);
     }
-#pragma unroll
-    for (int q = 0; q < PD - 1; ++q)
-      if (it + q < ke) step(q, it + q);
 
     // epilogue: lane holds rows (g4*4 + r) and column l16 of every 16x16 tile
     if (split == 1 && EPI != kEpiPartial) {
@@ -238,6 +229,8 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
         }
     }
   }
+  // no wave may end while its last (clamped) stage loads are still writing LDS
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 // Sums the split-K partials in split order and applies the epilogue (4 outputs / thread).
@@ -316,11 +309,7 @@ size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always)
 
 template <typename T, int EPI, int BN>
 static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st) {
-  const int grid = (BN == 256 ? 1 : 2) * num_cu;
-  if (p.a_rows)
-    gemm_kernel<T, EPI, BN, true><<<grid, BN * 2, 0, st>>>(p);
-  else
-    gemm_kernel<T, EPI, BN, false><<<grid, BN * 2, 0, st>>>(p);
+  gemm_kernel<T, EPI, BN><<<num_cu, BN * 2, 0, st>>>(p);
   // the reduction only runs when some row count could make the device choose split > 1
   if (EPI != kEpiPartial && ceil_div(p.N, BN) < kGemmMinTiles) {
     const int Nout = (EPI == kEpiSwiGLU) ? p.ff : p.N;

@@ -12,12 +12,10 @@ namespace specfold {
 constexpr int kResolve = 1;
 constexpr int kPack = 2;
 
-// Gate: writes ratio[slot] and recompute[slot] where those pointers are non-null (the
-// ratio needs fold_src), and rstd[slot] = 1/sqrt(mean(H[slot]^2) + eps) when rstd is.
+// Gate: writes ratio[slot] and recompute[slot] where those pointers are non-null.
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
-                       float* ratio, uint8_t* recompute, float* rstd, float eps,
-                       hipStream_t st);
+                       float* ratio, uint8_t* recompute, hipStream_t st);
 size_t resolve_pack_lds_bytes(int S);
 hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,
                                const int32_t* src_in, int N, int B, int mode, int32_t* src_out,
@@ -54,12 +52,6 @@ struct GemmParams {
   int N;             // logical output columns (2*ff for SwiGLU)
   int Kd;
   int ff;            // SwiGLU only
-  // Optional fused RMSNorm on the A operand: row m of A is row a_rows[m] of `A` (clamped to
-  // [0, a_rows_cap)), multiplied by a_scale[that row] and by a_gain[k] before rounding.
-  const int32_t* a_rows;
-  int a_rows_cap;
-  const float* a_scale;
-  const void* a_gain;
 };
 
 constexpr int kGemmBM = 128;

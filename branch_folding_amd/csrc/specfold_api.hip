@@ -106,7 +106,7 @@ size_t padded_ld(size_t cols, size_t eb) { return cols + 128 / eb; }
 // Workspace layout of one layer.
 struct Layout {
   size_t ratio, rec, src, packed, slot_row, count;
-  size_t rstd, qkv, part_o, part_lse, attn, h, a2, G, F, gpart;
+  size_t qkv, part_o, part_lse, attn, h, a2, G, F, gpart;
   size_t total;
   size_t ld_d, ld_qkv, ld_q, ld_ff;   // padded row strides (elements)
 };
@@ -142,7 +142,6 @@ Layout layout_of(const specfold_shape* s) {
   L.packed = take(S * 4);
   L.slot_row = take(S * 4);
   L.count = take(256);
-  L.rstd = take(S * 4);
   L.qkv = take(S * L.ld_qkv * eb);
   L.part_o = take(prow * qd * 4);
   L.part_lse = take(prow * (size_t)s->n_q_heads * 4);
@@ -175,12 +174,11 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
     void* ev = begin ? probe->start : probe->stop;
     return ev ? hipEventRecord((hipEvent_t)ev, st) : hipSuccess;
   };
-  float* rstd = (float*)(ws + L.rstd);
-  // the gate pass also yields every row's RMSNorm scale; with a given fold state it
-  // writes no mask, and ratios only into a caller's ratio buffer
+  // with a given fold state the gate writes no mask, and runs only to fill a caller's
+  // ratio buffer
   HIP_CHECK(mark(SPECFOLD_STEP_GATE, true));
-  HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, state_in ? nullptr : rec, rstd,
-                           s->rms_eps, st));
+  if (!state_in || ratio)
+    HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, state_in ? nullptr : rec, st));
   HIP_CHECK(mark(SPECFOLD_STEP_GATE, false));
   if (!state_in) {
     HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, true));
@@ -197,10 +195,15 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   float* gpart = (float*)(ws + L.gpart);
 
 
+  // gathered, RMS-normalised packed rows (A1 shares its buffer with the FFN input A2,
+  // which is written only after the QKV GEMM has consumed A1)
+  HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM1, true));
+  HIP_CHECK(launch_rmsnorm_gather<T>(hin, packed, count, S, S, d, s->rms_eps, w->rms1, A2,
+                                     (int)L.ld_d, st));
+  HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM1, false));
+
   GemmParams gp{};
-  // RMSNorm of the packed rows is applied inside the GEMM's A loader
-  gp.A = hin; gp.lda = d; gp.a_rows = packed; gp.a_rows_cap = S; gp.a_scale = rstd;
-  gp.a_gain = w->rms1; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = L.ld_qkv;
+  gp.A = A2; gp.lda = L.ld_d; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = L.ld_qkv;
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = qkvd; gp.Kd = d;
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
@@ -369,10 +372,10 @@ specfold_status specfold_gate(const specfold_shape* shape, const void* hidden,
   (void)hipGetLastError();   // do not report an earlier, unrelated failure
   if (sh->dtype == SPECFOLD_BF16) {
     HIP_CHECK(launch_gate<bf16>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
-                                ratio, recompute, nullptr, 0.f, s));
+                                ratio, recompute, s));
   } else {
     HIP_CHECK(launch_gate<float>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
-                                 ratio, recompute, nullptr, 0.f, s));
+                                 ratio, recompute, s));
   }
   return ok();
 }

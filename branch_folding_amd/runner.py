@@ -141,12 +141,16 @@ class DeviceStack:
 
     def load_states(self, states) -> None:
         """Copy per-layer fold states (recompute, src_node, packed_slot, slot_row,
-        packed_count as host arrays) into the device buffers."""
-        for dev, st in zip(self.states, states):
-            for k in ("recompute", "src_node", "packed_slot", "slot_row", "packed_count"):
-                v = np.asarray(st[k]).reshape(-1)
-                v = v.astype(np.uint8 if k == "recompute" else np.int32)
-                dev[k][: v.size].copy_(torch.from_numpy(v).to(self.device))
+        packed_count as host arrays) into the device buffers of layers 0, 1, ..."""
+        for l, st in enumerate(states):
+            self._load_state(l, st)
+
+    def _load_state(self, l: int, st) -> None:
+        dev = self.states[l]
+        for k in ("recompute", "src_node", "packed_slot", "slot_row", "packed_count"):
+            v = np.asarray(st[k]).reshape(-1)
+            v = v.astype(np.uint8 if k == "recompute" else np.int32)
+            dev[k][: v.size].copy_(torch.from_numpy(v).to(self.device))
 
     def forward(self, tau: float, stream=None, state_in: bool = False,
                 record_states: bool = True) -> torch.Tensor:
@@ -154,6 +158,26 @@ class DeviceStack:
         L.specfold_stack_forward(self.shape, self.w, self.prefix if self.cfg.prefix else None,
                                  self.H, self.out, self.fold_src, tau,
                                  self.states if (record_states or state_in) else None, flags,
+                                 self.ws, self.ws_bytes, stream)
+        return self.out
+
+    def layer_forward(self, l: int, x, tau: float, stream=None, state_in=None) -> torch.Tensor:
+        """Layer l alone (specfold_layer_forward) on hidden state x, with the stack's
+        buffers; the fold state goes to (or, given state_in, comes from) layer l's state
+        buffers."""
+        if not hasattr(self, "xbuf"):
+            self.xbuf = torch.empty_like(self.H)
+        if isinstance(x, torch.Tensor):
+            self.xbuf.copy_(x.reshape(self.xbuf.shape))
+        else:
+            self.xbuf.copy_(to_device(np.asarray(x, dtype=np.float32).reshape(self.xbuf.shape),
+                                      self.dt, self.device))
+        flags = 0
+        if state_in is not None:
+            self._load_state(l, state_in)
+            flags = L.SPECFOLD_FLAG_FOLD_STATE_IN
+        L.specfold_layer_forward(self.shape, self.w[l], self.prefix[l] if self.cfg.prefix else None,
+                                 self.xbuf, self.out, self.fold_src, tau, self.states[l], flags,
                                  self.ws, self.ws_bytes, stream)
         return self.out
 
