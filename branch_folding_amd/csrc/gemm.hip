@@ -233,6 +233,159 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
+// ---------------------------------------------------------------------------------------
+// SwiGLU gate/up GEMM in column slabs.  The ff/16 (gate, up) pairs of 16-column blocks are
+// dealt out in contiguous ranges of P or P+1 pairs, one unit per CU, so every CU streams an
+// equal share of the weights with no split-K partials: a fixed 256-column tiling leaves
+// ~40% of the CUs idle at the 7B shape, and one CU cannot pull much more than ~30 GB/s
+// from HBM on its own.  A unit has 4 waves; each covers 32 rows and every block of the
+// slab, so both halves of an output element land in the same lane.  The main loop is the
+// same direct-to-LDS three-stage ring as gemm_kernel, templated on P so that the per-wave
+// load count (and with it the s_waitcnt immediate) is a compile-time constant.
+// ---------------------------------------------------------------------------------------
+constexpr int kSlabMaxPairs = 6;
+constexpr int kSlabThreads = 256;
+
+template <typename T, int P>
+__device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, int pair0,
+                                          char* As0, char* As1, char* As2, char* Ws0,
+                                          char* Ws1, char* Ws2) {
+  using G = GemmTile<T>;
+  constexpr int NB = 2 * P;                  // 16-column blocks: gate_0, up_0, gate_1, ...
+  constexpr int AQ = kGemmBM * kGemmBKBytes / 1024 / 4;   // A loads per wave (4)
+  constexpr int WQ = NB * 16 * kGemmBKBytes / 1024 / 4;   // W loads per wave (P)
+  constexpr int LPI = AQ + WQ;
+  const int kiters = p.Kd / G::BK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int lr = lane >> 3, lpc = lane & 7;
+  const char* Ab = (const char*)p.A;
+  const char* Wb = (const char*)p.W;
+
+  const char* a_src[AQ];
+  const char* w_src[WQ];
+#pragma unroll
+  for (int q = 0; q < AQ; ++q) {
+    const int r = (wave * AQ + q) * 8 + lr;
+    const int c = lpc ^ ((r >> 1) & 7);
+    a_src[q] = Ab + (size_t)imin(m0 + r, M - 1) * p.lda * sizeof(T) + c * 16;
+  }
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) {
+    const int r = (wave * WQ + q) * 8 + lr;           // stage row: block r/16, row r%16
+    const int c = lpc ^ ((r >> 1) & 7);
+    const int b = r >> 4;
+    const int j = (pair0 + (b >> 1)) * 16 + (r & 15);
+    const int wr = (b & 1) ? p.ff + j : j;
+    w_src[q] = Wb + (size_t)wr * p.ldw * sizeof(T) + c * 16;
+  }
+  auto issue = [&](char* as, char* ws, int it) {
+    const size_t off = (size_t)imin(it, kiters - 1) * kGemmBKBytes;
+#pragma unroll
+    for (int q = 0; q < WQ; ++q)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(w_src[q] + off),
+                                       (lds_void_t*)(ws + (wave * WQ + q) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < AQ; ++q)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[q] + off),
+                                       (lds_void_t*)(as + (wave * AQ + q) * 1024), 16, 0, 0);
+  };
+
+  f32x4 acc[2][NB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool rows_live = (m0 + wave * 32) < M;
+  auto compute = [&](const char* as, const char* ws) {
+    if (!rows_live) return;
+#pragma unroll
+    for (int ks = 0; ks < kGemmBKBytes / 64; ++ks) {
+      const int c = ks * 4 + g4;
+      uint4 af[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(as + swz(wave * 32 + i * 16 + l16, c));
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint4 bf = *reinterpret_cast<const uint4*>(ws + swz(j * 16 + l16, c));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][j] = mma_kstep(af[i], bf, acc[i][j], T());
+      }
+    }
+  };
+  auto body = [&](char* as, char* ws, char* as2, char* ws2, int i) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPI));
+    __builtin_amdgcn_s_barrier();
+    issue(as2, ws2, i + 2);
+    if (i < kiters) compute(as, ws);
+  };
+
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_barrier();
+  issue(As0, Ws0, 0);
+  issue(As1, Ws1, 1);
+  for (int it = 0; it < kiters; it += kGemmStages) {
+    body(As0, Ws0, As2, Ws2, it);
+    body(As1, Ws1, As0, Ws0, it + 1);
+    body(As2, Ws2, As1, Ws1, it + 2);
+  }
+
+  // epilogue: lane holds rows g4*4 + r of each 16-row block and column l16 of each block
+  T* C = (T*)p.C;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int pr = 0; pr < P; ++pr) {
+      const int col = (pair0 + pr) * 16 + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wave * 32 + i * 16 + g4 * 4 + r;
+        if (row < M) {
+          const float gv = acc[i][2 * pr][r], uv = acc[i][2 * pr + 1][r];
+          C[(size_t)row * p.ldc + col] = from_f32<T>(silu_f(gv) * uv);
+        }
+      }
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kSlabThreads) swiglu_slab_kernel(GemmParams p, int slabs) {
+  constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
+  constexpr int W_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
+  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
+  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
+  if (M <= 0) return;
+  const int pairs = p.ff / 16;
+  const int base = pairs / slabs, rem = pairs - base * slabs;
+  const int mb = ceil_div(M, kGemmBM);
+  for (int u = blockIdx.x; u < mb * slabs; u += gridDim.x) {
+    const int mt = u / slabs, sl = u - mt * slabs;
+    const int np = base + (sl < rem ? 1 : 0);
+    const int pair0 = sl * base + imin(sl, rem);
+    const int m0 = mt * kGemmBM;
+    switch (np) {
+      case 1: slab_unit<T, 1>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
+      case 2: slab_unit<T, 2>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
+      case 3: slab_unit<T, 3>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
+      case 4: slab_unit<T, 4>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
+      case 5: slab_unit<T, 5>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
+      case 6: slab_unit<T, 6>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
+      default: break;          // the host never makes slabs wider than kSlabMaxPairs
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+// Slab count for an ff-wide SwiGLU GEMM: one per CU, unless that needs wider slabs.
+static int swiglu_slabs(int ff, int num_cu) {
+  const int pairs = ff / 16;
+  int slabs = pairs < num_cu ? pairs : num_cu;
+  if (ceil_div(pairs, slabs) > kSlabMaxPairs) slabs = ceil_div(pairs, kSlabMaxPairs);
+  return slabs;
+}
+
 // Sums the split-K partials in split order and applies the epilogue (4 outputs / thread).
 template <typename T, int EPI, int BN>
 __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
@@ -311,7 +464,8 @@ template <typename T, int EPI, int BN>
 static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st) {
   gemm_kernel<T, EPI, BN><<<num_cu, BN * 2, 0, st>>>(p);
   // the reduction only runs when some row count could make the device choose split > 1
-  if (EPI != kEpiPartial && ceil_div(p.N, BN) < kGemmMinTiles) {
+  if (EPI != kEpiPartial &&
+      gemm_split(ceil_div(p.N, BN), p.Kd / (kGemmBKBytes / (int)sizeof(T))) > 1) {
     const int Nout = (EPI == kEpiSwiGLU) ? p.ff : p.N;
     const long total = (long)p.m_cap * (Nout / 4);
     const int rgrid = (int)((total + 255) / 256 < 2048 ? (total + 255) / 256 : 2048);
@@ -322,6 +476,11 @@ static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st
 
 template <typename T, int EPI>
 static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t st) {
+  if (EPI == kEpiSwiGLU) {
+    const int slabs = swiglu_slabs(p.ff, num_cu);
+    swiglu_slab_kernel<T><<<slabs, kSlabThreads, 0, st>>>(p, slabs);
+    return hipGetLastError();
+  }
   return gemm_tile_n(p.N) == 256 ? launch_gemm_bn<T, EPI, 256>(p, num_cu, st)
                                  : launch_gemm_bn<T, EPI, 128>(p, num_cu, st);
 }

@@ -56,24 +56,22 @@ struct GemmParams {
 
 constexpr int kGemmBM = 128;
 constexpr int kGemmBKBytes = 128;
-constexpr int kGemmMaxSplit = 16;
-// Tile counts at or above this keep every CU streaming without splitting K.
-constexpr int kGemmMinTiles = 128;
+constexpr int kGemmMaxSplit = 24;
+// Split-K keeps units >= this many k-iterations long, so a unit's fp32 partial plane stays
+// small next to the weight bytes it streams.
+constexpr int kGemmMinUnitIters = 8;
 
 // Split-K factor chosen on the device from the tile count (the packed row count is only
-// known there); kiters = number of 128-byte k-iterations.
-// Split-K targets about this many work units: with 256-column tiles each unit keeps one CU
-// streaming, and fewer, longer units keep the split-K partial traffic small.
-constexpr int kGemmTargetUnits = 144;
+// known there); kiters = number of 128-byte k-iterations.  One CU pulls only a fraction of
+// HBM bandwidth on its own, so the work is split until there is about one unit per CU
+// (never more: a second round on some CUs costs as much as the whole first one).
 __host__ __device__ inline int gemm_split(int tiles, int kiters) {
   if (tiles <= 0) return 1;
-  if (tiles >= kGemmMinTiles) return 1;
-  int s = (kGemmTargetUnits + tiles - 1) / tiles;
-  int smax = kiters / 4;
-  if (smax < 1) smax = 1;
+  int s = kPlanCUs / tiles;
+  const int smax = kiters / kGemmMinUnitIters;
   if (s > smax) s = smax;
   if (s > kGemmMaxSplit) s = kGemmMaxSplit;
-  return s;
+  return s < 1 ? 1 : s;
 }
 
 template <typename T>

@@ -123,7 +123,6 @@ Layout layout_of(const specfold_shape* s) {
   const int ebi = (int)eb;
   gp = std::max(gp, gemm_partial_elems((int)S, (int)qkvd, (int)d, ebi));
   gp = std::max(gp, gemm_partial_elems((int)S, (int)d, (int)qd, ebi, true));
-  gp = std::max(gp, gemm_partial_elems((int)S, (int)(2 * ff), (int)d, ebi));
   gp = std::max(gp, gemm_partial_elems((int)S, (int)d, (int)ff, ebi));
   Layout L;
   L.ld_d = padded_ld(d, eb);
