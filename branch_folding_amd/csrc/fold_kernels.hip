@@ -10,37 +10,84 @@ namespace specfold {
 // Gate (SpecFold explainer, paragraph on measuring ||H_child - H_parent|| / ||H_parent||
 // at the layer input).  One wave per slot; fp32 sums of squares; fold iff r <= tau.
 // ratio and recompute are each optional (a caller-given fold state needs ratios only).
+// With `An` the same pass also writes every slot's RMS-normalised row
+// An[slot] = H[slot] / sqrt(mean(H[slot]^2) + eps) * g (the QKV GEMM gathers the packed
+// ones), so the layer input is read once for both.  Loads go four 16-byte chunks per lane
+// at a time so a row costs a couple of memory round trips, not one per chunk.
 // ------------------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
                                                    const int32_t* __restrict__ fold_src,
                                                    int N, int B, int d, float tau,
                                                    float* __restrict__ ratio,
-                                                   uint8_t* __restrict__ recompute) {
+                                                   uint8_t* __restrict__ recompute,
+                                                   const T* __restrict__ g, float eps,
+                                                   T* __restrict__ An, int ld_an) {
   const int lane = threadIdx.x & 63;
   const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (slot >= N * B) return;
   const int n = slot / B, i = slot - n * B;
+  const bool decide = (ratio != nullptr) || (recompute != nullptr);
   int p = -1;
-  if (n > 0 && fold_src) p = fold_src[n];
+  if (n > 0 && decide && fold_src) p = fold_src[n];
   const bool has_parent = (n > 0) && (p >= 0) && (p < n);
   const T* c = H + (size_t)slot * d;
   const T* q = has_parent ? H + ((size_t)p * B + i) * d : c;
   constexpr int VE = Pack16<T>::kElems;
+  constexpr int U = 4;                       // chunks per lane in flight
   const int chunks = d / VE;
-  float sd = 0.f, sp = 0.f;
-  if (has_parent) {
-    for (int ch = lane; ch < chunks; ch += 64) {
-      float fc[VE], fp[VE];
-      unpack16(ld16(c + ch * VE), fc, T());
-      unpack16(ld16(q + ch * VE), fp, T());
+  float sd = 0.f, sp = 0.f, sc = 0.f;
+  for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
+    uint4 vc[U], vp[U];
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const float df = fc[e] - fp[e];
-        sd = fmaf(df, df, sd);
-        sp = fmaf(fp[e], fp[e], sp);
+    for (int u = 0; u < U; ++u) {
+      const int ch = imin(c0 + 64 * u, chunks - 1);
+      vc[u] = ld16(c + ch * VE);
+      if (has_parent) vp[u] = ld16(q + ch * VE);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + 64 * u >= chunks) break;
+      float fc[VE], fp[VE];
+      unpack16(vc[u], fc, T());
+#pragma unroll
+      for (int e = 0; e < VE; ++e) sc = fmaf(fc[e], fc[e], sc);
+      if (has_parent) {
+        unpack16(vp[u], fp, T());
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const float df = fc[e] - fp[e];
+          sd = fmaf(df, df, sd);
+          sp = fmaf(fp[e], fp[e], sp);
+        }
       }
     }
+  }
+  if (An) {
+    const float rstd = 1.0f / sqrtf(wave_sum(sc) / (float)d + eps);
+    T* o = An + (size_t)slot * ld_an;
+    for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
+      uint4 vc[U], vg[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ch = imin(c0 + 64 * u, chunks - 1);
+        vc[u] = ld16(c + ch * VE);
+        vg[u] = ld16(g + ch * VE);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (c0 + 64 * u >= chunks) break;
+        float fc[VE], fg[VE];
+        unpack16(vc[u], fc, T());
+        unpack16(vg[u], fg, T());
+#pragma unroll
+        for (int e = 0; e < VE; ++e) fc[e] = fc[e] * rstd * fg[e];
+        st16(o + (c0 + 64 * u) * VE, pack16(fc, T()));
+      }
+    }
+  }
+  if (!decide) return;
+  if (has_parent) {
     sd = wave_sum(sd);
     sp = wave_sum(sp);
   }
@@ -82,37 +129,31 @@ __global__ void __launch_bounds__(kPackThreads) resolve_pack_kernel(
     int32_t* __restrict__ slot_row, int32_t* __restrict__ packed_count) {
   extern __shared__ int32_t lds[];
   const int S = N * B;
-  int32_t* src_l = lds;          // [S]
-  int32_t* rank_l = lds + S;     // [S]
+  int32_t* src_l = lds;                               // [S] source node of each slot
+  int32_t* rank_l = lds + S;                          // [S] parent slot, later packed row
+  uint8_t* rec_l = reinterpret_cast<uint8_t*>(lds + 2 * S);   // [S] computes its own row
   __shared__ int32_t wave_cnt[kPackThreads / 64];
   __shared__ int32_t base_sh;
   const int t = threadIdx.x;
   const bool do_resolve = (mode & kResolve) != 0;
   const bool do_pack = (mode & kPack) != 0;
 
-  // effective recompute flag of a slot: root rows and nodes with a malformed fold
-  // source always compute their own rows.
-  auto eff_rec = [&](int s) -> bool {
+  // One parallel pass over global memory: a slot computes its own row if it is a root
+  // row, marked for recompute, or its node has a malformed fold source; otherwise its
+  // parent slot is (fold_src[n], i).
+  for (int s = t; s < S; s += kPackThreads) {
     const int n = s / B;
-    return n == 0 || recompute[s] != 0 || (fold_src != nullptr && !node_ok(fold_src, n));
-  };
-
-  if (do_resolve) {
-    for (int i = t; i < B; i += kPackThreads) {
-      src_l[i] = 0;
-      for (int n = 1; n < N; ++n) {
-        const int s = n * B + i;
-        if (eff_rec(s)) {
-          src_l[s] = n;
-        } else {
-          src_l[s] = src_l[fold_src[n] * B + i];
-        }
-      }
+    bool own = (n == 0) || recompute[s] != 0;
+    int ps = s;
+    if (fold_src != nullptr && n > 0) {
+      const int f = fold_src[n];
+      if (f < 0 || f >= n) own = true;
+      else ps = f * B + (s - n * B);
     }
-  } else {
-    for (int s = t; s < S; s += kPackThreads) {
+    rec_l[s] = own ? 1 : 0;
+    if (do_resolve) rank_l[s] = ps;
+    else {
       int v = src_in[s];
-      const int n = s / B;
       // a source must be an earlier-or-equal node; anything else is treated as the slot
       // itself (memory safety for malformed inputs)
       if (v < 0 || v > n) v = n;
@@ -120,23 +161,32 @@ __global__ void __launch_bounds__(kPackThreads) resolve_pack_kernel(
     }
   }
   __syncthreads();
-  if (do_resolve && src_out) {
-    for (int s = t; s < S; s += kPackThreads) src_out[s] = src_l[s];
+  if (do_resolve) {
+    // one thread per position walks the nodes in topological order, in LDS only
+    for (int i = t; i < B; i += kPackThreads) {
+      src_l[i] = 0;
+      for (int n = 1; n < N; ++n) {
+        const int s = n * B + i;
+        src_l[s] = rec_l[s] ? n : src_l[rank_l[s]];
+      }
+    }
+    __syncthreads();
+    if (src_out)
+      for (int s = t; s < S; s += kPackThreads) src_out[s] = src_l[s];
   }
   if (!do_pack) return;
 
-  // stable compaction of recompute slots
+  // a slot is packed iff it computes its own row
+  auto packed_of = [&](int s) -> bool {
+    return do_resolve ? (src_l[s] == s / B) : (rec_l[s] != 0);
+  };
+  // stable compaction of the packed slots (ballot + popcount + per-wave offsets)
   const int lane = t & 63, wave = t >> 6;
   if (t == 0) base_sh = 0;
   __syncthreads();
   for (int c0 = 0; c0 < S; c0 += kPackThreads) {
     const int s = c0 + t;
-    bool f = false;
-    if (s < S) {
-      const int n = s / B;
-      // a slot is packed iff it computes its own row
-      f = do_resolve ? (src_l[s] == n) : eff_rec(s);
-    }
+    const bool f = (s < S) && packed_of(s);
     const uint64_t bal = __ballot(f);
     const int before = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
     if (lane == 0) wave_cnt[wave] = __popcll(bal);
@@ -157,84 +207,43 @@ __global__ void __launch_bounds__(kPackThreads) resolve_pack_kernel(
     __syncthreads();
   }
   for (int s = t; s < S; s += kPackThreads) {
-    const int i = s % B;
-    int src = src_l[s];
-    int target = src * B + i;
+    const int target = src_l[s] * B + s % B;
     // the source slot must be packed; fall back to the slot itself otherwise
     int k = -1;
-    {
-      const int n_src = src;
-      bool packed = do_resolve ? (src_l[target] == n_src) : eff_rec(target);
-      if (packed) k = rank_l[target];
-    }
-    if (k < 0) {
-      const bool self_packed = do_resolve ? (src_l[s] == s / B) : eff_rec(s);
-      k = self_packed ? rank_l[s] : 0;
-    }
+    if (packed_of(target)) k = rank_l[target];
+    if (k < 0) k = packed_of(s) ? rank_l[s] : 0;
     slot_row[s] = k;
   }
   if (t == 0) packed_count[0] = base_sh;
 }
 
 // ------------------------------------------------------------------------------------
-// Gathered RMSNorm: out[k] = X[rows[k]] / sqrt(mean(X^2) + eps) * g, for k < K (device).
-// One wave per packed row.
-// ------------------------------------------------------------------------------------
-template <typename T>
-__global__ void __launch_bounds__(256) rmsnorm_gather_kernel(
-    const T* __restrict__ X, const int32_t* __restrict__ rows, const int32_t* __restrict__ count,
-    int cap, int S, int d, float eps, const T* __restrict__ g, T* __restrict__ out, int ld_out) {
-  const int lane = threadIdx.x & 63;
-  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int K = imin(*count, cap);
-  if (k >= K) return;
-  int r = rows[k];
-  r = imin(imax(r, 0), S - 1);
-  const T* x = X + (size_t)r * d;
-  constexpr int VE = Pack16<T>::kElems;
-  const int chunks = d / VE;
-  float ss = 0.f;
-  for (int ch = lane; ch < chunks; ch += 64) {
-    float f[VE];
-    unpack16(ld16(x + ch * VE), f, T());
-#pragma unroll
-    for (int e = 0; e < VE; ++e) ss = fmaf(f[e], f[e], ss);
-  }
-  ss = wave_sum(ss);
-  const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
-  T* o = out + (size_t)k * ld_out;
-  for (int ch = lane; ch < chunks; ch += 64) {
-    float f[VE], w[VE];
-    unpack16(ld16(x + ch * VE), f, T());
-    unpack16(ld16(g + ch * VE), w, T());
-#pragma unroll
-    for (int e = 0; e < VE; ++e) f[e] = f[e] * rstd * w[e];
-    st16(o + ch * VE, pack16(f, T()));
-  }
-}
-
-// ------------------------------------------------------------------------------------
 // O-projection finish: h = H + sum of the split-K partials, then the FFN's RMSNorm for the
-// rows that are packed.  One wave per slot; pass 2 re-reads the row this lane just wrote.
+// rows that are packed.  One 256-thread workgroup per slot (enough workgroups to spread the
+// partial-plane reads over every CU); the row's sum of squares is reduced through LDS and
+// pass 2 re-reads the h chunks this thread just wrote.
 // ------------------------------------------------------------------------------------
+constexpr int kFinishThreads = 256;
+
 template <typename T>
-__global__ void __launch_bounds__(256) oproj_finish_kernel(
+__global__ void __launch_bounds__(kFinishThreads) oproj_finish_kernel(
     const float* __restrict__ partial, int split, const T* __restrict__ H, T* __restrict__ h,
     int S, int d, const int32_t* __restrict__ slot_row, const int32_t* __restrict__ packed_slot,
     const int32_t* __restrict__ count, const T* __restrict__ g, float eps, T* __restrict__ A2,
     int ld_a2) {
-  const int lane = threadIdx.x & 63;
-  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (s >= S) return;
+  __shared__ float red[kFinishThreads / 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int s = blockIdx.x;
   constexpr int VE = Pack16<T>::kElems;
   const int chunks = d / VE;
   const size_t plane = (size_t)S * d;
+  const size_t row = (size_t)s * d;
   float ss = 0.f;
-  for (int ch = lane; ch < chunks; ch += 64) {
+  for (int ch = t; ch < chunks; ch += kFinishThreads) {
     float x[VE];
-    unpack16(ld16(H + (size_t)s * d + ch * VE), x, T());
+    unpack16(ld16(H + row + ch * VE), x, T());
     for (int q = 0; q < split; ++q) {
-      const float* pp = partial + q * plane + (size_t)s * d + ch * VE;
+      const float* pp = partial + q * plane + row + ch * VE;
 #pragma unroll
       for (int e = 0; e < VE; e += 4) {
         const float4 v = *reinterpret_cast<const float4*>(pp + e);
@@ -242,20 +251,25 @@ __global__ void __launch_bounds__(256) oproj_finish_kernel(
       }
     }
     const uint4 hv = pack16(x, T());
-    st16(h + (size_t)s * d + ch * VE, hv);
+    st16(h + row + ch * VE, hv);
     float r[VE];
     unpack16(hv, r, T());                       // statistics of the rounded h
 #pragma unroll
     for (int e = 0; e < VE; ++e) ss = fmaf(r[e], r[e], ss);
   }
-  ss = wave_sum(ss);
   const int K = imin(*count, S);
   const int k = imin(imax(slot_row[s], 0), imax(K - 1, 0));
   if (K <= 0 || packed_slot[k] != s) return;     // not a packed row: no FFN input
-  const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int ch = lane; ch < chunks; ch += 64) {
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kFinishThreads / 64; ++w) tot += red[w];
+  const float rstd = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int ch = t; ch < chunks; ch += kFinishThreads) {
     float x[VE], w[VE];
-    unpack16(ld16(h + (size_t)s * d + ch * VE), x, T());
+    unpack16(ld16(h + row + ch * VE), x, T());
     unpack16(ld16(g + ch * VE), w, T());
 #pragma unroll
     for (int e = 0; e < VE; ++e) x[e] = x[e] * rstd * w[e];
@@ -297,14 +311,17 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ h,
 // ------------------------------------------------------------------------------------
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
-                       float* ratio, uint8_t* recompute, hipStream_t st) {
+                       float* ratio, uint8_t* recompute, const void* g, float eps,
+                       void* An, int ld_an, hipStream_t st) {
   const int S = N * B;
   gate_kernel<T><<<ceil_div(S, 4), 256, 0, st>>>((const T*)H, fold_src, N, B, d, tau, ratio,
-                                                 recompute);
+                                                 recompute, (const T*)g, eps, (T*)An, ld_an);
   return hipGetLastError();
 }
 
-size_t resolve_pack_lds_bytes(int S) { return (size_t)2 * S * sizeof(int32_t); }
+size_t resolve_pack_lds_bytes(int S) {
+  return (size_t)2 * S * sizeof(int32_t) + (((size_t)S + 3) & ~(size_t)3);
+}
 
 hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,
                                const int32_t* src_in, int N, int B, int mode, int32_t* src_out,
@@ -318,15 +335,6 @@ hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src
   }
   resolve_pack_kernel<<<1, kPackThreads, lds, st>>>(recompute, fold_src, src_in, N, B, mode,
                                                      src_out, packed_slot, slot_row, count);
-  return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_rmsnorm_gather(const void* X, const int32_t* rows, const int32_t* count,
-                                 int cap, int S, int d, float eps, const void* g, void* out,
-                                 int ld_out, hipStream_t st) {
-  rmsnorm_gather_kernel<T><<<ceil_div(cap, 4), 256, 0, st>>>(
-      (const T*)X, rows, count, cap, S, d, eps, (const T*)g, (T*)out, ld_out);
   return hipGetLastError();
 }
 
@@ -346,7 +354,7 @@ hipError_t launch_oproj_finish(const float* partial, int split, const void* H, v
                                int d, const int32_t* slot_row, const int32_t* packed_slot,
                                const int32_t* count, const void* g, float eps, void* A2,
                                int ld_a2, hipStream_t st) {
-  oproj_finish_kernel<T><<<ceil_div(S, 4), 256, 0, st>>>(partial, split, (const T*)H, (T*)h, S, d,
+  oproj_finish_kernel<T><<<S, kFinishThreads, 0, st>>>(partial, split, (const T*)H, (T*)h, S, d,
                                                           slot_row, packed_slot, count,
                                                           (const T*)g, eps, (T*)A2, ld_a2);
   return hipGetLastError();
@@ -359,15 +367,9 @@ template hipError_t launch_oproj_finish<bf16>(const float*, int, const void*, vo
                                               const void*, float, void*, int, hipStream_t);
 
 template hipError_t launch_gate<float>(const void*, const int32_t*, int, int, int, float, float*,
-                                       uint8_t*, hipStream_t);
+                                       uint8_t*, const void*, float, void*, int, hipStream_t);
 template hipError_t launch_gate<bf16>(const void*, const int32_t*, int, int, int, float, float*,
-                                      uint8_t*, hipStream_t);
-template hipError_t launch_rmsnorm_gather<float>(const void*, const int32_t*, const int32_t*, int,
-                                                 int, int, float, const void*, void*, int,
-                                                 hipStream_t);
-template hipError_t launch_rmsnorm_gather<bf16>(const void*, const int32_t*, const int32_t*, int,
-                                                int, int, float, const void*, void*, int,
-                                                hipStream_t);
+                                      uint8_t*, const void*, float, void*, int, hipStream_t);
 template hipError_t launch_combine<float>(const void*, const void*, const int32_t*, const int32_t*,
                                           int, int, int, void*, hipStream_t);
 template hipError_t launch_combine<bf16>(const void*, const void*, const int32_t*, const int32_t*,

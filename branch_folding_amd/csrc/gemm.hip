@@ -108,7 +108,8 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
     for (int q = 0; q < AQ; ++q) {
       const int r = (wave * AQ + q) * 8 + lr;
       const int c = lpc ^ ((r >> 1) & 7);
-      const int ar = imin(m0 + r, M - 1);
+      int ar = imin(m0 + r, M - 1);
+      if (p.a_rows) ar = imin(imax(p.a_rows[ar], 0), p.a_rows_cap - 1);
       a_src[q] = Ab + (size_t)ar * p.lda * sizeof(T) + c * 16;
     }
 #pragma unroll

@@ -12,19 +12,17 @@ namespace specfold {
 constexpr int kResolve = 1;
 constexpr int kPack = 2;
 
-// Gate: writes ratio[slot] and recompute[slot] where those pointers are non-null.
+// Gate: writes ratio[slot] and recompute[slot] where those pointers are non-null, and
+// with An every slot's normalised row An[slot] = H[slot] * rstd * g (row stride ld_an).
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
-                       float* ratio, uint8_t* recompute, hipStream_t st);
+                       float* ratio, uint8_t* recompute, const void* g, float eps, void* An,
+                       int ld_an, hipStream_t st);
 size_t resolve_pack_lds_bytes(int S);
 hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,
                                const int32_t* src_in, int N, int B, int mode, int32_t* src_out,
                                int32_t* packed_slot, int32_t* slot_row, int32_t* count,
                                hipStream_t st);
-template <typename T>
-hipError_t launch_rmsnorm_gather(const void* X, const int32_t* rows, const int32_t* count,
-                                 int cap, int S, int d, float eps, const void* g, void* out,
-                                 int ld_out, hipStream_t st);
 template <typename T>
 hipError_t launch_combine(const void* h, const void* F, const int32_t* slot_row,
                           const int32_t* count, int cap, int S, int d, void* y, hipStream_t st);
@@ -52,6 +50,10 @@ struct GemmParams {
   int N;             // logical output columns (2*ff for SwiGLU)
   int Kd;
   int ff;            // SwiGLU only
+  // optional row gather: row m of the A operand is row a_rows[m] of `A` (clamped to
+  // [0, a_rows_cap)); nullptr = row m
+  const int32_t* a_rows;
+  int a_rows_cap;
 };
 
 constexpr int kGemmBM = 128;
@@ -81,7 +83,7 @@ int gemm_host_split(int M, int N, int Kd, int elem_bytes);
 
 // Finish of the O projection: h[s] = H[s] + sum of `split` partial planes (rounded to T),
 // and for every packed slot s (packed_slot[slot_row[s]] == s) the FFN input
-// A2[slot_row[s]] = h[s] / sqrt(mean(h[s]^2) + eps) * g.  One wave per slot.
+// A2[slot_row[s]] = h[s] / sqrt(mean(h[s]^2) + eps) * g.  One workgroup per slot.
 template <typename T>
 hipError_t launch_oproj_finish(const float* partial, int split, const void* H, void* h, int S,
                                int d, const int32_t* slot_row, const int32_t* packed_slot,

@@ -173,11 +173,14 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
     void* ev = begin ? probe->start : probe->stop;
     return ev ? hipEventRecord((hipEvent_t)ev, st) : hipSuccess;
   };
-  // with a given fold state the gate writes no mask, and runs only to fill a caller's
-  // ratio buffer
+  // The gate pass also writes every slot's RMS-normalised row (QKV input) into A1, which
+  // shares its buffer with the FFN input A2 (written only after the QKV GEMM has consumed
+  // A1).  With a given fold state it writes no mask, and ratios only into a caller's
+  // ratio buffer.
+  void* A2 = ws + L.a2;
   HIP_CHECK(mark(SPECFOLD_STEP_GATE, true));
-  if (!state_in || ratio)
-    HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, state_in ? nullptr : rec, st));
+  HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, state_in ? nullptr : rec, w->rms1,
+                           s->rms_eps, A2, (int)L.ld_d, st));
   HIP_CHECK(mark(SPECFOLD_STEP_GATE, false));
   if (!state_in) {
     HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, true));
@@ -188,21 +191,14 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   void* QKV = ws + L.qkv;
   void* ATT = ws + L.attn;
   void* Hh = ws + L.h;
-  void* A2 = ws + L.a2;
   void* G = ws + L.G;
   void* F = ws + L.F;
   float* gpart = (float*)(ws + L.gpart);
 
 
-  // gathered, RMS-normalised packed rows (A1 shares its buffer with the FFN input A2,
-  // which is written only after the QKV GEMM has consumed A1)
-  HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM1, true));
-  HIP_CHECK(launch_rmsnorm_gather<T>(hin, packed, count, S, S, d, s->rms_eps, w->rms1, A2,
-                                     (int)L.ld_d, st));
-  HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM1, false));
-
+  // packed rows of A1 are gathered by the GEMM's loads
   GemmParams gp{};
-  gp.A = A2; gp.lda = L.ld_d; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = L.ld_qkv;
+  gp.A = A2; gp.lda = L.ld_d; gp.a_rows = packed; gp.a_rows_cap = S; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = L.ld_qkv;
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = qkvd; gp.Kd = d;
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
@@ -371,10 +367,10 @@ specfold_status specfold_gate(const specfold_shape* shape, const void* hidden,
   (void)hipGetLastError();   // do not report an earlier, unrelated failure
   if (sh->dtype == SPECFOLD_BF16) {
     HIP_CHECK(launch_gate<bf16>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
-                                ratio, recompute, s));
+                                ratio, recompute, nullptr, 0.f, nullptr, 0, s));
   } else {
     HIP_CHECK(launch_gate<float>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
-                                 ratio, recompute, s));
+                                 ratio, recompute, nullptr, 0.f, nullptr, 0, s));
   }
   return ok();
 }

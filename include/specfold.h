@@ -229,9 +229,9 @@ specfold_status specfold_stack_forward(const specfold_shape* shape, int32_t num_
 
 /* Launch steps of specfold_layer_forward, for timing probes. */
 typedef enum specfold_step {
-  SPECFOLD_STEP_GATE = 0,          /* gate                                            */
+  SPECFOLD_STEP_GATE = 0,          /* gate (also every slot's RMS-normalised row)     */
   SPECFOLD_STEP_RESOLVE_PACK = 1,  /* provenance + packing                            */
-  SPECFOLD_STEP_RMSNORM1 = 2,      /* gather + RMSNorm of the packed rows (QKV input) */
+  SPECFOLD_STEP_RMSNORM1 = 2,      /* fused into the gate: not recorded               */
   SPECFOLD_STEP_QKV = 3,           /* packed QKV GEMM (incl. its split-K reduction)   */
   SPECFOLD_STEP_ATTN_PREFIX = 4,   /* prefix-phase attention                          */
   SPECFOLD_STEP_ATTN_BLOCK = 5,    /* block-phase attention + merge                   */
