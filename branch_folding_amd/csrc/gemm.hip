@@ -298,22 +298,30 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool rows_live = (m0 + wave * 32) < M;
+  // One wave per SIMD, so LDS latency is hidden inside the wave: all operand fragments of
+  // a k-step are read at once, and the second k-step's reads are in flight while the
+  // first k-step's MFMAs run.
   auto compute = [&](const char* as, const char* ws) {
     if (!rows_live) return;
+    constexpr int KS = kGemmBKBytes / 64;
+    uint4 af[KS][2], bfr[KS][NB];
 #pragma unroll
-    for (int ks = 0; ks < kGemmBKBytes / 64; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int c = ks * 4 + g4;
-      uint4 af[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(as + swz(wave * 32 + i * 16 + l16, c));
+        af[ks][i] = *reinterpret_cast<const uint4*>(as + swz(wave * 32 + i * 16 + l16, c));
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const uint4 bf = *reinterpret_cast<const uint4*>(ws + swz(j * 16 + l16, c));
-#pragma unroll
-        for (int i = 0; i < 2; ++i) acc[i][j] = mma_kstep(af[i], bf, acc[i][j], T());
-      }
+      for (int j = 0; j < NB; ++j)
+        bfr[ks][j] = *reinterpret_cast<const uint4*>(ws + swz(j * 16 + l16, c));
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep every read ahead of the MFMAs
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][j] = mma_kstep(af[ks][i], bfr[ks][j], acc[i][j], T());
   };
   auto body = [&](char* as, char* ws, char* as2, char* ws2, int i) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPI));
@@ -439,7 +447,9 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
   }
 }
 
-int gemm_tile_n(int N) { return N >= 256 ? 256 : 128; }
+// 128-column tiles: at one unit per CU the split-K partial planes cost more HBM traffic
+// than re-reading the (L2-resident) activation tile for twice as many column tiles.
+int gemm_tile_n(int) { return 128; }
 
 int gemm_host_split(int M, int N, int Kd, int elem_bytes) {
   const int BN = gemm_tile_n(N);
@@ -482,8 +492,7 @@ static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t s
     swiglu_slab_kernel<T><<<slabs, kSlabThreads, 0, st>>>(p, slabs);
     return hipGetLastError();
   }
-  return gemm_tile_n(p.N) == 256 ? launch_gemm_bn<T, EPI, 256>(p, num_cu, st)
-                                 : launch_gemm_bn<T, EPI, 128>(p, num_cu, st);
+  return launch_gemm_bn<T, EPI, 128>(p, num_cu, st);
 }
 
 template <typename T>
