@@ -25,7 +25,7 @@ constexpr int kQRows = 64;  // query rows per workgroup (16 per wave)
 template <typename T, int DH>
 struct AttnTile {
   static constexpr int VE = 16 / sizeof(T);
-  static constexpr int LDK = DH + VE;        // K tile row stride (elements)
+  static constexpr int LDK = DH + 2 * VE;    // K tile row stride (elements, 32 B padding)
   static constexpr int LDV = kKeys + VE;     // transposed V tile row stride
   static constexpr int KSTEPS_QK = DH * (int)sizeof(T) / 64;   // 64-byte k-steps over dh
   static constexpr int KSTEPS_PV = kKeys * (int)sizeof(T) / 64;  // over the 64 keys
@@ -36,24 +36,82 @@ struct AttnState {
   float m, l;
 };
 
-// Stage one tile of up to 64 keys into LDS (rows >= nkeys zero-filled).  key_ptr(j)
-// returns the address of key j's K row, val_ptr(j) its V row.
+// A 64-key K/V tile moves global -> registers -> LDS in two steps, so the next tile's
+// loads can be in flight while the current tile is being attended.
+//   K: thread t holds chunks c = t + 256*u (key c / CPR, 16-byte chunk c % CPR), stored in
+//      natural layout (row stride LDK).
+//   V: thread t holds KQ consecutive keys kq*KQ .. kq*KQ+KQ-1 of one 16-byte chunk db
+//      (kq = t % (64/KQ), db = t / (64/KQ)); it transposes them in registers and writes
+//      each of its VE dh rows of Vt as one KQ-element vector (row stride LDV).
+template <typename T, int DH>
+struct KVRegs {
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int CPR = DH / VE;          // 16-byte chunks per row
+  static constexpr int KC = kKeys * CPR / 256; // K chunks per thread
+  static constexpr int KQ = kKeys * CPR / 256; // V keys per thread
+  uint4 k[KC];
+  uint4 v[KQ];
+};
+
 template <typename T, int DH, typename KF, typename VF>
-__device__ __forceinline__ void stage_kv(T* Ks, T* Vt, int nkeys, KF key_ptr, VF val_ptr) {
-  using A = AttnTile<T, DH>;
-  constexpr int VE = A::VE;
-  constexpr int CPR = DH / VE;                 // 16-byte chunks per row
-  for (int c = threadIdx.x; c < kKeys * CPR; c += blockDim.x) {
-    const int j = c / CPR, cc = c - j * CPR;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (j < nkeys) {
-      kv = ld16(key_ptr(j) + cc * VE);
-      vv = ld16(val_ptr(j) + cc * VE);
-    }
-    *reinterpret_cast<uint4*>(&Ks[j * A::LDK + cc * VE]) = kv;
-    const T* ve = reinterpret_cast<const T*>(&vv);
+__device__ __forceinline__ void load_kv(KVRegs<T, DH>& r, int nkeys, KF key_ptr, VF val_ptr) {
+  using R = KVRegs<T, DH>;
+  const int t = threadIdx.x;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) Vt[(cc * VE + e) * A::LDV + j] = ve[e];
+  for (int u = 0; u < R::KC; ++u) {
+    const int c = t + 256 * u, j = c / R::CPR, cc = c - j * R::CPR;
+    r.k[u] = j < nkeys ? ld16(key_ptr(j) + cc * R::VE) : make_uint4(0, 0, 0, 0);
+  }
+  const int kq = t % (kKeys / R::KQ), db = t / (kKeys / R::KQ);
+#pragma unroll
+  for (int u = 0; u < R::KQ; ++u) {
+    const int j = kq * R::KQ + u;
+    r.v[u] = j < nkeys ? ld16(val_ptr(j) + db * R::VE) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ uint32_t word_at(const uint4& x, int i) {
+  return i == 0 ? x.x : (i == 1 ? x.y : (i == 2 ? x.z : x.w));
+}
+// 16-bit element e (of 8) of x, zero-extended
+__device__ __forceinline__ uint32_t bf16_at(const uint4& x, int e) {
+  return (word_at(x, e >> 1) >> (16 * (e & 1))) & 0xffffu;
+}
+
+template <typename T, int DH>
+__device__ __forceinline__ void store_kv(T* Ks, T* Vt, const KVRegs<T, DH>& r) {
+  using R = KVRegs<T, DH>;
+  using A = AttnTile<T, DH>;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < R::KC; ++u) {
+    const int c = t + 256 * u, j = c / R::CPR, cc = c - j * R::CPR;
+    *reinterpret_cast<uint4*>(&Ks[j * A::LDK + cc * R::VE]) = r.k[u];
+  }
+  const int kq = t % (kKeys / R::KQ), db = t / (kKeys / R::KQ);
+  constexpr int NWORD = R::KQ * (int)sizeof(T) / 4;     // 32-bit words per Vt row piece
+#pragma unroll
+  for (int e = 0; e < R::VE; ++e) {
+    uint32_t w[NWORD];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int u = 0; u < R::KQ; u += 2)
+        w[u / 2] = bf16_at(r.v[u], e) | (bf16_at(r.v[u + 1], e) << 16);
+    } else {
+#pragma unroll
+      for (int u = 0; u < R::KQ; ++u) w[u] = word_at(r.v[u], e);
+    }
+    T* dst = &Vt[(db * R::VE + e) * A::LDV + kq * R::KQ];
+    if constexpr (NWORD == 1) {
+      *reinterpret_cast<uint32_t*>(dst) = w[0];
+    } else if constexpr (NWORD == 2) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NWORD / 4; ++q)
+        reinterpret_cast<uint4*>(dst)[q] =
+            make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+    }
   }
 }
 
@@ -183,15 +241,25 @@ __global__ void __launch_bounds__(256, 2) attn_prefix_kernel(AttnParams p) {
     for (int nt = 0; nt < A::NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int c0 = (int)((long)s * chunks / ns), c1 = (int)((long)(s + 1) * chunks / ns);
+    auto kp = [&](int key0) {
+      return [=](int j) { return pk + (size_t)(key0 + j) * p.stride_tok + (size_t)kvh * p.stride_head; };
+    };
+    auto vp = [&](int key0) {
+      return [=](int j) { return pv + (size_t)(key0 + j) * p.stride_tok + (size_t)kvh * p.stride_head; };
+    };
+    // tile c is staged from registers while tile c + 1 is already being loaded
+    KVRegs<T, DH> kv;
+    if (c0 < c1) load_kv<T, DH>(kv, imin(kKeys, p.P - c0 * kKeys), kp(c0 * kKeys), vp(c0 * kKeys));
     for (int c = c0; c < c1; ++c) {
       const int key0 = c * kKeys;
       const int nkeys = imin(kKeys, p.P - key0);
       __syncthreads();
-      stage_kv<T, DH>(
-          Ks, Vt, nkeys,
-          [&](int j) { return pk + (size_t)(key0 + j) * p.stride_tok + (size_t)kvh * p.stride_head; },
-          [&](int j) { return pv + (size_t)(key0 + j) * p.stride_tok + (size_t)kvh * p.stride_head; });
+      store_kv<T, DH>(Ks, Vt, kv);
       __syncthreads();
+      if (c + 1 < c1) {
+        const int key1 = key0 + kKeys;
+        load_kv<T, DH>(kv, imin(kKeys, p.P - key1), kp(key1), vp(key1));
+      }
       attend_tile<T, DH>(Ks, Vt, nkeys, qf, p.scale_log2, st, o);
     }
     if (valid) {
@@ -237,36 +305,61 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
     const int rr = valid ? r : p.B * g - 1;
     const int i = rr / g, h = kvh * g + (rr - i * g);
     const int k = row_of(n * p.B + i);
+    // branch n's own block rows are the keys; their packed rows come from slot_row
+    auto kp = [&](int key0) {
+      return [=](int j) { return qkv + (size_t)row_of(n * p.B + key0 + j) * p.ld_qkv + koff + (size_t)kvh * DH; };
+    };
+    auto vp = [&](int key0) {
+      return [=](int j) { return qkv + (size_t)row_of(n * p.B + key0 + j) * p.ld_qkv + voff + (size_t)kvh * DH; };
+    };
+    KVRegs<T, DH> kv;
+    load_kv<T, DH>(kv, imin(kKeys, p.B), kp(0), vp(0));
     const T* qp = qkv + (size_t)k * p.ld_qkv + (size_t)h * DH;
     uint4 qf[A::KSTEPS_QK];
 #pragma unroll
     for (int ks = 0; ks < A::KSTEPS_QK; ++ks) qf[ks] = ld16(qp + ks * 4 * VE + g4 * VE);
 
-    // start from the prefix partials of packed row k
+    // start from the prefix partials of packed row k (merged a batch of splits at a time,
+    // so all loads of a batch are in flight together)
     AttnState st{-__builtin_inff(), 0.f};
     f32x4 o[A::NT];
 #pragma unroll
     for (int nt = 0; nt < A::NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (ns > 0) {
-      float M0 = -__builtin_inff();
-      for (int s = 0; s < ns; ++s) M0 = fmaxf(M0, p.part_lse[((size_t)s * K + k) * p.n_q + h]);
-      if (M0 > -__builtin_inff()) {
-        float l = 0.f;
-        for (int s = 0; s < ns; ++s) {
-          const float w = exp2f(p.part_lse[((size_t)s * K + k) * p.n_q + h] - M0);
-          l += w;
-          const float* po = p.part_o + (((size_t)s * K + k) * p.n_q + h) * DH;
+    constexpr int PB = 16 / A::NT;            // 2 (dh 128) or 4 (dh 64) splits per batch
+    for (int s0 = 0; s0 < ns; s0 += PB) {
+      float ls[PB];
+      float4 po[PB][A::NT];
+#pragma unroll
+      for (int b = 0; b < PB; ++b) {
+        const int sb = imin(s0 + b, ns - 1);
+        const size_t prow = ((size_t)sb * K + k) * p.n_q + h;
+        ls[b] = (s0 + b < ns) ? p.part_lse[prow] : -__builtin_inff();
+        const float* pp = p.part_o + prow * DH;
+#pragma unroll
+        for (int nt = 0; nt < A::NT; ++nt)
+          po[b][nt] = *reinterpret_cast<const float4*>(pp + nt * 16 + g4 * 4);
+      }
+      float mb = st.m;
+#pragma unroll
+      for (int b = 0; b < PB; ++b) mb = fmaxf(mb, ls[b]);
+      if (mb > -__builtin_inff()) {
+        const float alpha = exp2f(st.m - mb);
+        st.l *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < A::NT; ++nt) o[nt] *= alpha;
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+          const float w = exp2f(ls[b] - mb);       // 0 for an empty or absent split
+          st.l += w;
 #pragma unroll
           for (int nt = 0; nt < A::NT; ++nt) {
-            const float4 v = *reinterpret_cast<const float4*>(po + nt * 16 + g4 * 4);
-            o[nt][0] += w * v.x;
-            o[nt][1] += w * v.y;
-            o[nt][2] += w * v.z;
-            o[nt][3] += w * v.w;
+            o[nt][0] += w * po[b][nt].x;
+            o[nt][1] += w * po[b][nt].y;
+            o[nt][2] += w * po[b][nt].z;
+            o[nt][3] += w * po[b][nt].w;
           }
         }
-        st.m = M0;
-        st.l = l;
+        st.m = mb;
       }
     }
 
@@ -274,11 +367,12 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
       const int key0 = c * kKeys;
       const int nkeys = imin(kKeys, p.B - key0);
       __syncthreads();
-      stage_kv<T, DH>(
-          Ks, Vt, nkeys,
-          [&](int j) { return qkv + (size_t)row_of(n * p.B + key0 + j) * p.ld_qkv + koff + (size_t)kvh * DH; },
-          [&](int j) { return qkv + (size_t)row_of(n * p.B + key0 + j) * p.ld_qkv + voff + (size_t)kvh * DH; });
+      store_kv<T, DH>(Ks, Vt, kv);
       __syncthreads();
+      if (c + 1 < kchunks) {
+        const int key1 = key0 + kKeys;
+        load_kv<T, DH>(kv, imin(kKeys, p.B - key1), kp(key1), vp(key1));
+      }
       attend_tile<T, DH>(Ks, Vt, nkeys, qf, p.scale_log2, st, o);
     }
     if (valid) {
