@@ -10,10 +10,11 @@ namespace specfold {
 // Gate (SpecFold explainer, paragraph on measuring ||H_child - H_parent|| / ||H_parent||
 // at the layer input).  One wave per slot; fp32 sums of squares; fold iff r <= tau.
 // ratio and recompute are each optional (a caller-given fold state needs ratios only).
-// With `An` the same pass also writes every slot's RMS-normalised row
-// An[slot] = H[slot] / sqrt(mean(H[slot]^2) + eps) * g (the QKV GEMM gathers the packed
-// ones), so the layer input is read once for both.  Loads go four 16-byte chunks per lane
-// at a time so a row costs a couple of memory round trips, not one per chunk.
+// With `An` the same pass also writes the RMS-normalised row
+// An[slot] = H[slot] / sqrt(mean(H[slot]^2) + eps) * g of every slot that computes its own
+// row -- decided here, or marked in `rec_given` -- for the QKV GEMM to gather, so the layer
+// input is read once for both.  Loads go four 16-byte chunks per lane at a time so a row
+// costs a couple of memory round trips, not one per chunk.
 // ------------------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
@@ -21,6 +22,7 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
                                                    int N, int B, int d, float tau,
                                                    float* __restrict__ ratio,
                                                    uint8_t* __restrict__ recompute,
+                                                   const uint8_t* __restrict__ rec_given,
                                                    const T* __restrict__ g, float eps,
                                                    T* __restrict__ An, int ld_an) {
   const int lane = threadIdx.x & 63;
@@ -29,8 +31,9 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
   const int n = slot / B, i = slot - n * B;
   const bool decide = (ratio != nullptr) || (recompute != nullptr);
   int p = -1;
-  if (n > 0 && decide && fold_src) p = fold_src[n];
-  const bool has_parent = (n > 0) && (p >= 0) && (p < n);
+  if (n > 0 && fold_src) p = fold_src[n];
+  const bool fs_ok = (n > 0) && (p >= 0) && (p < n);
+  const bool has_parent = decide && fs_ok;
   const T* c = H + (size_t)slot * d;
   const T* q = has_parent ? H + ((size_t)p * B + i) * d : c;
   constexpr int VE = Pack16<T>::kElems;
@@ -63,47 +66,42 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
       }
     }
   }
-  if (An) {
-    const float rstd = 1.0f / sqrtf(wave_sum(sc) / (float)d + eps);
-    T* o = An + (size_t)slot * ld_an;
-    for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
-      uint4 vc[U], vg[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ch = imin(c0 + 64 * u, chunks - 1);
-        vc[u] = ld16(c + ch * VE);
-        vg[u] = ld16(g + ch * VE);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (c0 + 64 * u >= chunks) break;
-        float fc[VE], fg[VE];
-        unpack16(vc[u], fc, T());
-        unpack16(vg[u], fg, T());
-#pragma unroll
-        for (int e = 0; e < VE; ++e) fc[e] = fc[e] * rstd * fg[e];
-        st16(o + (c0 + 64 * u) * VE, pack16(fc, T()));
-      }
-    }
-  }
-  if (!decide) return;
+  // fold decision (root rows and malformed fold sources always compute their own row)
+  bool rec = true;
   if (has_parent) {
     sd = wave_sum(sd);
     sp = wave_sum(sp);
+    const float num = sqrtf(sd), den = sqrtf(sp);
+    const float r = (den == 0.f) ? (num == 0.f ? 0.f : __builtin_inff()) : num / den;
+    rec = !(r <= tau);
+    if (lane == 0 && ratio) ratio[slot] = r;
+  } else if (lane == 0 && ratio) {
+    ratio[slot] = __builtin_inff();
   }
-  if (lane == 0) {
-    float r;
-    bool rec;
-    if (!has_parent) {
-      r = __builtin_inff();
-      rec = true;
-    } else {
-      const float num = sqrtf(sd), den = sqrtf(sp);
-      r = (den == 0.f) ? (num == 0.f ? 0.f : __builtin_inff()) : num / den;
-      rec = !(r <= tau);
+  if (lane == 0 && recompute) recompute[slot] = rec ? 1 : 0;
+  if (!An) return;
+  const bool own = rec_given ? (n == 0 || !fs_ok || rec_given[slot] != 0) : rec;
+  if (!own) return;                          // folded: the QKV GEMM never reads this row
+  const float rstd = 1.0f / sqrtf(wave_sum(sc) / (float)d + eps);
+  T* o = An + (size_t)slot * ld_an;
+  for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
+    uint4 vc[U], vg[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ch = imin(c0 + 64 * u, chunks - 1);
+      vc[u] = ld16(c + ch * VE);
+      vg[u] = ld16(g + ch * VE);
     }
-    if (ratio) ratio[slot] = r;
-    if (recompute) recompute[slot] = rec ? 1 : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + 64 * u >= chunks) break;
+      float fc[VE], fg[VE];
+      unpack16(vc[u], fc, T());
+      unpack16(vg[u], fg, T());
+#pragma unroll
+      for (int e = 0; e < VE; ++e) fc[e] = fc[e] * rstd * fg[e];
+      st16(o + (c0 + 64 * u) * VE, pack16(fc, T()));
+    }
   }
 }
 
@@ -311,11 +309,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ h,
 // ------------------------------------------------------------------------------------
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
-                       float* ratio, uint8_t* recompute, const void* g, float eps,
-                       void* An, int ld_an, hipStream_t st) {
+                       float* ratio, uint8_t* recompute, const uint8_t* rec_given,
+                       const void* g, float eps, void* An, int ld_an, hipStream_t st) {
   const int S = N * B;
   gate_kernel<T><<<ceil_div(S, 4), 256, 0, st>>>((const T*)H, fold_src, N, B, d, tau, ratio,
-                                                 recompute, (const T*)g, eps, (T*)An, ld_an);
+                                                 recompute, rec_given, (const T*)g, eps,
+                                                 (T*)An, ld_an);
   return hipGetLastError();
 }
 
@@ -367,9 +366,11 @@ template hipError_t launch_oproj_finish<bf16>(const float*, int, const void*, vo
                                               const void*, float, void*, int, hipStream_t);
 
 template hipError_t launch_gate<float>(const void*, const int32_t*, int, int, int, float, float*,
-                                       uint8_t*, const void*, float, void*, int, hipStream_t);
+                                       uint8_t*, const uint8_t*, const void*, float, void*, int,
+                                       hipStream_t);
 template hipError_t launch_gate<bf16>(const void*, const int32_t*, int, int, int, float, float*,
-                                      uint8_t*, const void*, float, void*, int, hipStream_t);
+                                      uint8_t*, const uint8_t*, const void*, float, void*, int,
+                                      hipStream_t);
 template hipError_t launch_combine<float>(const void*, const void*, const int32_t*, const int32_t*,
                                           int, int, int, void*, hipStream_t);
 template hipError_t launch_combine<bf16>(const void*, const void*, const int32_t*, const int32_t*,

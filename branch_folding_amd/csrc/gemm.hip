@@ -18,7 +18,8 @@
 //     distinct bank groups;
 //   * M (the packed row count) is known only on the device, so the kernel is persistent: a
 //     fixed grid reads M, derives the tile count and a split-K factor, and walks the work
-//     units, XCD-major so the M tiles of one weight tile share an XCD's L2.
+//     units XCD-major, numbered so that an XCD's units share K-slices of the activation
+//     operand and weight column tiles in its L2.
 // Split-K partial sums (fp32) are reduced by a separate kernel in split order, so results
 // are deterministic and no device-scope fences are needed.
 // Wave tile 64 x 64 (4 x 4 MFMA 16x16 tiles); a k-iteration is 128 bytes of K.
@@ -97,8 +98,11 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
   for (int u = blockIdx.x; u < per_xcd * 8; u += gridDim.x) {
     const int v = (u & 7) * per_xcd + (u >> 3);       // XCD u%8 owns a contiguous range
     if (v >= units) continue;
-    const int tile = v / split, s = v - tile * split;
-    const int mt = tile % mb, ntile = tile / mb;
+    // K-slice slowest, row tile fastest: an XCD's range covers one or two K-slices, so it
+    // pulls only those slices of the shared activation operand into its L2, and the row
+    // tiles that share a weight column tile run side by side
+    const int mt = v % mb, rest = v / mb;
+    const int ntile = rest % nt, s = rest / nt;
     const int m0 = mt * kGemmBM, n0 = ntile * BN;
     const int kb = (int)((long)s * kiters / split), ke = (int)((long)(s + 1) * kiters / split);
 

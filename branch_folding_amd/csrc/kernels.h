@@ -12,12 +12,13 @@ namespace specfold {
 constexpr int kResolve = 1;
 constexpr int kPack = 2;
 
-// Gate: writes ratio[slot] and recompute[slot] where those pointers are non-null, and
-// with An every slot's normalised row An[slot] = H[slot] * rstd * g (row stride ld_an).
+// Gate: writes ratio[slot] and recompute[slot] where those pointers are non-null, and with
+// An the normalised row An[slot] = H[slot] * rstd * g (row stride ld_an) of every slot that
+// computes its own row (as decided here, or as rec_given marks when it is non-null).
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
-                       float* ratio, uint8_t* recompute, const void* g, float eps, void* An,
-                       int ld_an, hipStream_t st);
+                       float* ratio, uint8_t* recompute, const uint8_t* rec_given,
+                       const void* g, float eps, void* An, int ld_an, hipStream_t st);
 size_t resolve_pack_lds_bytes(int S);
 hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,
                                const int32_t* src_in, int N, int B, int mode, int32_t* src_out,

@@ -173,14 +173,14 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
     void* ev = begin ? probe->start : probe->stop;
     return ev ? hipEventRecord((hipEvent_t)ev, st) : hipSuccess;
   };
-  // The gate pass also writes every slot's RMS-normalised row (QKV input) into A1, which
-  // shares its buffer with the FFN input A2 (written only after the QKV GEMM has consumed
-  // A1).  With a given fold state it writes no mask, and ratios only into a caller's
-  // ratio buffer.
+  // The gate pass also writes the RMS-normalised rows (QKV input) of the slots that compute
+  // their own row into A1, which shares its buffer with the FFN input A2 (written only after
+  // the QKV GEMM has consumed A1).  With a given fold state it writes no mask, and ratios
+  // only into a caller's ratio buffer.
   void* A2 = ws + L.a2;
   HIP_CHECK(mark(SPECFOLD_STEP_GATE, true));
-  HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, state_in ? nullptr : rec, w->rms1,
-                           s->rms_eps, A2, (int)L.ld_d, st));
+  HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, state_in ? nullptr : rec,
+                           state_in ? rec : nullptr, w->rms1, s->rms_eps, A2, (int)L.ld_d, st));
   HIP_CHECK(mark(SPECFOLD_STEP_GATE, false));
   if (!state_in) {
     HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, true));
@@ -367,10 +367,10 @@ specfold_status specfold_gate(const specfold_shape* shape, const void* hidden,
   (void)hipGetLastError();   // do not report an earlier, unrelated failure
   if (sh->dtype == SPECFOLD_BF16) {
     HIP_CHECK(launch_gate<bf16>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
-                                ratio, recompute, nullptr, 0.f, nullptr, 0, s));
+                                ratio, recompute, nullptr, nullptr, 0.f, nullptr, 0, s));
   } else {
     HIP_CHECK(launch_gate<float>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
-                                 ratio, recompute, nullptr, 0.f, nullptr, 0, s));
+                                 ratio, recompute, nullptr, nullptr, 0.f, nullptr, 0, s));
   }
   return ok();
 }
