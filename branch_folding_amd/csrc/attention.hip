@@ -6,9 +6,10 @@
 //   (lse, normalised output) over a range of prefix keys.  The prefix is read through the
 //   caller's strided view once per (KV head, 64-query tile) -- never copied per branch --
 //   and all g query heads of a KV head share every K/V tile.
+// Split merge: the prefix partials of each (packed row, head) are merged once.
 // Block phase: for every slot (n, i) and head h, the query of its packed row slot_row[n,i]
 //   attends to branch n's own block keys/values (rows slot_row[n, j]); the running state
-//   starts from the prefix partials of that packed row, which is the correction step.
+//   starts from the merged prefix partial of that packed row, which is the correction step.
 //
 // MFMA formulation: scores are computed transposed, S^T = K Q^T (keys as the A operand from
 // LDS, queries as the B operand in registers), so every lane ends up holding one query's
@@ -277,6 +278,66 @@ __global__ void __launch_bounds__(256, 2) attn_prefix_kernel(AttnParams p) {
 }
 
 // ------------------------------------------------------------------------------------
+// Merge of the prefix splits: plane 0 of (lse, o) becomes the merge of all ns planes, once
+// per (packed row, query head) instead of once per slot that reads it.  One wave per
+// (k, h); every lane loads before any lane stores, so the merge runs in place.
+// ------------------------------------------------------------------------------------
+template <int DH>
+__device__ __forceinline__ void merge_row(const AttnParams& p, int K, int ns, int row, int lane) {
+  constexpr int E = DH / 64;                  // output elements per lane
+  const size_t plane_l = (size_t)K * p.n_q;
+  constexpr int SB = 8;                      // splits per batch of loads
+  float m = -__builtin_inff();
+  for (int s0 = 0; s0 < ns; s0 += SB) {
+    float ls[SB];
+#pragma unroll
+    for (int b = 0; b < SB; ++b)
+      ls[b] = (s0 + b < ns) ? p.part_lse[(size_t)(s0 + b) * plane_l + row] : -__builtin_inff();
+#pragma unroll
+    for (int b = 0; b < SB; ++b) m = fmaxf(m, ls[b]);
+  }
+  float l = 0.f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  if (m > -__builtin_inff()) {
+    for (int s0 = 0; s0 < ns; s0 += SB) {
+      float ls[SB], v[SB][E];
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int sb = imin(s0 + b, ns - 1);
+        ls[b] = (s0 + b < ns) ? p.part_lse[(size_t)sb * plane_l + row] : -__builtin_inff();
+        const float* po = p.part_o + ((size_t)sb * plane_l + row) * DH + lane * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[b][e] = po[e];
+      }
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const float w = exp2f(ls[b] - m);       // 0 for an absent or empty split
+        l += w;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += w * v[b][e];
+      }
+    }
+  }
+  float* po = p.part_o + (size_t)row * DH + lane * E;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) po[e] = acc[e] * inv;
+  if (lane == 0) p.part_lse[row] = l > 0.f ? m + log2f(l) : -__builtin_inff();
+}
+
+template <int DH>
+__global__ void __launch_bounds__(256) attn_merge_kernel(AttnParams p) {
+  const int K = imin(*p.count, p.cap);
+  const int g = p.n_q / p.n_kv;
+  if (!attn_merge_on(K, g, p.n_kv, p.P, p.S)) return;
+  const int ns = attn_splits(K, g, p.n_kv, p.P);
+  const int lane = threadIdx.x & 63;
+  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < K * p.n_q; row += gridDim.x * 4)
+    merge_row<DH>(p, K, ns, row, lane);
+}
+
+// ------------------------------------------------------------------------------------
 // Block phase + merge.
 // ------------------------------------------------------------------------------------
 template <typename T, int DH>
@@ -288,7 +349,8 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
   const int K = imin(*p.count, p.cap);
   if (K <= 0) return;
   const int g = p.n_q / p.n_kv;
-  const int ns = attn_splits(K, g, p.n_kv, p.P);
+  // plane 0 holds all prefix splits when attn_merge_kernel merged them
+  const int ns = attn_merge_on(K, g, p.n_kv, p.P, p.S) ? 1 : attn_splits(K, g, p.n_kv, p.P);
   const int qtiles = ceil_div(p.B * g, kQRows);
   const int units = p.N * p.n_kv * qtiles;
   const int kchunks = ceil_div(p.B, kKeys);
@@ -399,9 +461,17 @@ template <typename T>
 hipError_t launch_attn_prefix(const AttnParams& p, int num_cu, hipStream_t st) {
   if (p.P <= 0) return hipSuccess;
   const int grid = 2 * num_cu;
-  if (p.dh == 128) attn_prefix_kernel<T, 128><<<grid, 256, 0, st>>>(p);
-  else if (p.dh == 64) attn_prefix_kernel<T, 64><<<grid, 256, 0, st>>>(p);
-  else return hipErrorInvalidValue;
+  const int mrows = ceil_div(p.cap * p.n_q, 4);
+  const int mgrid = mrows < num_cu ? mrows : num_cu;   // persistent
+  if (p.dh == 128) {
+    attn_prefix_kernel<T, 128><<<grid, 256, 0, st>>>(p);
+    attn_merge_kernel<128><<<mgrid, 256, 0, st>>>(p);
+  } else if (p.dh == 64) {
+    attn_prefix_kernel<T, 64><<<grid, 256, 0, st>>>(p);
+    attn_merge_kernel<64><<<mgrid, 256, 0, st>>>(p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

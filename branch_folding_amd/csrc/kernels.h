@@ -134,6 +134,12 @@ __host__ __device__ inline int attn_splits(int K, int g, int n_kv, int P) {
   if (s > kAttnMaxSplit) s = kAttnMaxSplit;
   return s;
 }
+// Whether the prefix splits are merged once per (packed row, head) before the block phase:
+// worth a pass when the slots' re-reads it saves, S * (ns - 1), dwarf its own K * (ns + 1).
+__host__ __device__ inline bool attn_merge_on(int K, int g, int n_kv, int P, int S) {
+  const int ns = attn_splits(K, g, n_kv, P);
+  return ns >= 2 && (long)S * (ns - 1) >= 8L * K * (ns + 1);
+}
 // largest nsplit * K over K in [1, S] (rows of partial storage)
 size_t attn_partial_rows(int S, int g, int n_kv, int P);
 
