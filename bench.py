@@ -218,7 +218,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 4],
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4],
                     help="configuration id (1 = the 7B-shaped headline layer)")
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
