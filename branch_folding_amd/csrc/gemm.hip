@@ -248,18 +248,23 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
 // same direct-to-LDS three-stage ring as gemm_kernel, templated on P so that the per-wave
 // load count (and with it the s_waitcnt immediate) is a compile-time constant.
 // ---------------------------------------------------------------------------------------
-constexpr int kSlabMaxPairs = 6;
+constexpr int kSlabMaxPairs = 5;
 constexpr int kSlabThreads = 256;
 
-template <typename T, int P>
+// One slab unit over R row tiles (R = 1 or 2) of 128 rows starting at m0.  With R = 2 each
+// weight chunk is loaded once for both row tiles (the slab is streamed once for up to 256
+// packed rows); stage s then holds {As_s, Bs_s, Ws_s} instead of {As_s, Ws_s}.
+template <typename T, int P, int R>
 __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, int pair0,
-                                          char* As0, char* As1, char* As2, char* Ws0,
-                                          char* Ws1, char* Ws2) {
+                                          char* As0, char* As1, char* As2, char* Bs0,
+                                          char* Bs1, char* Bs2, char* Ws0, char* Ws1,
+                                          char* Ws2) {
   using G = GemmTile<T>;
+  static_assert(R == 1 || R == 2, "one or two row tiles per pass");
   constexpr int NB = 2 * P;                  // 16-column blocks: gate_0, up_0, gate_1, ...
-  constexpr int AQ = kGemmBM * kGemmBKBytes / 1024 / 4;   // A loads per wave (4)
+  constexpr int AQ = kGemmBM * kGemmBKBytes / 1024 / 4;   // A loads per wave per row tile (4)
   constexpr int WQ = NB * 16 * kGemmBKBytes / 1024 / 4;   // W loads per wave (P)
-  constexpr int LPI = AQ + WQ;
+  constexpr int LPI = R * AQ + WQ;
   const int kiters = p.Kd / G::BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -267,14 +272,16 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
   const char* Ab = (const char*)p.A;
   const char* Wb = (const char*)p.W;
 
-  const char* a_src[AQ];
+  const char* a_src[R][AQ];
   const char* w_src[WQ];
 #pragma unroll
-  for (int q = 0; q < AQ; ++q) {
-    const int r = (wave * AQ + q) * 8 + lr;
-    const int c = lpc ^ ((r >> 1) & 7);
-    a_src[q] = Ab + (size_t)imin(m0 + r, M - 1) * p.lda * sizeof(T) + c * 16;
-  }
+  for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int r = (wave * AQ + q) * 8 + lr;
+      const int c = lpc ^ ((r >> 1) & 7);
+      a_src[rt][q] = Ab + (size_t)imin(m0 + rt * kGemmBM + r, M - 1) * p.lda * sizeof(T) + c * 16;
+    }
 #pragma unroll
   for (int q = 0; q < WQ; ++q) {
     const int r = (wave * WQ + q) * 8 + lr;           // stage row: block r/16, row r%16
@@ -284,109 +291,138 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
     const int wr = (b & 1) ? p.ff + j : j;
     w_src[q] = Wb + (size_t)wr * p.ldw * sizeof(T) + c * 16;
   }
-  auto issue = [&](char* as, char* ws, int it) {
+  // loads of k-iteration `it` into a stage: W, then the A tile(s)
+  auto issue = [&](char* a0, char* a1, char* ws, int it) {
     const size_t off = (size_t)imin(it, kiters - 1) * kGemmBKBytes;
 #pragma unroll
     for (int q = 0; q < WQ; ++q)
       __builtin_amdgcn_global_load_lds((glb_void_t*)(w_src[q] + off),
                                        (lds_void_t*)(ws + (wave * WQ + q) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int q = 0; q < AQ; ++q)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[q] + off),
-                                       (lds_void_t*)(as + (wave * AQ + q) * 1024), 16, 0, 0);
+    for (int rt = 0; rt < R; ++rt) {
+      char* as = rt == 0 ? a0 : a1;
+#pragma unroll
+      for (int q = 0; q < AQ; ++q)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[rt][q] + off),
+                                         (lds_void_t*)(as + (wave * AQ + q) * 1024), 16, 0, 0);
+    }
   };
 
-  f32x4 acc[2][NB];
+  f32x4 acc[R][2][NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool rows_live = (m0 + wave * 32) < M;
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[rt][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool live[R];
+#pragma unroll
+  for (int rt = 0; rt < R; ++rt) live[rt] = (m0 + rt * kGemmBM + wave * 32) < M;
   // One wave per SIMD, so LDS latency is hidden inside the wave: all operand fragments of
-  // a k-step are read at once, and the second k-step's reads are in flight while the
-  // first k-step's MFMAs run.
-  auto compute = [&](const char* as, const char* ws) {
-    if (!rows_live) return;
+  // a k-iteration are read at once, then its MFMAs run (the weight fragments serve every
+  // row tile).
+  auto compute = [&](const char* a0, const char* a1, const char* ws) {
+    if (!live[0]) return;
     constexpr int KS = kGemmBKBytes / 64;
-    uint4 af[KS][2], bfr[KS][NB];
+    uint4 af[R][KS][2], bfr[KS][NB];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = ks * 4 + g4;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[ks][i] = *reinterpret_cast<const uint4*>(as + swz(wave * 32 + i * 16 + l16, c));
+      for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          af[rt][ks][i] = *reinterpret_cast<const uint4*>((rt == 0 ? a0 : a1) +
+                                                          swz(wave * 32 + i * 16 + l16, c));
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         bfr[ks][j] = *reinterpret_cast<const uint4*>(ws + swz(j * 16 + l16, c));
     }
     __builtin_amdgcn_sched_barrier(0);   // keep every read ahead of the MFMAs
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int rt = 0; rt < R; ++rt) {
+      if (rt > 0 && !live[rt]) break;
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) acc[i][j] = mma_kstep(af[ks][i], bfr[ks][j], acc[i][j], T());
-  };
-  auto body = [&](char* as, char* ws, char* as2, char* ws2, int i) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPI));
-    __builtin_amdgcn_s_barrier();
-    issue(as2, ws2, i + 2);
-    if (i < kiters) compute(as, ws);
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[rt][i][j] = mma_kstep(af[rt][ks][i], bfr[ks][j], acc[rt][i][j], T());
+    }
   };
 
+  // three stages, two k-iterations in flight: once this wave's loads of i have landed
+  // (only the LPI loads of i + 1 may still be pending) and every wave has passed the
+  // barrier, the loads of i + 2 go into the stage freed by i - 1
+  auto body = [&](char* a0, char* a1, char* ws, char* n0, char* n1, char* nw, int i) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPI));
+    __builtin_amdgcn_s_barrier();
+    issue(n0, n1, nw, i + 2);
+    if (i < kiters) compute(a0, a1, ws);
+  };
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __builtin_amdgcn_s_barrier();
-  issue(As0, Ws0, 0);
-  issue(As1, Ws1, 1);
+  issue(As0, Bs0, Ws0, 0);
+  issue(As1, Bs1, Ws1, 1);
   for (int it = 0; it < kiters; it += kGemmStages) {
-    body(As0, Ws0, As2, Ws2, it);
-    body(As1, Ws1, As0, Ws0, it + 1);
-    body(As2, Ws2, As1, Ws1, it + 2);
+    body(As0, Bs0, Ws0, As2, Bs2, Ws2, it);
+    body(As1, Bs1, Ws1, As0, Bs0, Ws0, it + 1);
+    body(As2, Bs2, Ws2, As1, Bs1, Ws1, it + 2);
   }
 
   // epilogue: lane holds rows g4*4 + r of each 16-row block and column l16 of each block
   T* C = (T*)p.C;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-    for (int pr = 0; pr < P; ++pr) {
-      const int col = (pair0 + pr) * 16 + l16;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wave * 32 + i * 16 + g4 * 4 + r;
-        if (row < M) {
-          const float gv = acc[i][2 * pr][r], uv = acc[i][2 * pr + 1][r];
-          C[(size_t)row * p.ldc + col] = from_f32<T>(silu_f(gv) * uv);
+      for (int pr = 0; pr < P; ++pr) {
+        const int col = (pair0 + pr) * 16 + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + rt * kGemmBM + wave * 32 + i * 16 + g4 * 4 + r;
+          if (row < M) {
+            const float gv = acc[rt][i][2 * pr][r], uv = acc[rt][i][2 * pr + 1][r];
+            C[(size_t)row * p.ldc + col] = from_f32<T>(silu_f(gv) * uv);
+          }
         }
       }
-    }
 }
 
 template <typename T>
 __global__ void __launch_bounds__(kSlabThreads) swiglu_slab_kernel(GemmParams p, int slabs) {
   constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
   constexpr int W_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
+  // three stages of {A tile 0, A tile 1, W}: 3 x (16 + 16 + 20) KB = 156 KB
   __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Bs0[A_BYTES], Bs1[A_BYTES], Bs2[A_BYTES];
   __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
   const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
   if (M <= 0) return;
   const int pairs = p.ff / 16;
   const int base = pairs / slabs, rem = pairs - base * slabs;
   const int mb = ceil_div(M, kGemmBM);
-  for (int u = blockIdx.x; u < mb * slabs; u += gridDim.x) {
-    const int mt = u / slabs, sl = u - mt * slabs;
+  // more than one row tile: pairs of row tiles share every weight chunk
+  const int R = mb > 1 ? 2 : 1;
+  const int groups = ceil_div(mb, R);
+  for (int u = blockIdx.x; u < groups * slabs; u += gridDim.x) {
+    const int mg = u / slabs, sl = u - mg * slabs;
     const int np = base + (sl < rem ? 1 : 0);
     const int pair0 = sl * base + imin(sl, rem);
-    const int m0 = mt * kGemmBM;
+    const int m0 = mg * R * kGemmBM;
+#define SLAB_CASE(PP)                                                                        \
+  case PP:                                                                                   \
+    if (R == 1) slab_unit<T, PP, 1>(p, M, m0, pair0, As0, As1, As2, Bs0, Bs1, Bs2, Ws0, Ws1,  \
+                                    Ws2);                                                    \
+    else slab_unit<T, PP, 2>(p, M, m0, pair0, As0, As1, As2, Bs0, Bs1, Bs2, Ws0, Ws1, Ws2);  \
+    break;
     switch (np) {
-      case 1: slab_unit<T, 1>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
-      case 2: slab_unit<T, 2>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
-      case 3: slab_unit<T, 3>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
-      case 4: slab_unit<T, 4>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
-      case 5: slab_unit<T, 5>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
-      case 6: slab_unit<T, 6>(p, M, m0, pair0, As0, As1, As2, Ws0, Ws1, Ws2); break;
+      SLAB_CASE(1) SLAB_CASE(2) SLAB_CASE(3) SLAB_CASE(4) SLAB_CASE(5)
       default: break;          // the host never makes slabs wider than kSlabMaxPairs
     }
+#undef SLAB_CASE
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
