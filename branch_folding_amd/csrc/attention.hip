@@ -23,6 +23,14 @@ namespace specfold {
 constexpr int kKeys = 64;   // keys per LDS tile
 constexpr int kQRows = 64;  // query rows per workgroup (16 per wave)
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+// s_waitcnt immediates: at most n vector-memory operations pending (vmcnt split over bits
+// 3:0 and 15:14; expcnt and lgkmcnt not waited for), and the same with every LDS
+// operation of the wave returned
+constexpr int tr_waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int tr_waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
 template <typename T, int DH>
 struct AttnTile {
   static constexpr int VE = 16 / sizeof(T);
@@ -116,6 +124,52 @@ __device__ __forceinline__ void store_kv(T* Ks, T* Vt, const KVRegs<T, DH>& r) {
   }
 }
 
+// Raw v_exp_f32: 2^x for the softmax weights.  Its arguments are <= 0 here; results below
+// the normal range flush towards 0, which only drops weights under 2^-126 of the maximum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online-softmax update of one 64-key tile for the lane's query: sc[t][r] holds the raw
+// score of key t*16 + (lane/16)*4 + r and becomes its unnormalised weight
+// 2^(score * scale_log2 - m).  Keys >= nkeys (a ragged last tile) get weight 0.  The
+// running output is rescaled only when some lane's running maximum moved.
+template <int NT>
+__device__ __forceinline__ void softmax_tile(f32x4 (&sc)[4], int nkeys, float scale_log2,
+                                             AttnState& st, f32x4 (&o)[NT]) {
+  if (nkeys < kKeys) {   // uniform branch, ragged tiles only
+    // key t*16 + g4*4 + r is past the end iff t*16 + r >= nkeys - g4*4
+    const int th = nkeys - ((threadIdx.x & 63) >> 4) * 4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (t * 16 + r >= th) sc[t][r] = -__builtin_inff();
+  }
+  float mloc = sc[0][0];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[t][r]);
+  mloc = group4_max(mloc);
+  const float m_new = fmaxf(st.m, mloc * scale_log2);   // scale_log2 > 0
+  const float alpha = fast_exp2(st.m - m_new);           // st.m = -inf -> 0
+  float lsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pv = fast_exp2(fmaf(sc[t][r], scale_log2, -m_new));
+      sc[t][r] = pv;
+      lsum += pv;
+    }
+  lsum = group4_sum(lsum);
+  st.l = st.l * alpha + lsum;
+  st.m = m_new;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+  }
+}
+
 // Process one staged key tile for the wave's 16 queries.
 template <typename T, int DH>
 __device__ __forceinline__ void attend_tile(const T* Ks, const T* Vt, int nkeys,
@@ -137,34 +191,7 @@ __device__ __forceinline__ void attend_tile(const T* Ks, const T* Vt, int nkeys,
       sc[t] = mma_kstep(kf, qf[ks], sc[t], T());
     }
   }
-  float mloc = -__builtin_inff();
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = t * 16 + g4 * 4 + r;
-      float v = sc[t][r] * scale_log2;
-      if (key >= nkeys) v = -__builtin_inff();
-      sc[t][r] = v;
-      mloc = fmaxf(mloc, v);
-    }
-  mloc = group4_max(mloc);
-  const float m_new = fmaxf(st.m, mloc);
-  const float alpha = exp2f(st.m - m_new);     // st.m = -inf -> 0
-  float lsum = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float pv = exp2f(sc[t][r] - m_new);
-      sc[t][r] = pv;
-      lsum += pv;
-    }
-  lsum = group4_sum(lsum);
-  st.l = st.l * alpha + lsum;
-  st.m = m_new;
-#pragma unroll
-  for (int nt = 0; nt < A::NT; ++nt) o[nt] *= alpha;
+  softmax_tile<A::NT>(sc, nkeys, scale_log2, st, o);
 
   // O^T[n][q] += sum_keys Vt[n][key] * P[q][key]
 #pragma unroll
@@ -206,6 +233,8 @@ __device__ __forceinline__ void attend_tile(const T* Ks, const T* Vt, int nkeys,
 // ------------------------------------------------------------------------------------
 // Prefix phase.
 // ------------------------------------------------------------------------------------
+// fp32 and short bf16 prefixes: 64-query units, K/V tiles staged through registers (V
+// transposed on the way into LDS), two workgroups per CU.
 template <typename T, int DH>
 __global__ void __launch_bounds__(256, 2) attn_prefix_kernel(AttnParams p) {
   using A = AttnTile<T, DH>;
@@ -214,7 +243,7 @@ __global__ void __launch_bounds__(256, 2) attn_prefix_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) T Vt[DH * A::LDV];
   const int K = imin(*p.count, p.cap);
   const int g = p.n_q / p.n_kv;
-  const int ns = attn_splits(K, g, p.n_kv, p.P);
+  const int ns = attn_splits(K, g, p.n_kv, p.P, DH, (int)sizeof(T));
   if (ns == 0) return;
   const int qtiles = ceil_div(K * g, kQRows);
   const int units = p.n_kv * qtiles * ns;
@@ -278,45 +307,322 @@ __global__ void __launch_bounds__(256, 2) attn_prefix_kernel(AttnParams p) {
 }
 
 // ------------------------------------------------------------------------------------
+// Prefix phase, bf16.  A unit is 256 query rows (8 waves x 2 blocks of 16) of one KV head
+// against one key range, so every K/V tile staged in LDS serves 256 queries:
+//   * K and V tiles go global -> LDS with direct-to-LDS loads into a ring of four stages
+//     (separate arrays, so the compiler sees that loads into one stage never alias reads
+//     of another), three tiles in flight while one is attended; one s_waitcnt + s_barrier
+//     per tile;
+//   * V stays in its natural [key][dh] layout: the V^T operand of O^T = V^T P^T is read
+//     with ds_read_b64_tr_b16, which hands lane 4a+b of each 16-lane group element b of
+//     the 8-byte rows that lanes a, a+4, a+8 and a+12 point at, i.e. four consecutive keys
+//     of one dh column when the 16 lanes point at 4 keys x 4 column quads;
+//   * every K fragment and V fragment read from LDS feeds the MFMAs of both query blocks.
+// LDS rows are XOR-swizzled in 16-byte chunks (the loads pick their global chunk to
+// match): the K fragment reads (16 rows at one chunk) and the transposed V reads (8 rows
+// x 32 bytes per half wave) each touch distinct banks.
+// ------------------------------------------------------------------------------------
+constexpr int kTrWaves = 8;
+constexpr int kTrQRows = kTrWaves * 32;   // query rows per unit
+constexpr int kTrStages = 4;
+
+template <int DH>
+struct TrTile {
+  static constexpr int ROWB = DH * 2;                   // bytes per K (or V) row
+  static constexpr int TILEB = kKeys * ROWB;            // bytes per K (or V) tile
+  static constexpr int RP = 256 / ROWB;                 // rows per 256 bytes (1 or 2)
+  static constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
+  static constexpr int QI = TILEB / 1024 / kTrWaves;    // K (and V) loads per wave per tile
+  static constexpr int LPI = 2 * QI;                    // vector-memory ops per wave per tile
+  static constexpr int KSQ = DH / 32;                   // 64-byte k-steps over dh
+  static constexpr int NT = DH / 16;                    // 16-wide dh tiles of the output
+  static_assert(QI >= 1 && TILEB % (1024 * kTrWaves) == 0, "tile/loader mismatch");
+};
+// physical 16-byte chunk = logical chunk ^ swizzle(row)
+template <int DH>
+__device__ __forceinline__ int tr_kswz(int r) {
+  return (r / TrTile<DH>::RP) & (TrTile<DH>::CPR - 1);
+}
+template <int DH>
+__device__ __forceinline__ int tr_vswz(int r) {
+  return 2 * ((r / TrTile<DH>::RP) & (8 / TrTile<DH>::RP - 1));
+}
+
+// Direct-to-LDS 16-byte load (global_load_lds_dwordx4: lane i writes LDS bytes
+// [lds_base + 16 i, lds_base + 16 i + 16); lds_base must be wave-uniform).  Issued from
+// inline asm so that the compiler's wait-count pass does not see an LDS write: the
+// transposed V reads below carry no alias information, and against a tracked LDS DMA the
+// pass would drain every load in flight before each of them.  The kernel orders these
+// loads itself (s_waitcnt vmcnt + s_barrier before a stage is read); M0 is restored.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[b]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[g], off\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [g] "v"(g), [b] "s"(lds_base)
+      : "memory");
+}
+
+typedef short tr_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tr_v4s lds_tr_v4s;
+
+template <int DH>
+__device__ __forceinline__ void tr_attend(const char* Ks, const char* Vs, int nkeys,
+                                          const uint4 (&qf)[2][TrTile<DH>::KSQ],
+                                          const int (&kofs)[TrTile<DH>::KSQ],
+                                          const int (&vofs)[TrTile<DH>::NT], float scale_log2,
+                                          AttnState (&st)[2], f32x4 (&o)[2][TrTile<DH>::NT]) {
+  using Tt = TrTile<DH>;
+  // S^T = K Q^T: sc[b][t][r] = key t*16 + g4*4 + r, query l16 of block b
+  f32x4 sc[2][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    sc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < Tt::KSQ; ++ks) {
+      const uint4 kf = *reinterpret_cast<const uint4*>(Ks + kofs[ks] + t * 16 * Tt::ROWB);
+      sc[0][t] = mma_kstep(kf, qf[0][ks], sc[0][t], bf16());
+      sc[1][t] = mma_kstep(kf, qf[1][ks], sc[1][t], bf16());
+    }
+  }
+  softmax_tile<Tt::NT>(sc[0], nkeys, scale_log2, st[0], o[0]);
+  softmax_tile<Tt::NT>(sc[1], nkeys, scale_log2, st[1], o[1]);
+  // P^T as the B operand: k-step mu covers keys 32mu + 4*g4 + 0..3 and 32mu + 16 + 4*g4 + 0..3
+  uint4 pb[2][2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int mu = 0; mu < 2; ++mu) {
+      float pf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = sc[b][2 * mu][e];
+        pf[4 + e] = sc[b][2 * mu + 1][e];
+      }
+      pb[b][mu] = pack16(pf, bf16());
+    }
+  // O^T += V^T P^T with V^T fragments read transposed from the natural V tile: the same
+  // two key quads per lane group as the P^T operand above
+#pragma unroll
+  for (int mu = 0; mu < 2; ++mu)
+#pragma unroll
+    for (int nt = 0; nt < Tt::NT; ++nt) {
+      const tr_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_tr_v4s*)(Vs + vofs[nt] + 32 * mu * Tt::ROWB));
+      const tr_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_tr_v4s*)(Vs + vofs[nt] + (32 * mu + 16) * Tt::ROWB));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      const uint4 vf = make_uint4(l2.x, l2.y, h2.x, h2.y);
+      o[0][nt] = mma_kstep(vf, pb[0][mu], o[0][nt], bf16());
+      o[1][nt] = mma_kstep(vf, pb[1][mu], o[1][nt], bf16());
+    }
+}
+
+template <int DH>
+__global__ void __launch_bounds__(kTrWaves * 64, 1) attn_prefix_tr_kernel(AttnParams p) {
+  using Tt = TrTile<DH>;
+  constexpr int QI = Tt::QI, LPI = Tt::LPI, KSQ = Tt::KSQ, NT = Tt::NT;
+  __shared__ __attribute__((aligned(1024))) char K0[Tt::TILEB], K1[Tt::TILEB], K2[Tt::TILEB],
+      K3[Tt::TILEB];
+  __shared__ __attribute__((aligned(1024))) char V0[Tt::TILEB], V1[Tt::TILEB], V2[Tt::TILEB],
+      V3[Tt::TILEB];
+  const int K = imin(*p.count, p.cap);
+  const int g = p.n_q / p.n_kv;
+  const int ns = attn_splits(K, g, p.n_kv, p.P, DH, 2);
+  if (ns == 0) return;
+  const int rows = K * g;
+  const int qtiles = ceil_div(rows, kTrQRows);
+  const int units = p.n_kv * qtiles * ns;
+  const int chunks = ceil_div(p.P, kKeys);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g4 = lane >> 4, l16 = lane & 15;
+  const char* qkv = (const char*)p.qkv;
+  const long st_tok = p.stride_tok * 2, st_head = p.stride_head * 2;   // bytes
+
+  // LDS byte offsets of this lane's fragments: K rows t*16 + l16 at chunk 4ks + g4 (plus
+  // t*16 rows); V^T quads at key 4*g4 + l16/4, dh 16nt + 4*(l16%4) (plus 32mu / +16 keys)
+  int kofs[KSQ], vofs[NT];
+#pragma unroll
+  for (int ks = 0; ks < KSQ; ++ks)
+    kofs[ks] = l16 * Tt::ROWB + (((4 * ks + g4) ^ tr_kswz<DH>(l16)) << 4);
+  {
+    const int vr = 4 * g4 + (l16 >> 2);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      vofs[nt] = vr * Tt::ROWB + (((2 * nt + ((l16 & 3) >> 1)) ^ tr_vswz<DH>(vr)) << 4) +
+                 8 * (l16 & 1);
+  }
+  // loader geometry: load q of this wave fills LDS bytes (wave*QI + q)*1024 + 16*lane of a
+  // stage, i.e. row r, physical chunk pc, and fetches the matching logical chunk; lko / lvo
+  // are the byte offsets of that K / V chunk from the tile's first row (< 64 rows)
+  uint32_t lko[QI], lvo[QI];
+#pragma unroll
+  for (int q = 0; q < QI; ++q) {
+    const int byte = (wave * QI + q) * 1024 + 16 * lane;
+    const int r = byte / Tt::ROWB, pc = (byte % Tt::ROWB) >> 4;
+    lko[q] = (uint32_t)(r * st_tok) + ((pc ^ tr_kswz<DH>(r)) << 4);
+    lvo[q] = (uint32_t)(r * st_tok) + ((pc ^ tr_vswz<DH>(r)) << 4);
+  }
+  const int wq = __builtin_amdgcn_readfirstlane(wave) * QI * 1024;   // wave's LDS slice
+
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    // split fastest: the splits of one query tile run on different XCDs concurrently
+    const int s = u % ns, rest = u / ns;
+    const int qt = rest % qtiles, kvh = rest / qtiles;
+    uint4 qf[2][KSQ];
+    bool valid[2];
+    int krow[2], hq[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int r = qt * kTrQRows + wave * 32 + b * 16 + l16;
+      valid[b] = r < rows;
+      const int rr = valid[b] ? r : rows - 1;
+      krow[b] = rr / g;
+      hq[b] = kvh * g + (rr - krow[b] * g);
+      const char* qp = qkv + ((size_t)krow[b] * p.ld_qkv + (size_t)hq[b] * DH) * 2;
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) qf[b][ks] = ld16(qp + (4 * ks + g4) * 16);
+    }
+    AttnState st[2] = {{-__builtin_inff(), 0.f}, {-__builtin_inff(), 0.f}};
+    f32x4 o[2][NT];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[b][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int c0 = (int)((long)s * chunks / ns), c1 = (int)((long)(s + 1) * chunks / ns);
+    const int n = c1 - c0;
+    const char* kb = (const char*)p.pk + (size_t)kvh * st_head;
+    const char* vb = (const char*)p.pv + (size_t)kvh * st_head;
+    // Every tile slot issues its loads, so each wave has exactly two tiles in flight behind
+    // the one it waits for and the wait count is a constant the compiler can track (with
+    // conditional loads it drains the ring at the loop head).  Slots past the unit's last
+    // tile load one shared cache line (the head's first row) into the stage just freed;
+    // rows past the prefix (a ragged last tile) load the last key: finite values whose
+    // weights the softmax sets to 0.
+    auto issue = [&](char* Kd, char* Vd, int i) {
+      const int key0 = (c0 + i) * kKeys;
+      const uint32_t kl = lds_addr(Kd) + wq, vl = lds_addr(Vd) + wq;
+      const char* ks[QI];
+      const char* vs[QI];
+      if (i >= n) {                       // past the unit's last tile
+#pragma unroll
+        for (int q = 0; q < QI; ++q) ks[q] = kb, vs[q] = vb;
+      } else {
+        const char* kt = kb + (size_t)key0 * st_tok;
+        const char* vt = vb + (size_t)key0 * st_tok;
+        if (key0 + kKeys <= p.P) {        // full tile
+#pragma unroll
+          for (int q = 0; q < QI; ++q) ks[q] = kt + lko[q], vs[q] = vt + lvo[q];
+        } else {                          // ragged last tile: rows past the end reload row P-1
+          const int last = p.P - 1 - key0;
+#pragma unroll
+          for (int q = 0; q < QI; ++q) {
+            const int r = ((wave * QI + q) * 1024 + 16 * lane) / Tt::ROWB;
+            const int cut = r > last ? r - last : 0;
+            ks[q] = kt + lko[q] - (long)cut * st_tok;
+            vs[q] = vt + lvo[q] - (long)cut * st_tok;
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < QI; ++q) {
+        dma16(ks[q], kl + q * 1024);
+        dma16(vs[q], vl + q * 1024);
+      }
+    };
+    // tile i: once it has landed (tiles i + 1 and i + 2 may still be in flight) and every
+    // wave has finished tile i - 1, the loads of tile i + 3 go into the stage of i - 1
+    auto body = [&](const char* Kc, const char* Vc, char* Kn, char* Vn, int i) {
+      if (i >= n) return;
+      __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm(2 * LPI));
+      __builtin_amdgcn_s_barrier();
+      issue(Kn, Vn, i + 3);
+      const int nkeys = imin(kKeys, p.P - (c0 + i) * kKeys);
+      tr_attend<DH>(Kc, Vc, nkeys, qf, kofs, vofs, p.scale_log2, st, o);
+    };
+    // the previous unit's loads, stores and LDS reads and this unit's query loads are done
+    // before the ring is refilled (the scheduling fence keeps the query loads above the
+    // wait, so no later wait has to drain the ring for them)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+    issue(K0, V0, 0);
+    issue(K1, V1, 1);
+    issue(K2, V2, 2);
+    for (int it = 0; it < n; it += kTrStages) {
+      body(K0, V0, K3, V3, it);
+      body(K1, V1, K0, V0, it + 1);
+      body(K2, V2, K1, V1, it + 2);
+      body(K3, V3, K2, V2, it + 3);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (!valid[b]) continue;
+      const float inv = st[b].l > 0.f ? 1.0f / st[b].l : 0.f;
+      const float lse = st[b].l > 0.f ? st[b].m + log2f(st[b].l) : -__builtin_inff();
+      float* po = p.part_o + (((size_t)s * K + krow[b]) * p.n_q + hq[b]) * DH;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float4 v = make_float4(o[b][nt][0] * inv, o[b][nt][1] * inv, o[b][nt][2] * inv,
+                                     o[b][nt][3] * inv);
+        *reinterpret_cast<float4*>(po + nt * 16 + g4 * 4) = v;
+      }
+      if (g4 == 0) p.part_lse[((size_t)s * K + krow[b]) * p.n_q + hq[b]] = lse;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
+}
+
+// ------------------------------------------------------------------------------------
 // Merge of the prefix splits: plane 0 of (lse, o) becomes the merge of all ns planes, once
 // per (packed row, query head) instead of once per slot that reads it.  One wave per
-// (k, h); every lane loads before any lane stores, so the merge runs in place.
+// (k, h): lane s < ns loads split s's lse, the wave reduces the maximum and the weights,
+// then every lane combines its DH/64 output elements over the splits, the loads of eight
+// splits in flight at a time.  Every lane loads before any lane stores, so the merge runs
+// in place.
 // ------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
 template <int DH>
 __device__ __forceinline__ void merge_row(const AttnParams& p, int K, int ns, int row, int lane) {
   constexpr int E = DH / 64;                  // output elements per lane
+  constexpr int SB = 8;                       // splits per batch of loads
   const size_t plane_l = (size_t)K * p.n_q;
-  constexpr int SB = 8;                      // splits per batch of loads
-  float m = -__builtin_inff();
-  for (int s0 = 0; s0 < ns; s0 += SB) {
-    float ls[SB];
-#pragma unroll
-    for (int b = 0; b < SB; ++b)
-      ls[b] = (s0 + b < ns) ? p.part_lse[(size_t)(s0 + b) * plane_l + row] : -__builtin_inff();
-#pragma unroll
-    for (int b = 0; b < SB; ++b) m = fmaxf(m, ls[b]);
-  }
+  const float ls = lane < ns ? p.part_lse[(size_t)lane * plane_l + row] : -__builtin_inff();
+  const float m = wave_max(ls);
   float l = 0.f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   if (m > -__builtin_inff()) {
+    const float w = exp2f(ls - m);            // 0 for lanes past ns and for empty splits
+    l = wave_sum(w);
     for (int s0 = 0; s0 < ns; s0 += SB) {
-      float ls[SB], v[SB][E];
+      float ws[SB], v[SB][E];
 #pragma unroll
       for (int b = 0; b < SB; ++b) {
         const int sb = imin(s0 + b, ns - 1);
-        ls[b] = (s0 + b < ns) ? p.part_lse[(size_t)sb * plane_l + row] : -__builtin_inff();
+        ws[b] = s0 + b < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sb))
+                            : 0.f;
         const float* po = p.part_o + ((size_t)sb * plane_l + row) * DH + lane * E;
 #pragma unroll
         for (int e = 0; e < E; ++e) v[b][e] = po[e];
       }
 #pragma unroll
-      for (int b = 0; b < SB; ++b) {
-        const float w = exp2f(ls[b] - m);       // 0 for an absent or empty split
-        l += w;
+      for (int b = 0; b < SB; ++b)
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += w * v[b][e];
-      }
+        for (int e = 0; e < E; ++e) acc[e] += ws[b] * v[b][e];
     }
   }
   float* po = p.part_o + (size_t)row * DH + lane * E;
@@ -326,12 +632,13 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, int K, int ns, in
   if (lane == 0) p.part_lse[row] = l > 0.f ? m + log2f(l) : -__builtin_inff();
 }
 
-template <int DH>
+template <typename T, int DH>
 __global__ void __launch_bounds__(256) attn_merge_kernel(AttnParams p) {
   const int K = imin(*p.count, p.cap);
   const int g = p.n_q / p.n_kv;
-  if (!attn_merge_on(K, g, p.n_kv, p.P, p.S)) return;
-  const int ns = attn_splits(K, g, p.n_kv, p.P);
+  constexpr int EB = (int)sizeof(T);
+  if (!attn_merge_on(K, g, p.n_kv, p.P, p.S, DH, EB)) return;
+  const int ns = attn_splits(K, g, p.n_kv, p.P, DH, EB);
   const int lane = threadIdx.x & 63;
   for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < K * p.n_q; row += gridDim.x * 4)
     merge_row<DH>(p, K, ns, row, lane);
@@ -350,7 +657,8 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
   if (K <= 0) return;
   const int g = p.n_q / p.n_kv;
   // plane 0 holds all prefix splits when attn_merge_kernel merged them
-  const int ns = attn_merge_on(K, g, p.n_kv, p.P, p.S) ? 1 : attn_splits(K, g, p.n_kv, p.P);
+  constexpr int EB = (int)sizeof(T);
+  const int ns = attn_merge_on(K, g, p.n_kv, p.P, p.S, DH, EB) ? 1 : attn_splits(K, g, p.n_kv, p.P, DH, EB);
   const int qtiles = ceil_div(p.B * g, kQRows);
   const int units = p.N * p.n_kv * qtiles;
   const int kchunks = ceil_div(p.B, kKeys);
@@ -448,27 +756,47 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
   }
 }
 
-size_t attn_partial_rows(int S, int g, int n_kv, int P) {
+size_t attn_partial_rows(int S, int g, int n_kv, int P, int dh, int elem_bytes) {
   size_t best = 0;
   for (int K = 1; K <= S; ++K) {
-    const size_t v = (size_t)attn_splits(K, g, n_kv, P) * K;
+    const size_t v = (size_t)attn_splits(K, g, n_kv, P, dh, elem_bytes) * K;
     if (v > best) best = v;
   }
   return best;
 }
 
+// Whether the split merge can run for some packed count K <= cap (otherwise its launch is
+// skipped).  The last shape asked about is remembered: a stack asks with the same one for
+// every layer.
+static bool merge_possible(int cap, int g, int n_kv, int P, int S, int dh, int eb) {
+  thread_local int key[7] = {-1, -1, -1, -1, -1, -1, -1};
+  thread_local bool val = false;
+  const int k[7] = {cap, g, n_kv, P, S, dh, eb};
+  bool same = true;
+  for (int i = 0; i < 7; ++i) same = same && key[i] == k[i];
+  if (same) return val;
+  bool v = false;
+  for (int K = 1; K <= cap && !v; ++K) v = attn_merge_on(K, g, n_kv, P, S, dh, eb);
+  for (int i = 0; i < 7; ++i) key[i] = k[i];
+  val = v;
+  return v;
+}
+
 template <typename T>
 hipError_t launch_attn_prefix(const AttnParams& p, int num_cu, hipStream_t st) {
   if (p.P <= 0) return hipSuccess;
-  const int grid = 2 * num_cu;
   const int mrows = ceil_div(p.cap * p.n_q, 4);
-  const int mgrid = mrows < num_cu ? mrows : num_cu;   // persistent
+  const int mgrid = mrows < 4 * num_cu ? mrows : 4 * num_cu;   // grid-stride over rows
+  const bool tr = attn_use_tr((int)sizeof(T), p.P);
+  const bool merge = merge_possible(p.cap, p.n_q / p.n_kv, p.n_kv, p.P, p.S, p.dh, (int)sizeof(T));
   if (p.dh == 128) {
-    attn_prefix_kernel<T, 128><<<grid, 256, 0, st>>>(p);
-    attn_merge_kernel<128><<<mgrid, 256, 0, st>>>(p);
+    if (tr) attn_prefix_tr_kernel<128><<<num_cu, kTrWaves * 64, 0, st>>>(p);
+    else attn_prefix_kernel<T, 128><<<2 * num_cu, 256, 0, st>>>(p);
+    if (merge) attn_merge_kernel<T, 128><<<mgrid, 256, 0, st>>>(p);
   } else if (p.dh == 64) {
-    attn_prefix_kernel<T, 64><<<grid, 256, 0, st>>>(p);
-    attn_merge_kernel<64><<<mgrid, 256, 0, st>>>(p);
+    if (tr) attn_prefix_tr_kernel<64><<<num_cu, kTrWaves * 64, 0, st>>>(p);
+    else attn_prefix_kernel<T, 64><<<2 * num_cu, 256, 0, st>>>(p);
+    if (merge) attn_merge_kernel<T, 64><<<mgrid, 256, 0, st>>>(p);
   } else {
     return hipErrorInvalidValue;
   }

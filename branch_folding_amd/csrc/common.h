@@ -42,17 +42,16 @@ __device__ __forceinline__ void unpack16(const uint4& u, float (&f)[4], float) {
   f[2] = __uint_as_float(u.z);
   f[3] = __uint_as_float(u.w);
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// pairs convert with one v_cvt_pk_bf16_f32 each (round to nearest even)
 __device__ __forceinline__ uint4 pack16(const float (&f)[8], bf16) {
-  uint4 u;
   uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    bf16 lo = (bf16)f[2 * e], hi = (bf16)f[2 * e + 1];
-    w[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-  }
-  u.x = w[0]; u.y = w[1]; u.z = w[2]; u.w = w[3];
-  return u;
+  for (int e = 0; e < 4; ++e)
+    w[e] = __builtin_bit_cast(uint32_t,
+                              __builtin_convertvector(f32x2{f[2 * e], f[2 * e + 1]}, bf16x2));
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 __device__ __forceinline__ uint4 pack16(const float (&f)[4], float) {
   uint4 u;
@@ -85,16 +84,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
-// Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48) in the VALU.
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with the even rows
+// of its second (v_permlane32_swap: the upper 32 lanes of the first with the lower 32 of
+// the second); with the same value in both operands every lane gets back {its own value,
+// lane l^16's} (resp. l^32's), in some order.  No LDS round trip, unlike ds_bpermute.
 __device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, kWave));
-  v = fmaxf(v, __shfl_xor(v, 32, kWave));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group4_sum(float v) {
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // ------------------------------------------------------------------------------------

@@ -122,26 +122,63 @@ struct AttnParams {
 };
 
 constexpr int kAttnMaxSplit = 32;
-__host__ __device__ inline int attn_splits(int K, int g, int n_kv, int P) {
-  if (P <= 0 || K <= 0) return 0;
-  const int qtiles = (K * g + 63) / 64;
-  const int units = n_kv * qtiles;
-  const int chunks = (P + 63) / 64;
-  int s = (2 * kPlanCUs + units - 1) / units;
-  int smax = chunks / 2;
-  if (smax < 1) smax = 1;
-  if (s > smax) s = smax;
-  if (s > kAttnMaxSplit) s = kAttnMaxSplit;
-  return s;
+// Prefix-phase kernels: bf16 prefixes of at least kAttnTrMinPrefix keys run 256-query
+// units, one workgroup per CU (direct-to-LDS K/V ring, transposed V reads); shorter bf16
+// prefixes and fp32 run 64-query units, two workgroups per CU (K/V staged through
+// registers), which spreads a short prefix over four times as many units.
+constexpr int kAttnTrMinPrefix = 2048;
+static_assert(kPlanCUs == 256, "attn_splits shifts by log2 of the slot count");
+__host__ __device__ inline bool attn_use_tr(int elem_bytes, int P) {
+  return elem_bytes == 2 && P >= kAttnTrMinPrefix;
 }
-// Whether the prefix splits are merged once per (packed row, head) before the block phase:
-// worth a pass when the slots' re-reads it saves, S * (ns - 1), dwarf its own K * (ns + 1).
-__host__ __device__ inline bool attn_merge_on(int K, int g, int n_kv, int P, int S) {
-  const int ns = attn_splits(K, g, n_kv, P);
-  return ns >= 2 && (long)S * (ns - 1) >= 8L * K * (ns + 1);
+struct AttnPlan {
+  int qrows, slots;
+};
+__host__ __device__ inline AttnPlan attn_plan(int elem_bytes, int P) {
+  return attn_use_tr(elem_bytes, P) ? AttnPlan{256, kPlanCUs} : AttnPlan{64, 2 * kPlanCUs};
+}
+// Prefix key splits per (KV head, query tile) unit, a power of two.  A unit streams
+// ceil(chunks / s) key tiles and the grid runs `slots` units at a time (a power of two), so
+// the prefix phase takes about ceil(units * s / slots) rounds of that many tiles.  Each
+// split also costs its partial rows: K*g*n_kv rows of dh+1 floats written, merged and read
+// again, about rows*(dh+1) / 2^18 quarter tiles at the measured tile time and partial
+// traffic rate.  s minimises the sum (in quarter tiles).  Every workgroup of the attention
+// kernels evaluates this on the device, so it uses shifts only.
+__host__ __device__ inline int attn_splits(int K, int g, int n_kv, int P, int dh,
+                                           int elem_bytes) {
+  if (P <= 0 || K <= 0) return 0;
+  const AttnPlan pl = attn_plan(elem_bytes, P);
+  const int lslots = pl.slots == 2 * kPlanCUs ? 9 : 8;   // log2 of 512 / 256
+  const int units = n_kv * ((K * g + pl.qrows - 1) / pl.qrows);
+  const int chunks = (P + 63) >> 6;
+  const long per_split = ((long)K * g * n_kv * (dh + 1)) >> 18;
+  const int split_cost = per_split < 1 ? 1 : (int)per_split;
+  int best = 1;
+  long best_cost = -1;
+  for (int ls = 0; (1 << ls) <= kAttnMaxSplit && ((1 << ls) <= chunks / 2 || ls == 0); ++ls) {
+    const int s = 1 << ls;
+    const long rounds = ((long)units * s + (1 << lslots) - 1) >> lslots;
+    const long cost = rounds * ((chunks + s - 1) >> ls) * 4 + (long)s * split_cost;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+// Whether the prefix splits are merged once per (packed row, head) before the block phase.
+// Without the pass every slot reads all ns partial planes of its packed row; with it the
+// pass reads K * ns planes and writes K, and the slots read one.  It is worth its own
+// launch when the partial bytes it saves exceed ~16 MB (a few microseconds of traffic).
+__host__ __device__ inline bool attn_merge_on(int K, int g, int n_kv, int P, int S, int dh,
+                                              int elem_bytes) {
+  const int ns = attn_splits(K, g, n_kv, P, dh, elem_bytes);
+  if (ns < 2) return false;
+  const long saved_rows = (long)S * (ns - 1) - (long)K * (ns + 1);
+  return saved_rows * g * n_kv * (dh + 1) * 4 >= (16L << 20);
 }
 // largest nsplit * K over K in [1, S] (rows of partial storage)
-size_t attn_partial_rows(int S, int g, int n_kv, int P);
+size_t attn_partial_rows(int S, int g, int n_kv, int P, int dh, int elem_bytes);
 
 template <typename T>
 hipError_t launch_attn_prefix(const AttnParams& p, int num_cu, hipStream_t st);

@@ -118,7 +118,7 @@ Layout layout_of(const specfold_shape* s) {
   const size_t qkvd = (size_t)(s->n_q_heads + 2 * s->n_kv_heads) * dh;
   const size_t qd = (size_t)s->n_q_heads * dh;
   const int g = s->n_q_heads / s->n_kv_heads;
-  const size_t prow = attn_partial_rows((int)S, g, s->n_kv_heads, s->prefix_len);
+  const size_t prow = attn_partial_rows((int)S, g, s->n_kv_heads, s->prefix_len, (int)dh, (int)eb);
   size_t gp = 0;
   const int ebi = (int)eb;
   gp = std::max(gp, gemm_partial_elems((int)S, (int)qkvd, (int)d, ebi));
