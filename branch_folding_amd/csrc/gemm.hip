@@ -98,11 +98,14 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
   for (int u = blockIdx.x; u < per_xcd * 8; u += gridDim.x) {
     const int v = (u & 7) * per_xcd + (u >> 3);       // XCD u%8 owns a contiguous range
     if (v >= units) continue;
-    // K-slice slowest, row tile fastest: an XCD's range covers one or two K-slices, so it
-    // pulls only those slices of the shared activation operand into its L2, and the row
-    // tiles that share a weight column tile run side by side
-    const int mt = v % mb, rest = v / mb;
-    const int ntile = rest % nt, s = rest / nt;
+    // K-slice slowest: an XCD's range covers one or two K-slices, so it pulls only those
+    // slices of the shared activation operand into its L2.  Within a K-slice the tiles go in
+    // bands of up to 8 row tiles, row tile fastest: the units an XCD runs side by side cover
+    // a few column tiles of one band, so both operands of a round stay in its L2 (row tile
+    // fastest over all rows would stream every activation row tile once per column tile).
+    const int s = v / (mb * nt), vt = v - s * (mb * nt);
+    const int band = vt / (8 * nt), bh = imin(8, mb - band * 8), vb = vt - band * 8 * nt;
+    const int mt = band * 8 + vb % bh, ntile = vb / bh;
     const int m0 = mt * kGemmBM, n0 = ntile * BN;
     const int kb = (int)((long)s * kiters / split), ke = (int)((long)(s + 1) * kiters / split);
 
@@ -143,23 +146,31 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool rows_live = (m0 + wm * 64) < M;
 
+    // One wave per SIMD, so LDS latency is hidden inside the wave: all operand fragments of
+    // the k-iteration are read at once (the second k-step's reads land while the first
+    // k-step's MFMAs run), then its MFMAs.
     auto compute = [&](const char* as, const char* ws) {
       if (!rows_live) return;
+      constexpr int KS = kGemmBKBytes / 64;
+      uint4 af[KS][4], bfr[KS][4];
 #pragma unroll
-      for (int ks = 0; ks < kGemmBKBytes / 64; ++ks) {
-        uint4 af[4], bfr[4];
+      for (int ks = 0; ks < KS; ++ks) {
         const int c = ks * 4 + g4;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const uint4*>(as + swz(wm * 64 + i * 16 + l16, c));
+          af[ks][i] = *reinterpret_cast<const uint4*>(as + swz(wm * 64 + i * 16 + l16, c));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          bfr[j] = *reinterpret_cast<const uint4*>(ws + swz(wn * 64 + j * 16 + l16, c));
+          bfr[ks][j] = *reinterpret_cast<const uint4*>(ws + swz(wn * 64 + j * 16 + l16, c));
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep every read ahead of the MFMAs
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mma_kstep(af[i], bfr[j], acc[i][j], T());
-      }
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = mma_kstep(af[ks][i], bfr[ks][j], acc[i][j], T());
     };
     // k-iteration i on stage (as, ws): once this wave's loads of i have landed (only the
     // LPI loads of i + 1 may still be pending) and every wave has passed the barrier --
