@@ -65,6 +65,19 @@ EDGE = [
 ]
 
 
+# bf16 prefixes of 2048+ keys take the 256-query prefix kernel (direct-to-LDS ring,
+# transposed V reads): ragged last tiles (52 keys; 1 key), head_dim 128 and 64, GQA 7:1 and
+# 2:1, enough packed rows for several query tiles and splits.
+LONG_PREFIX = [
+    custom_config(name="longp-ragged-dh128", num_nodes=9, block=40, hidden=256, n_q=7, n_kv=1,
+                  head_dim=128, ffn=256, prefix=2100, dtype="bf16", graph="dag",
+                  reveal=(1, 3), seed=37),
+    custom_config(name="longp-ragged-dh64", num_nodes=6, block=24, hidden=256, n_q=4, n_kv=2,
+                  head_dim=64, ffn=256, prefix=2049, dtype="bf16", graph="chain",
+                  reveal=(1, 2), seed=38),
+]
+
+
 def _check_layer(cfg, w, tau, L, DeviceLayer, slots=None):
     _say(f"[gpu] layer {cfg.name} tau={tau} S={cfg.slots}")
     dl = DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src)
@@ -110,6 +123,13 @@ def test_layer_small(cfg, tau):
     L, DeviceLayer = _dev()
     w = _workload(cfg)
     _check_layer(cfg, w, tau, L, DeviceLayer)
+
+
+@pytest.mark.parametrize("cfg", LONG_PREFIX, ids=lambda c: c.name)
+@pytest.mark.parametrize("tau", [-1.0, 0.05])
+def test_layer_long_prefix(cfg, tau):
+    L, DeviceLayer = _dev()
+    _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
 
 
 def test_fold_steps_individually():
