@@ -126,13 +126,17 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
       const int wr = w_row_of<EPI, BN>(n0 + r, p.N, p.ff);
       w_src[q] = Wb + (size_t)wr * p.ldw * sizeof(T) + c * 16;
     }
-    // Stage loads of k-iteration `it` (clamped to the unit's last one: cache hits, unused).
-    auto issue = [&](char* as, char* ws, int it) {
+    // Stage loads of k-iteration `it` (clamped to the unit's last one: cache hits, unused):
+    // the weight tile and the A tile.
+    auto issue_w = [&](char* ws, int it) {
       const size_t off = (size_t)imin(it, ke - 1) * kGemmBKBytes;
 #pragma unroll
       for (int q = 0; q < WQ; ++q)
         __builtin_amdgcn_global_load_lds((glb_void_t*)(w_src[q] + off),
                                          (lds_void_t*)(ws + (wave * WQ + q) * 1024), 16, 0, 0);
+    };
+    auto issue_a = [&](char* as, int it) {
+      const size_t off = (size_t)imin(it, ke - 1) * kGemmBKBytes;
 #pragma unroll
       for (int q = 0; q < AQ; ++q)
         __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[q] + off),
@@ -175,19 +179,24 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
     // k-iteration i on stage (as, ws): once this wave's loads of i have landed (only the
     // LPI loads of i + 1 may still be pending) and every wave has passed the barrier --
     // so all loads of i are visible and nobody still reads the stage that held i - 1 --
-    // the loads of i + 2 go into that freed stage and the MFMAs run on stage i.
+    // the loads of i + 2 go into that freed stage and the MFMAs run on stage i.  The
+    // weight tile is issued before the MFMAs and the A tile after them, so a wave whose
+    // CU has too many loads outstanding does not stall at the issue before its MFMAs.
     auto body = [&](char* as, char* ws, char* as2, char* ws2, int i) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPI));
       __builtin_amdgcn_s_barrier();
-      issue(as2, ws2, i + 2);
+      issue_w(ws2, i + 2);
       if (i < ke) compute(as, ws);
+      issue_a(as2, i + 2);
     };
 
     // every wave is done with the previous unit's stages and its loads have landed
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
-    issue(As0, Ws0, kb);
-    issue(As1, Ws1, kb + 1);
+    issue_w(Ws0, kb);
+    issue_a(As0, kb);
+    issue_w(Ws1, kb + 1);
+    issue_a(As1, kb + 1);
     for (int it = kb; it < ke; it += kGemmStages) {
       body(As0, Ws0, As2, Ws2, it);
       body(As1, Ws1, As0, Ws0, it + 1);
@@ -302,13 +311,16 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
     const int wr = (b & 1) ? p.ff + j : j;
     w_src[q] = Wb + (size_t)wr * p.ldw * sizeof(T) + c * 16;
   }
-  // loads of k-iteration `it` into a stage: W, then the A tile(s)
-  auto issue = [&](char* a0, char* a1, char* ws, int it) {
+  // loads of k-iteration `it` into a stage: the weight chunk, and the A tile(s)
+  auto issue_w = [&](char* ws, int it) {
     const size_t off = (size_t)imin(it, kiters - 1) * kGemmBKBytes;
 #pragma unroll
     for (int q = 0; q < WQ; ++q)
       __builtin_amdgcn_global_load_lds((glb_void_t*)(w_src[q] + off),
                                        (lds_void_t*)(ws + (wave * WQ + q) * 1024), 16, 0, 0);
+  };
+  auto issue_a = [&](char* a0, char* a1, int it) {
+    const size_t off = (size_t)imin(it, kiters - 1) * kGemmBKBytes;
 #pragma unroll
     for (int rt = 0; rt < R; ++rt) {
       char* as = rt == 0 ? a0 : a1;
@@ -365,17 +377,24 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
 
   // three stages, two k-iterations in flight: once this wave's loads of i have landed
   // (only the LPI loads of i + 1 may still be pending) and every wave has passed the
-  // barrier, the loads of i + 2 go into the stage freed by i - 1
+  // barrier, the loads of i + 2 go into the stage freed by i - 1.  The weight chunk (HBM,
+  // long latency) is issued before the MFMAs of i, the A tiles (L2 hits) after them: a CU
+  // keeps only so many loads outstanding, and with a full stage in flight the issue of the
+  // whole next stage would stall the wave before its MFMAs (18% of the time at 129..256
+  // rows).
   auto body = [&](char* a0, char* a1, char* ws, char* n0, char* n1, char* nw, int i) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPI));
     __builtin_amdgcn_s_barrier();
-    issue(n0, n1, nw, i + 2);
+    issue_w(nw, i + 2);
     if (i < kiters) compute(a0, a1, ws);
+    issue_a(n0, n1, i + 2);
   };
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __builtin_amdgcn_s_barrier();
-  issue(As0, Bs0, Ws0, 0);
-  issue(As1, Bs1, Ws1, 1);
+  issue_w(Ws0, 0);
+  issue_a(As0, Bs0, 0);
+  issue_w(Ws1, 1);
+  issue_a(As1, Bs1, 1);
   for (int it = 0; it < kiters; it += kGemmStages) {
     body(As0, Bs0, Ws0, As2, Bs2, Ws2, it);
     body(As1, Bs1, Ws1, As0, Bs0, Ws0, it + 1);
