@@ -380,6 +380,10 @@ __device__ __forceinline__ void tr_attend(const char* Ks, const char* Vs, int nk
                                           const int (&vofs)[TrTile<DH>::NT], float scale_log2,
                                           AttnState (&st)[2], f32x4 (&o)[2][TrTile<DH>::NT]) {
   using Tt = TrTile<DH>;
+  // The two waves sharing a SIMD alternate between MFMA phases and the softmax; the MFMA
+  // phases run at raised wave priority, so one wave's MFMAs issue ahead of the other's
+  // softmax and the matrix pipe stays busy.
+  __builtin_amdgcn_s_setprio(1);
   // S^T = K Q^T: sc[b][t][r] = key t*16 + g4*4 + r, query l16 of block b
   f32x4 sc[2][4];
 #pragma unroll
@@ -393,6 +397,7 @@ __device__ __forceinline__ void tr_attend(const char* Ks, const char* Vs, int nk
       sc[1][t] = mma_kstep(kf, qf[1][ks], sc[1][t], bf16());
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   softmax_tile<Tt::NT>(sc[0], nkeys, scale_log2, st[0], o[0]);
   softmax_tile<Tt::NT>(sc[1], nkeys, scale_log2, st[1], o[1]);
   // P^T as the B operand: k-step mu covers keys 32mu + 4*g4 + 0..3 and 32mu + 16 + 4*g4 + 0..3
@@ -411,6 +416,7 @@ __device__ __forceinline__ void tr_attend(const char* Ks, const char* Vs, int nk
     }
   // O^T += V^T P^T with V^T fragments read transposed from the natural V tile: the same
   // two key quads per lane group as the P^T operand above
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int mu = 0; mu < 2; ++mu)
 #pragma unroll
@@ -424,6 +430,7 @@ __device__ __forceinline__ void tr_attend(const char* Ks, const char* Vs, int nk
       o[0][nt] = mma_kstep(vf, pb[0][mu], o[0][nt], bf16());
       o[1][nt] = mma_kstep(vf, pb[1][mu], o[1][nt], bf16());
     }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int DH>
@@ -539,14 +546,16 @@ __global__ void __launch_bounds__(kTrWaves * 64, 1) attn_prefix_tr_kernel(AttnPa
       }
     };
     // tile i: once it has landed (tiles i + 1 and i + 2 may still be in flight) and every
-    // wave has finished tile i - 1, the loads of tile i + 3 go into the stage of i - 1
+    // wave has finished tile i - 1, tile i is attended and the loads of tile i + 3 go into
+    // the stage of i - 1 (after the MFMAs: with two tiles in flight the CU's outstanding
+    // loads are at their limit, and issuing first would stall the wave before its MFMAs)
     auto body = [&](const char* Kc, const char* Vc, char* Kn, char* Vn, int i) {
       if (i >= n) return;
       __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm(2 * LPI));
       __builtin_amdgcn_s_barrier();
-      issue(Kn, Vn, i + 3);
       const int nkeys = imin(kKeys, p.P - (c0 + i) * kKeys);
       tr_attend<DH>(Kc, Vc, nkeys, qf, kofs, vofs, p.scale_log2, st, o);
+      issue(Kn, Vn, i + 3);
     };
     // the previous unit's loads, stores and LDS reads and this unit's query loads are done
     // before the ring is refilled (the scheduling fence keeps the query loads above the
