@@ -4,9 +4,12 @@
 //
 // Prefix phase: for every packed row k and query head h, online-softmax partials
 //   (lse, normalised output) over a range of prefix keys.  The prefix is read through the
-//   caller's strided view once per (KV head, 64-query tile) -- never copied per branch --
-//   and all g query heads of a KV head share every K/V tile.
-// Split merge: the prefix partials of each (packed row, head) are merged once.
+//   caller's strided view once per (KV head, query tile) -- never copied per branch -- and
+//   all g query heads of a KV head share every K/V tile.  Two kernels: 256-query tiles
+//   with a direct-to-LDS K/V ring for bf16 prefixes of 2048+ keys, 64-query tiles with
+//   K/V staged through registers otherwise (short prefixes spread over more units).
+// Split merge: the prefix partials of each (packed row, head) are merged once, when that
+//   saves enough partial traffic; otherwise the block phase merges them.
 // Block phase: for every slot (n, i) and head h, the query of its packed row slot_row[n,i]
 //   attends to branch n's own block keys/values (rows slot_row[n, j]); the running state
 //   starts from the merged prefix partial of that packed row, which is the correction step.
@@ -14,7 +17,8 @@
 // MFMA formulation: scores are computed transposed, S^T = K Q^T (keys as the A operand from
 // LDS, queries as the B operand in registers), so every lane ends up holding one query's
 // scores for 16 keys; the output is accumulated transposed, O^T = V^T P^T, so the
-// probabilities feed the B operand straight from registers and V is staged transposed.
+// probabilities feed the B operand straight from registers; the V^T operand comes from a
+// transposed copy of V in LDS, or from V's natural layout through transposed LDS reads.
 #include "common.h"
 #include "kernels.h"
 
