@@ -168,14 +168,16 @@ __host__ __device__ inline int attn_splits(int K, int g, int n_kv, int P, int dh
 }
 // Whether the prefix splits are merged once per (packed row, head) before the block phase.
 // Without the pass every slot reads all ns partial planes of its packed row; with it the
-// pass reads K * ns planes and writes K, and the slots read one.  It is worth its own
-// launch when the partial bytes it saves exceed ~16 MB (a few microseconds of traffic).
+// pass reads K * ns planes and writes K, and the slots read one.  The pass costs a launch
+// (~4.5 us even when it finds nothing to do) plus its traffic, so it runs only when the
+// partial bytes it saves exceed 32 MB; a shape for which no packed count gets there (the
+// 7B layer with a 512-key prefix) never launches it.
 __host__ __device__ inline bool attn_merge_on(int K, int g, int n_kv, int P, int S, int dh,
                                               int elem_bytes) {
   const int ns = attn_splits(K, g, n_kv, P, dh, elem_bytes);
   if (ns < 2) return false;
   const long saved_rows = (long)S * (ns - 1) - (long)K * (ns + 1);
-  return saved_rows * g * n_kv * (dh + 1) * 4 >= (16L << 20);
+  return saved_rows * g * n_kv * (dh + 1) * 4 >= (32L << 20);
 }
 // largest nsplit * K over K in [1, S] (rows of partial storage)
 size_t attn_partial_rows(int S, int g, int n_kv, int P, int dh, int elem_bytes);
