@@ -13,8 +13,8 @@ namespace specfold {
 // With `An` the same pass also writes the RMS-normalised row
 // An[slot] = H[slot] / sqrt(mean(H[slot]^2) + eps) * g of every slot that computes its own
 // row -- decided here, or marked in `rec_given` -- for the QKV GEMM to gather, so the layer
-// input is read once for both.  Loads go four 16-byte chunks per lane at a time so a row
-// costs a couple of memory round trips, not one per chunk.
+// input is read once for both.  A row of up to 512 16-byte chunks is fetched in a single
+// round of loads and kept in registers for the normalisation.
 // ------------------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
@@ -30,41 +30,53 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
   if (slot >= N * B) return;
   const int n = slot / B, i = slot - n * B;
   const bool decide = (ratio != nullptr) || (recompute != nullptr);
+  constexpr int VE = Pack16<T>::kElems;
+  constexpr int U = 8;                       // chunks per lane held in registers
+  const int chunks = d / VE;
+  const T* c = H + (size_t)slot * d;
+  // The child row's loads go out before the fold source is known, so its lookup and the
+  // row fetch overlap; rows of up to 64*U chunks take one round of loads, and the
+  // normalisation pass reuses the registers instead of re-reading the row.
+  uint4 vc[U], vp[U], vg[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) vc[u] = ld16(c + imin(lane + 64 * u, chunks - 1) * VE);
+  if (An) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) vg[u] = ld16(g + imin(lane + 64 * u, chunks - 1) * VE);
+  }
   int p = -1;
   if (n > 0 && fold_src) p = fold_src[n];
   const bool fs_ok = (n > 0) && (p >= 0) && (p < n);
   const bool has_parent = decide && fs_ok;
-  const T* c = H + (size_t)slot * d;
   const T* q = has_parent ? H + ((size_t)p * B + i) * d : c;
-  constexpr int VE = Pack16<T>::kElems;
-  constexpr int U = 4;                       // chunks per lane in flight
-  const int chunks = d / VE;
+  if (has_parent) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) vp[u] = ld16(q + imin(lane + 64 * u, chunks - 1) * VE);
+  }
   float sd = 0.f, sp = 0.f, sc = 0.f;
-  for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
-    uint4 vc[U], vp[U];
+  auto accum = [&](const uint4& xc, const uint4& xp) {
+    float fc[VE], fp[VE];
+    unpack16(xc, fc, T());
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ch = imin(c0 + 64 * u, chunks - 1);
-      vc[u] = ld16(c + ch * VE);
-      if (has_parent) vp[u] = ld16(q + ch * VE);
-    }
+    for (int e = 0; e < VE; ++e) sc = fmaf(fc[e], fc[e], sc);
+    if (has_parent) {
+      unpack16(xp, fp, T());
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (c0 + 64 * u >= chunks) break;
-      float fc[VE], fp[VE];
-      unpack16(vc[u], fc, T());
-#pragma unroll
-      for (int e = 0; e < VE; ++e) sc = fmaf(fc[e], fc[e], sc);
-      if (has_parent) {
-        unpack16(vp[u], fp, T());
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          const float df = fc[e] - fp[e];
-          sd = fmaf(df, df, sd);
-          sp = fmaf(fp[e], fp[e], sp);
-        }
+      for (int e = 0; e < VE; ++e) {
+        const float df = fc[e] - fp[e];
+        sd = fmaf(df, df, sd);
+        sp = fmaf(fp[e], fp[e], sp);
       }
     }
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (lane + 64 * u < chunks) accum(vc[u], vp[u]);
+  // rows longer than 64*U chunks: the remaining chunks stream through in further rounds
+  for (int c0 = lane + 64 * U; c0 < chunks; c0 += 64) {
+    const uint4 xc = ld16(c + c0 * VE);
+    const uint4 xp = has_parent ? ld16(q + c0 * VE) : xc;
+    accum(xc, xp);
   }
   // fold decision (root rows and malformed fold sources always compute their own row)
   bool rec = true;
@@ -84,25 +96,18 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
   if (!own) return;                          // folded: the QKV GEMM never reads this row
   const float rstd = 1.0f / sqrtf(wave_sum(sc) / (float)d + eps);
   T* o = An + (size_t)slot * ld_an;
-  for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
-    uint4 vc[U], vg[U];
+  auto norm = [&](const uint4& xc, const uint4& xg, int ch) {
+    float fc[VE], fg[VE];
+    unpack16(xc, fc, T());
+    unpack16(xg, fg, T());
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ch = imin(c0 + 64 * u, chunks - 1);
-      vc[u] = ld16(c + ch * VE);
-      vg[u] = ld16(g + ch * VE);
-    }
+    for (int e = 0; e < VE; ++e) fc[e] = fc[e] * rstd * fg[e];
+    st16(o + ch * VE, pack16(fc, T()));
+  };
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (c0 + 64 * u >= chunks) break;
-      float fc[VE], fg[VE];
-      unpack16(vc[u], fc, T());
-      unpack16(vg[u], fg, T());
-#pragma unroll
-      for (int e = 0; e < VE; ++e) fc[e] = fc[e] * rstd * fg[e];
-      st16(o + (c0 + 64 * u) * VE, pack16(fc, T()));
-    }
-  }
+  for (int u = 0; u < U; ++u)
+    if (lane + 64 * u < chunks) norm(vc[u], vg[u], lane + 64 * u);
+  for (int c0 = lane + 64 * U; c0 < chunks; c0 += 64) norm(ld16(c + c0 * VE), ld16(g + c0 * VE), c0);
 }
 
 // ------------------------------------------------------------------------------------
