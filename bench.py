@@ -224,6 +224,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also run the tau sweep of config 2")
+    ap.add_argument("--budget-sweep", action="store_true",
+                    help="also run the draft-budget sweep: the 7B layer at 1+{3,7,15,31,63} "
+                         "branches, dense and folded")
     ap.add_argument("--stack", action="store_true",
                     help="also time the 28-layer stack (config 3) end to end")
     ap.add_argument("--stack-steps", type=int, default=20)
@@ -255,8 +258,11 @@ def main():
     log(f"[bench] K={K} of S={cfg.slots} packed rows")
 
     dom = L.STEPS.index("ffn_gate_up")
-    ms, per = time_layer(dl, tau, args.steps, args.warmup, ev, stream, probe_step=dom)
+    # the timed steps carry no probe events; the dominant kernel's launch duration is
+    # measured in a second pass of the same length with events around that launch only
+    ms, _ = time_layer(dl, tau, args.steps, args.warmup, ev, stream)
     log(f"[bench] {ms * 1e3:.1f} us per verify layer")
+    _, per = time_layer(dl, tau, args.steps, 2, ev, stream, probe_step=dom)
     dom_ms = sum(per) / len(per)
     alg = algorithmic(cfg, K)
     dom_bytes = alg["ffn_gate_up"]["bytes"]
@@ -296,8 +302,16 @@ def main():
     report = {"main": result}
     if args.sweep:
         report["tau_sweep"] = tau_sweep(ev, stream, args.steps, args.warmup)
-    if args.stack:
+    if args.budget_sweep:
         del dl
+        torch.cuda.empty_cache()
+        report["budget_sweep"] = budget_sweep(w, ev, stream, args.steps, args.warmup)
+        result["budget_sweep"] = [{k: r[k] for k in ("branches", "tau", "K", "us",
+                                                     "branch_tokens_per_s")}
+                                  for r in report["budget_sweep"]]
+    if args.stack:
+        if not args.budget_sweep:
+            del dl
         torch.cuda.empty_cache()
         report["stack"] = stack_bench(ev, stream, args.stack_steps, 3)
         result["stack"] = {k: report["stack"][k] for k in
@@ -330,6 +344,35 @@ def tau_sweep(ev, stream, steps, warmup):
         rows.append(dict(tau=tau, K=K, recompute_fraction=K / cfg.slots, us=ms * 1e3,
                          kernels_us=kern))
         log(f"[bench] sweep tau={tau}: K={K} ({K / cfg.slots:.3f}) {ms * 1e3:.1f} us")
+    return rows
+
+
+def budget_sweep(w1, ev, stream, steps, warmup):
+    """Per-verify-layer time against the draft budget (the pages' Fig. 3 plots the
+    per-verify latency rising with it): the 7B-shaped layer with 1 + {3, 7, 15, 31, 63}
+    branches of one 3-ary level-order tree, dense (tau < 0, every branch recomputed) and
+    folded at the configuration's tau.  Weights and prefix are those of the 1 + 15 layer
+    (the same seed draws the same values); only the graph and the hidden states change."""
+    import torch
+    from branch_folding_amd.runner import DeviceLayer
+    from synth import BUDGETS, budget_config, make_workload
+    rows = []
+    for n in BUDGETS:
+        cfg = budget_config(n)
+        wn = make_workload(cfg, layers=1, weights=False)
+        dl = DeviceLayer(cfg, w1.weights[0], w1.cache, wn.H, wn.fold_src)
+        for tau in (-1.0, cfg.tau):
+            dl.forward(tau, stream=stream)
+            torch.cuda.synchronize()
+            K = dl.fold_state()["K"]
+            ms, _ = time_layer(dl, tau, steps, warmup, ev, stream)
+            rows.append(dict(branches=n, slots=cfg.slots, tau=tau, K=K,
+                             recompute_fraction=K / cfg.slots, us=ms * 1e3,
+                             branch_tokens_per_s=cfg.slots / (ms * 1e-3)))
+            log(f"[bench] budget 1+{n - 1} tau={tau}: K={K} of {cfg.slots} "
+                f"{ms * 1e3:.1f} us ({cfg.slots / (ms * 1e-3) / 1e6:.2f} M branch-tok/s)")
+        del dl
+        torch.cuda.empty_cache()
     return rows
 
 

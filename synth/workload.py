@@ -32,7 +32,8 @@ import numpy as np
 __all__ = [
     "Config", "CONFIGS", "Workload", "make_workload", "make_layer_weights",
     "round_bf16", "bf16_bits", "draft_graph", "hidden_states", "prefix_cache",
-    "custom_config", "graph_depth", "layer_weights_of", "layer_cache_of", "iter_layers",
+    "custom_config", "budget_config", "BUDGETS", "graph_depth", "layer_weights_of",
+    "layer_cache_of", "iter_layers",
 ]
 
 
@@ -91,6 +92,18 @@ CONFIGS: Dict[int, Config] = {
               head_dim=128, ffn=14336, prefix=16384, dtype="bf16", tau=0.02,
               graph="dag_deep", reveal=(1, 4), seed=1004, max_depth=6),
 }
+
+
+# Draft budgets of the budget sweep (SpecFold explainer, Fig. 3 and the draft-budget
+# appendix: per-verify latency against the number of draft branches): the 7B-shaped layer
+# with 1 + {3, 7, 15, 31, 63} branches of the same 3-ary level-order tree.
+BUDGETS: Tuple[int, ...] = (4, 8, 16, 32, 64)
+
+
+def budget_config(num_nodes: int) -> Config:
+    """The 7B-shaped layer with `num_nodes` nodes (root + children); same seed, weights and
+    prefix as the 1 + 15 layer, so only the draft graph and the hidden states change."""
+    return CONFIGS[1].with_(num_nodes=num_nodes, name=f"7b-layer-1+{num_nodes - 1}")
 
 
 def custom_config(**kw) -> Config:

@@ -13,7 +13,7 @@ import torch
 
 from parity_util import (TOL, assert_fold_state_equal, max_abs_rel, oracle_layer,
                          oracle_state)
-from synth import CONFIGS, custom_config, make_workload
+from synth import CONFIGS, budget_config, custom_config, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -231,3 +231,21 @@ def test_cfg4_stress_sampled():
     slots += [(int(rng.integers(0, cfg.num_nodes)), int(rng.integers(0, cfg.block)))
               for _ in range(27)]
     _check_layer(cfg, w, cfg.tau, L, DeviceLayer, slots=slots)
+
+
+@pytest.mark.parametrize("n,tau", [(4, 0.05), (4, -1.0), (64, 0.05), (64, -1.0)])
+def test_budget_sweep_ends(n, tau):
+    """The draft-budget sweep's smallest and largest layers (7B shape, 1 + 3 and 1 + 63
+    branches of the 3-ary tree), folded and dense, in the benchmark's launch configuration.
+    1 + 3 compares every slot; 1 + 63 (2048 slots) compares sampled slots the oracle
+    evaluates one by one: roots, the deepest leaves, the last slot."""
+    L, DeviceLayer = _dev()
+    cfg = budget_config(n)
+    w = _workload(cfg)
+    slots = None
+    if cfg.slots > 512:
+        rng = np.random.default_rng(1)
+        slots = [(0, 0), (0, cfg.block - 1), (n - 1, cfg.block - 1), (n // 2, 3)]
+        slots += [(int(rng.integers(0, n)), int(rng.integers(0, cfg.block)))
+                  for _ in range(20)]
+    _check_layer(cfg, w, tau, L, DeviceLayer, slots=slots)

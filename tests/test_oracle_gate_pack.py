@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import bruteforce_provenance, fold_state, gate, pack, resolve
-from synth import CONFIGS, custom_config, graph_depth, make_workload
+from synth import BUDGETS, CONFIGS, budget_config, custom_config, graph_depth, make_workload
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -159,6 +159,28 @@ def test_pack_invariants(cfg_id):
     for n in range(N):
         for i in range(B):
             assert sr[n, i] == order[int(src[n, i]) * B + i]
+
+
+def test_budget_sweep_fold_states_nest():
+    """The draft-budget sweep grows one 3-ary level-order tree: each smaller budget's graph,
+    hidden states and fold decisions are the first nodes of the next one's, so the packed
+    count never falls as branches are added, and every budget keeps the pack invariant."""
+    prev = None
+    for n in BUDGETS:
+        cfg = budget_config(n)
+        w = make_workload(cfg, weights=False)
+        assert list(w.fold_src[1:]) == [(m - 1) // 3 for m in range(1, n)]
+        st = fold_state(w.H, w.fold_src, cfg.tau)
+        B = cfg.block
+        assert st["K"] == B + int(np.sum(~(st["r32"][1:] <= np.float32(cfg.tau))))
+        assert fold_state(w.H, w.fold_src, -1.0)["K"] == cfg.slots
+        if prev is not None:
+            pn, pH, prec, pK = prev
+            np.testing.assert_array_equal(w.H[:pn], pH)
+            np.testing.assert_array_equal(st["recompute"][:pn], prec)
+            assert st["K"] >= pK
+        prev = (n, w.H, st["recompute"], st["K"])
+    assert budget_config(16) == CONFIGS[1].with_(name=budget_config(16).name)
 
 
 def test_pack_edge_cases():
