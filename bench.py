@@ -227,6 +227,8 @@ def main():
     ap.add_argument("--budget-sweep", action="store_true",
                     help="also run the draft-budget sweep: the 7B layer at 1+{3,7,15,31,63} "
                          "branches, dense and folded")
+    ap.add_argument("--gate-sweep", action="store_true",
+                    help="also time specfold_gate alone on hidden states of 34 to 134 MB")
     ap.add_argument("--stack", action="store_true",
                     help="also time the 28-layer stack (config 3) end to end")
     ap.add_argument("--stack-steps", type=int, default=20)
@@ -302,6 +304,9 @@ def main():
     report = {"main": result}
     if args.sweep:
         report["tau_sweep"] = tau_sweep(ev, stream, args.steps, args.warmup)
+    if args.gate_sweep:
+        report["gate_sweep"] = gate_sweep(ev, stream)
+        result["gate_sweep"] = report["gate_sweep"]
     if args.budget_sweep:
         del dl
         torch.cuda.empty_cache()
@@ -344,6 +349,51 @@ def tau_sweep(ev, stream, steps, warmup):
         rows.append(dict(tau=tau, K=K, recompute_fraction=K / cfg.slots, us=ms * 1e3,
                          kernels_us=kern))
         log(f"[bench] sweep tau={tau}: K={K} ({K / cfg.slots:.3f}) {ms * 1e3:.1f} us")
+    return rows
+
+
+def gate_sweep(ev, stream, reps=50):
+    """Streaming rate of the gate kernel alone (specfold_gate: ratios and masks) at the
+    stress layer's row shape (hidden 4096, block 64, bf16, 3-ary tree) with 64 to 256
+    nodes, i.e. 33.6 MB to 134 MB of hidden states (256 x 64 is the largest slot count
+    one call takes).  Algorithmic bytes count every row
+    once (a parent row is also some other branch's own row) plus the 5 output bytes per
+    slot; the rate is also given against the child + parent reads the kernel issues."""
+    import torch
+    from branch_folding_amd import _lib as L
+    d, B = 4096, 64
+    rows = []
+    for n in (64, 128, 256):
+        S = n * B
+        g = torch.Generator(device="cuda").manual_seed(n)
+        H = torch.randn(S * d, device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16)
+        fs = torch.tensor([-1] + [(m - 1) // 3 for m in range(1, n)], dtype=torch.int32,
+                          device="cuda")
+        ratio = torch.empty(S, dtype=torch.float32, device="cuda")
+        rec = torch.empty(S, dtype=torch.uint8, device="cuda")
+        sh = L.Shape(num_nodes=n, block=B, hidden=d, n_q_heads=32, n_kv_heads=4, head_dim=128,
+                     ffn=14336, prefix_len=0, rms_eps=1e-6, dtype=L.SPECFOLD_BF16)
+        for _ in range(3):
+            L.specfold_gate(sh, H, fs, 0.02, ratio, rec, stream)
+        t0, t1 = ev.create(2)
+        torch.cuda.synchronize()
+        ev.record(t0, stream)
+        for _ in range(reps):
+            L.specfold_gate(sh, H, fs, 0.02, ratio, rec, stream)
+        ev.record(t1, stream)
+        torch.cuda.synchronize()
+        us = ev.ms(t0, t1) / reps * 1e3
+        ev.destroy([t0, t1])
+        alg = S * d * 2 + S * 5
+        issued = 2 * S * d * 2 - B * d * 2 + S * 5
+        rows.append(dict(nodes=n, slots=S, hidden_bytes=S * d * 2, us=us,
+                         GBps=alg / (us * 1e-6) / 1e9, hbm_frac=alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         issued_GBps=issued / (us * 1e-6) / 1e9))
+        log(f"[bench] gate sweep {S * d * 2 / 1e6:.0f} MB: {us:.1f} us, "
+            f"{rows[-1]['GBps']:.0f} GB/s ({rows[-1]['hbm_frac'] * 100:.0f}% of HBM peak), "
+            f"{rows[-1]['issued_GBps']:.0f} GB/s of child+parent reads")
+        del H, fs, ratio, rec
+        torch.cuda.empty_cache()
     return rows
 
 
