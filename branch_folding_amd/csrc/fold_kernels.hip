@@ -16,43 +16,22 @@ namespace specfold {
 // input is read once for both.  A row of up to 512 16-byte chunks is fetched in a single
 // round of loads and kept in registers for the normalisation.
 // ------------------------------------------------------------------------------------
-template <typename T>
-__global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
-                                                   const int32_t* __restrict__ fold_src,
-                                                   int N, int B, int d, float tau,
-                                                   float* __restrict__ ratio,
-                                                   uint8_t* __restrict__ recompute,
-                                                   const uint8_t* __restrict__ rec_given,
-                                                   const T* __restrict__ g, float eps,
-                                                   T* __restrict__ An, int ld_an) {
-  const int lane = threadIdx.x & 63;
-  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (slot >= N * B) return;
-  const int n = slot / B, i = slot - n * B;
-  const bool decide = (ratio != nullptr) || (recompute != nullptr);
+constexpr int kGateU = 8;                    // 16-byte chunks per lane held in registers
+
+// Everything of the gate after the rows are loaded: sums of squares over the chunks held in
+// registers (and, for rows longer than 64*kGateU chunks, the rest through tail_c / tail_p),
+// the fold decision, and the normalised row of a slot that computes its own row.
+template <typename T, typename TailC, typename TailP>
+__device__ __forceinline__ void gate_finish(int lane, int slot, int n, int d, bool fs_ok,
+                                            bool has_parent, float tau, float* ratio,
+                                            uint8_t* recompute, const uint8_t* rec_given,
+                                            const T* g, float eps, T* An, int ld_an,
+                                            const uint4 (&vc)[kGateU], const uint4 (&vp)[kGateU],
+                                            const uint4 (&vg)[kGateU], TailC tail_c,
+                                            TailP tail_p) {
   constexpr int VE = Pack16<T>::kElems;
-  constexpr int U = 8;                       // chunks per lane held in registers
+  constexpr int U = kGateU;
   const int chunks = d / VE;
-  const T* c = H + (size_t)slot * d;
-  // The child row's loads go out before the fold source is known, so its lookup and the
-  // row fetch overlap; rows of up to 64*U chunks take one round of loads, and the
-  // normalisation pass reuses the registers instead of re-reading the row.
-  uint4 vc[U], vp[U], vg[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) vc[u] = ld16(c + imin(lane + 64 * u, chunks - 1) * VE);
-  if (An) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) vg[u] = ld16(g + imin(lane + 64 * u, chunks - 1) * VE);
-  }
-  int p = -1;
-  if (n > 0 && fold_src) p = fold_src[n];
-  const bool fs_ok = (n > 0) && (p >= 0) && (p < n);
-  const bool has_parent = decide && fs_ok;
-  const T* q = has_parent ? H + ((size_t)p * B + i) * d : c;
-  if (has_parent) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) vp[u] = ld16(q + imin(lane + 64 * u, chunks - 1) * VE);
-  }
   float sd = 0.f, sp = 0.f, sc = 0.f;
   auto accum = [&](const uint4& xc, const uint4& xp) {
     float fc[VE], fp[VE];
@@ -74,9 +53,8 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
     if (lane + 64 * u < chunks) accum(vc[u], vp[u]);
   // rows longer than 64*U chunks: the remaining chunks stream through in further rounds
   for (int c0 = lane + 64 * U; c0 < chunks; c0 += 64) {
-    const uint4 xc = ld16(c + c0 * VE);
-    const uint4 xp = has_parent ? ld16(q + c0 * VE) : xc;
-    accum(xc, xp);
+    const uint4 xc = tail_c(c0);
+    accum(xc, has_parent ? tail_p(c0) : xc);
   }
   // fold decision (root rows and malformed fold sources always compute their own row)
   bool rec = true;
@@ -107,7 +85,119 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
 #pragma unroll
   for (int u = 0; u < U; ++u)
     if (lane + 64 * u < chunks) norm(vc[u], vg[u], lane + 64 * u);
-  for (int c0 = lane + 64 * U; c0 < chunks; c0 += 64) norm(ld16(c + c0 * VE), ld16(g + c0 * VE), c0);
+  for (int c0 = lane + 64 * U; c0 < chunks; c0 += 64) norm(tail_c(c0), ld16(g + c0 * VE), c0);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
+                                                   const int32_t* __restrict__ fold_src,
+                                                   int N, int B, int d, float tau,
+                                                   float* __restrict__ ratio,
+                                                   uint8_t* __restrict__ recompute,
+                                                   const uint8_t* __restrict__ rec_given,
+                                                   const T* __restrict__ g, float eps,
+                                                   T* __restrict__ An, int ld_an) {
+  const int lane = threadIdx.x & 63;
+  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (slot >= N * B) return;
+  const int n = slot / B, i = slot - n * B;
+  const bool decide = (ratio != nullptr) || (recompute != nullptr);
+  constexpr int VE = Pack16<T>::kElems;
+  constexpr int U = kGateU;
+  const int chunks = d / VE;
+  const T* c = H + (size_t)slot * d;
+  // The child row's loads go out before the fold source is known, so its lookup and the
+  // row fetch overlap; rows of up to 64*U chunks take one round of loads, and the
+  // normalisation pass reuses the registers instead of re-reading the row.
+  uint4 vc[U], vp[U], vg[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) vc[u] = ld16(c + imin(lane + 64 * u, chunks - 1) * VE);
+  if (An) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) vg[u] = ld16(g + imin(lane + 64 * u, chunks - 1) * VE);
+  }
+  int p = -1;
+  if (n > 0 && fold_src) p = fold_src[n];
+  const bool fs_ok = (n > 0) && (p >= 0) && (p < n);
+  const bool has_parent = decide && fs_ok;
+  const T* q = has_parent ? H + ((size_t)p * B + i) * d : c;
+  if (has_parent) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) vp[u] = ld16(q + imin(lane + 64 * u, chunks - 1) * VE);
+  }
+  gate_finish<T>(lane, slot, n, d, fs_ok, has_parent, tau, ratio, recompute, rec_given, g, eps,
+                 An, ld_an, vc, vp, vg, [&](int ch) { return ld16(c + ch * VE); },
+                 [&](int ch) { return ld16(q + ch * VE); });
+}
+
+// ------------------------------------------------------------------------------------
+// Combine of layer l fused with the gate of layer l+1 (a stack of layers: the gate runs at
+// every layer on the residual stream the previous layer hands over).  One wave per slot
+// forms y = h + F[slot_row] for its slot and for the slot's fold source (recomputed, not
+// read back: another wave writes it), rounds both to T as the stored output is rounded,
+// writes its own y, and runs the next layer's gate on the two rows: ratio, mask and the
+// RMS-normalised row for the next QKV GEMM.  Bit-identical to the combine followed by the
+// gate; one launch and one read of y fewer.  Rows of at most 64*kGateU chunks.
+// ------------------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) combine_gate_kernel(
+    const T* __restrict__ h, const T* __restrict__ F, const int32_t* __restrict__ slot_row,
+    const int32_t* __restrict__ count, int cap, T* __restrict__ y,
+    const int32_t* __restrict__ fold_src, int N, int B, int d, float tau,
+    float* __restrict__ ratio, uint8_t* __restrict__ recompute, const T* __restrict__ g,
+    float eps, T* __restrict__ An, int ld_an) {
+  const int lane = threadIdx.x & 63;
+  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (slot >= N * B) return;
+  const int n = slot / B, i = slot - n * B;
+  constexpr int VE = Pack16<T>::kElems;
+  constexpr int U = kGateU;
+  const int chunks = d / VE;
+  const int K = imin(*count, cap);
+  auto row_of = [&](int s) { return imin(imax(slot_row[s], 0), imax(K - 1, 0)); };
+  int p = -1;
+  if (n > 0 && fold_src) p = fold_src[n];
+  const bool fs_ok = (n > 0) && (p >= 0) && (p < n);
+  const int ps = fs_ok ? p * B + i : slot;
+  const T* hc = h + (size_t)slot * d;
+  const T* fc = F + (size_t)row_of(slot) * d;
+  const T* hp = h + (size_t)ps * d;
+  const T* fp = F + (size_t)row_of(ps) * d;
+  uint4 vc[U], vp[U], vg[U], xh[U], xf[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int ch = imin(lane + 64 * u, chunks - 1) * VE;
+    xh[u] = ld16(hc + ch);
+    xf[u] = ld16(fc + ch);
+    vg[u] = ld16(g + ch);
+  }
+  auto add = [&](const uint4& a, const uint4& b) {
+    float fa[VE], fb[VE];
+    unpack16(a, fa, T());
+    unpack16(b, fb, T());
+#pragma unroll
+    for (int e = 0; e < VE; ++e) fa[e] += fb[e];
+    return pack16(fa, T());
+  };
+  T* yc = y + (size_t)slot * d;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    vc[u] = add(xh[u], xf[u]);
+    if (lane + 64 * u < chunks) st16(yc + (lane + 64 * u) * VE, vc[u]);
+  }
+  if (fs_ok) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ch = imin(lane + 64 * u, chunks - 1) * VE;
+      xh[u] = ld16(hp + ch);
+      xf[u] = ld16(fp + ch);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) vp[u] = add(xh[u], xf[u]);
+  }
+  gate_finish<T>(lane, slot, n, d, fs_ok, fs_ok, tau, ratio, recompute, nullptr, g, eps, An,
+                 ld_an, vc, vp, vg, [&](int) { return make_uint4(0, 0, 0, 0); },
+                 [&](int) { return make_uint4(0, 0, 0, 0); });
 }
 
 // ------------------------------------------------------------------------------------
@@ -322,6 +412,28 @@ hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int
                                                  (T*)An, ld_an);
   return hipGetLastError();
 }
+
+bool combine_gate_fits(int d, int elem_bytes) { return d / (16 / elem_bytes) <= 64 * kGateU; }
+
+template <typename T>
+hipError_t launch_combine_gate(const void* h, const void* F, const int32_t* slot_row,
+                               const int32_t* count, int cap, void* y, const int32_t* fold_src,
+                               int N, int B, int d, float tau, float* ratio, uint8_t* recompute,
+                               const void* g, float eps, void* An, int ld_an, hipStream_t st) {
+  if (!combine_gate_fits(d, (int)sizeof(T))) return hipErrorInvalidValue;
+  combine_gate_kernel<T><<<ceil_div(N * B, 4), 256, 0, st>>>(
+      (const T*)h, (const T*)F, slot_row, count, cap, (T*)y, fold_src, N, B, d, tau, ratio,
+      recompute, (const T*)g, eps, (T*)An, ld_an);
+  return hipGetLastError();
+}
+template hipError_t launch_combine_gate<float>(const void*, const void*, const int32_t*,
+                                               const int32_t*, int, void*, const int32_t*, int,
+                                               int, int, float, float*, uint8_t*, const void*,
+                                               float, void*, int, hipStream_t);
+template hipError_t launch_combine_gate<bf16>(const void*, const void*, const int32_t*,
+                                              const int32_t*, int, void*, const int32_t*, int,
+                                              int, int, float, float*, uint8_t*, const void*,
+                                              float, void*, int, hipStream_t);
 
 size_t resolve_pack_lds_bytes(int S) {
   return (size_t)2 * S * sizeof(int32_t) + (((size_t)S + 3) & ~(size_t)3);

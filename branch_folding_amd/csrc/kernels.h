@@ -19,6 +19,16 @@ template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
                        float* ratio, uint8_t* recompute, const uint8_t* rec_given,
                        const void* g, float eps, void* An, int ld_an, hipStream_t st);
+// Combine of one layer fused with the next layer's gate: y = h + F[slot_row] (rounded to
+// T), then the gate of y against its fold source's y with the next layer's tau and RMSNorm
+// gain g, writing ratio / recompute (where non-null) and the normalised rows An of the slots
+// that recompute.  Only for rows of at most 512 16-byte chunks (combine_gate_fits).
+bool combine_gate_fits(int d, int elem_bytes);
+template <typename T>
+hipError_t launch_combine_gate(const void* h, const void* F, const int32_t* slot_row,
+                               const int32_t* count, int cap, void* y, const int32_t* fold_src,
+                               int N, int B, int d, float tau, float* ratio, uint8_t* recompute,
+                               const void* g, float eps, void* An, int ld_an, hipStream_t st);
 size_t resolve_pack_lds_bytes(int S);
 hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,
                                const int32_t* src_in, int N, int B, int mode, int32_t* src_out,

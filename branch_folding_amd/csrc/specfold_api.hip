@@ -154,13 +154,23 @@ Layout layout_of(const specfold_shape* s) {
   return L;
 }
 
+// The next layer's gate, run by this layer's combine (layer stacks): its RMSNorm gain,
+// threshold and fold-state outputs.  Its normalised rows go to this workspace's A2 buffer,
+// where the next layer's QKV GEMM reads them.
+struct NextGate {
+  const void* rms1;
+  float tau;
+  float* ratio;
+  uint8_t* rec;
+};
+
 template <typename T>
 specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights* w,
                           const specfold_kv_view* prefix, const void* hin, void* hout,
                           const int32_t* fold_src, float tau, float* ratio, uint8_t* rec,
                           int32_t* src, int32_t* packed, int32_t* slot_row, int32_t* count,
                           bool state_in, char* ws, const Layout& L, hipStream_t st,
-                          const specfold_probe* probe) {
+                          const specfold_probe* probe, bool gate_done, const NextGate* next) {
   const int N = s->num_nodes, B = s->block, S = N * B, d = s->hidden, ff = s->ffn;
   const int dh = s->head_dim, nq = s->n_q_heads, nkv = s->n_kv_heads;
   const int qkvd = (nq + 2 * nkv) * dh, qd = nq * dh;
@@ -177,10 +187,13 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   // their own row into A1, which shares its buffer with the FFN input A2 (written only after
   // the QKV GEMM has consumed A1).  With a given fold state it writes no mask, and ratios
   // only into a caller's ratio buffer.
+  // With gate_done the previous layer's combine already ran this gate.
   void* A2 = ws + L.a2;
   HIP_CHECK(mark(SPECFOLD_STEP_GATE, true));
-  HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, state_in ? nullptr : rec,
-                           state_in ? rec : nullptr, w->rms1, s->rms_eps, A2, (int)L.ld_d, st));
+  if (!gate_done)
+    HIP_CHECK(launch_gate<T>(hin, fold_src, N, B, d, tau, ratio, state_in ? nullptr : rec,
+                             state_in ? rec : nullptr, w->rms1, s->rms_eps, A2, (int)L.ld_d,
+                             st));
   HIP_CHECK(mark(SPECFOLD_STEP_GATE, false));
   if (!state_in) {
     HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, true));
@@ -249,7 +262,12 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_DOWN, false));
 
   HIP_CHECK(mark(SPECFOLD_STEP_COMBINE, true));
-  HIP_CHECK(launch_combine<T>(Hh, F, slot_row, count, S, S, d, hout, st));
+  if (next)
+    HIP_CHECK(launch_combine_gate<T>(Hh, F, slot_row, count, S, hout, fold_src, N, B, d,
+                                     next->tau, next->ratio, next->rec, next->rms1, s->rms_eps,
+                                     A2, (int)L.ld_d, st));
+  else
+    HIP_CHECK(launch_combine<T>(Hh, F, slot_row, count, S, S, d, hout, st));
   HIP_CHECK(mark(SPECFOLD_STEP_COMBINE, false));
   return ok();
 }
@@ -327,15 +345,29 @@ specfold_status check_workspace(void* workspace, size_t workspace_bytes, size_t 
 
 // Fold-state buffers of one call (caller's where given, else the workspace's) and the
 // launch sequence in the layer's dtype.
+// `next_weights` / `next_state` (layer stacks, fold states made on the device): this layer's
+// combine also runs the next layer's gate into the next layer's fold-state buffers;
+// `gate_done`: the previous layer's combine ran this layer's gate.
 specfold_status launch_layer(const specfold_shape* shape, const specfold_layer_weights* weights,
                              const specfold_kv_view* prefix, const void* hidden_in,
                              void* hidden_out, const int32_t* fold_src, float tau,
                              specfold_fold_state* state, bool state_in, char* ws,
-                             const Layout& L, hipStream_t s, const specfold_probe* probe) {
+                             const Layout& L, hipStream_t s, const specfold_probe* probe,
+                             bool gate_done = false,
+                             const specfold_layer_weights* next_weights = nullptr,
+                             specfold_fold_state* next_state = nullptr) {
   auto pick = [&](auto* user, size_t off) {
     using P = decltype(user);
     return user ? user : (P)(ws + off);
   };
+  NextGate ng{};
+  if (next_weights) {
+    ng.rms1 = next_weights->rms1;
+    ng.tau = tau;
+    ng.ratio = pick(next_state ? next_state->ratio : (float*)nullptr, L.ratio);
+    ng.rec = pick(next_state ? next_state->recompute : (uint8_t*)nullptr, L.rec);
+  }
+  const NextGate* next = next_weights ? &ng : nullptr;
   float* ratio = pick(state ? state->ratio : (float*)nullptr, L.ratio);
   if (state_in && !(state && state->ratio && fold_src)) ratio = nullptr;
   uint8_t* rec = pick(state ? state->recompute : (uint8_t*)nullptr, L.rec);
@@ -345,9 +377,11 @@ specfold_status launch_layer(const specfold_shape* shape, const specfold_layer_w
   int32_t* count = pick(state ? state->packed_count : (int32_t*)nullptr, L.count);
   if (shape->dtype == SPECFOLD_BF16)
     return run_layer<bf16>(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, ratio,
-                           rec, src, packed, slot_row, count, state_in, ws, L, s, probe);
+                           rec, src, packed, slot_row, count, state_in, ws, L, s, probe,
+                           gate_done, next);
   return run_layer<float>(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, ratio,
-                          rec, src, packed, slot_row, count, state_in, ws, L, s, probe);
+                          rec, src, packed, slot_row, count, state_in, ws, L, s, probe,
+                          gate_done, next);
 }
 
 }  // namespace
@@ -505,12 +539,17 @@ specfold_status specfold_stack_forward(const specfold_shape* shape, int32_t num_
   }
   // layer l writes hidden_out when (num_layers - 1 - l) is even, else the workspace's
   // spare hidden buffer, so consecutive layers never alias and the last writes hidden_out
+  // With fold states made on the device, layer l's combine also runs layer l+1's gate on the
+  // output it writes (same results, one launch and one pass over the hidden states fewer).
+  const bool fuse = !state_in && combine_gate_fits(shape->hidden, (int)elem_bytes(shape));
   const void* x = hidden_in;
   for (int l = 0; l < num_layers; ++l) {
     void* y = ((num_layers - 1 - l) % 2 == 0) ? hidden_out : (void*)pong;
+    const bool fuse_next = fuse && l + 1 < num_layers;
     st = launch_layer(shape, &weights[l], prefix ? &prefix[l] : nullptr, x, y, fold_src, tau,
                       states ? &states[l] : nullptr, state_in, ws, L, (hipStream_t)stream,
-                      nullptr);
+                      nullptr, fuse && l > 0, fuse_next ? &weights[l + 1] : nullptr,
+                      fuse_next && states ? &states[l + 1] : nullptr);
     if (st != SPECFOLD_OK) return st;
     x = y;
   }
