@@ -47,6 +47,7 @@ import numpy as np
 __all__ = [
     "gate", "resolve", "pack", "rms_norm", "silu", "layer", "serial_layer",
     "bruteforce_provenance", "FoldState", "fold_state", "round_to_bf16", "stack",
+    "lm_head_argmax",
 ]
 
 
@@ -379,3 +380,39 @@ def stack(layer_params: Iterable[Tuple[Dict[str, np.ndarray], np.ndarray, np.nda
             y = round_to_bf16(y).astype(dtype)
         x = y
     return dict(y=x, states=got_states, K=Ks, inputs=inputs)
+
+
+# ---------------------------------------------------------------------------------------
+# (10) After the last layer: LM-head logits of the final layer's packed rows and every
+#      branch's predicted token at every position (the verify step compares the branches'
+#      predictions; the acceptance rule itself is not on the pages).  Reading: a folded
+#      slot takes the prediction of its resolved source, as it takes the source's FFN
+#      output ([SF] reuse path); with every slot packed (tau < 0) each slot gets its own.
+# ---------------------------------------------------------------------------------------
+def lm_head_argmax(y: np.ndarray, g_final: np.ndarray, w_lm: np.ndarray, state: FoldState,
+                   eps: float, rows: Optional[Sequence[int]] = None,
+                   dtype=np.float64) -> Dict[str, np.ndarray]:
+    """y [N, B, d] final hidden states, g_final [d] final RMSNorm gain, w_lm [V, d].
+
+    For packed row k (slot packed_slot[k]): a_k = RMSNorm(y[slot]) * g_final, logits
+    a_k . w_lm[v] for every v, row_token[k] = the first index of the maximum logit,
+    row_logit[k] = that maximum.  token[n, i] = row_token[slot_row[n, i]].
+    `rows` limits the evaluation to some packed rows (their row_token / row_logit /
+    logits entries; token is then only returned for the slots whose row was evaluated,
+    -1 elsewhere)."""
+    N, B, d = y.shape
+    ps = np.asarray(state["packed_slot"])
+    K = int(state["K"])
+    ks = np.arange(K) if rows is None else np.asarray(sorted(set(int(r) for r in rows)))
+    flat = y.reshape(N * B, d).astype(dtype)
+    a = rms_norm(flat[ps[ks]], np.asarray(g_final, dtype=dtype), eps)
+    logits = a @ np.asarray(w_lm, dtype=dtype).T
+    best = np.argmax(logits, axis=1)              # first index of the maximum
+    row_token = np.full(K, -1, dtype=np.int64)
+    row_logit = np.full(K, np.nan, dtype=dtype)
+    row_token[ks] = best
+    row_logit[ks] = logits[np.arange(len(ks)), best]
+    sr = np.asarray(state["slot_row"])
+    token = row_token[sr]
+    return dict(row_token=row_token, row_logit=row_logit, token=token, logits=logits,
+                rows=ks)

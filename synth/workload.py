@@ -33,6 +33,7 @@ __all__ = [
     "Config", "CONFIGS", "Workload", "make_workload", "make_layer_weights",
     "round_bf16", "bf16_bits", "draft_graph", "hidden_states", "prefix_cache",
     "custom_config", "budget_config", "BUDGETS", "graph_depth", "layer_weights_of",
+    "lm_head_weights", "VOCAB_7B",
     "layer_cache_of", "iter_layers",
 ]
 
@@ -104,6 +105,22 @@ def budget_config(num_nodes: int) -> Config:
     """The 7B-shaped layer with `num_nodes` nodes (root + children); same seed, weights and
     prefix as the 1 + 15 layer, so only the draft graph and the hidden states change."""
     return CONFIGS[1].with_(num_nodes=num_nodes, name=f"7b-layer-1+{num_nodes - 1}")
+
+
+# Vocabulary of the 7B-shaped model family (Qwen2-style tokenizer size) for the LM head
+# that follows the layer stack.
+VOCAB_7B = 152064
+
+
+def lm_head_weights(cfg: Config, vocab: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Final RMSNorm gain (ones, like the layers' gains) and LM-head weight [vocab, d]
+    ~ N(0, weight_std^2), rounded to the configuration's storage format.  Seeded from the
+    configuration's seed on a stream of its own, so the layer inputs do not change."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 0x1B, vocab])))
+    w = rng.standard_normal((vocab, cfg.hidden), dtype=np.float32)
+    w *= np.float32(cfg.weight_std)
+    g = np.ones(cfg.hidden, dtype=np.float32)
+    return _storage(cfg, g), _storage(cfg, w)
 
 
 def custom_config(**kw) -> Config:
