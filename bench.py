@@ -229,6 +229,9 @@ def main():
                          "branches, dense and folded")
     ap.add_argument("--gate-sweep", action="store_true",
                     help="also time specfold_gate alone on hidden states of 34 to 134 MB")
+    ap.add_argument("--lm-head", action="store_true",
+                    help="also time the LM head + per-branch argmax (vocab 152064) on the 7B "
+                         "layer's packed rows")
     ap.add_argument("--stack", action="store_true",
                     help="also time the 28-layer stack (config 3) end to end")
     ap.add_argument("--stack-steps", type=int, default=20)
@@ -307,6 +310,9 @@ def main():
     if args.gate_sweep:
         report["gate_sweep"] = gate_sweep(ev, stream)
         result["gate_sweep"] = report["gate_sweep"]
+    if args.lm_head:
+        report["lm_head"] = lm_head_bench(cfg, w, dl, tau, ev, stream, args.steps, args.warmup)
+        result["lm_head"] = report["lm_head"]
     if args.budget_sweep:
         del dl
         torch.cuda.empty_cache()
@@ -350,6 +356,56 @@ def tau_sweep(ev, stream, steps, warmup):
                          kernels_us=kern))
         log(f"[bench] sweep tau={tau}: K={K} ({K / cfg.slots:.3f}) {ms * 1e3:.1f} us")
     return rows
+
+
+def lm_head_bench(cfg, w, dl, tau, ev, stream, steps, warmup):
+    """The step after the last layer: logits of the packed rows against a [152064, d] LM
+    head and every branch's argmax token, with the fold state the layer just produced
+    (specfold_lm_head_argmax).  Algorithmic bytes: the head once, the packed rows, the
+    hidden states' normalisation pass and the token outputs."""
+    import torch
+    from branch_folding_amd import _lib as L
+    from branch_folding_amd.runner import shape_of
+    from synth import VOCAB_7B, lm_head_weights
+    g, wl = lm_head_weights(cfg, VOCAB_7B)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    gd = torch.from_numpy(g).to(dt).cuda()
+    wd = torch.from_numpy(wl).to(dt).cuda()
+    del wl
+    dl.forward(tau, stream=stream)
+    torch.cuda.synchronize()
+    st = dl.state                      # the layer's fold state, on the device
+    hid = dl.out                       # the layer's output stands in for the final hidden states
+    sh = shape_of(cfg)
+    S, K, d = cfg.slots, dl.fold_state()["K"], cfg.hidden
+    nb = L.specfold_lm_head_workspace_bytes(sh, VOCAB_7B)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    rt = torch.empty(S, dtype=torch.int32, device="cuda")
+    rl = torch.empty(S, dtype=torch.float32, device="cuda")
+    tok = torch.empty(S, dtype=torch.int32, device="cuda")
+    call = lambda: L.specfold_lm_head_argmax(sh, VOCAB_7B, gd, wd, hid, st["packed_slot"],
+                                             st["slot_row"], st["packed_count"], rt, rl, tok,
+                                             ws, nb, stream)
+    for _ in range(warmup):
+        call()
+    t0, t1 = ev.create(2)
+    torch.cuda.synchronize()
+    ev.record(t0, stream)
+    for _ in range(steps):
+        call()
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    us = ev.ms(t0, t1) / steps * 1e3
+    ev.destroy([t0, t1])
+    eb = 2 if cfg.dtype == "bf16" else 4
+    alg = VOCAB_7B * d * eb + S * d * eb * 2 + K * d * eb + S * 4
+    res = dict(vocab=VOCAB_7B, packed_rows=K, us=us, GBps=alg / (us * 1e-6) / 1e9,
+               hbm_frac=alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=alg)
+    log(f"[bench] LM head (vocab {VOCAB_7B}, {K} packed rows, {S} slots): {us:.1f} us, "
+        f"{res['GBps']:.0f} GB/s ({res['hbm_frac'] * 100:.0f}% of HBM peak)")
+    del wd, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def gate_sweep(ev, stream, reps=50):

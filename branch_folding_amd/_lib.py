@@ -87,6 +87,9 @@ _SIGS = {
                                               ctypes.POINTER(KVView), _P, _P, _P,
                                               ctypes.c_float, ctypes.POINTER(FoldState),
                                               ctypes.c_uint32, _P, ctypes.c_size_t, _P]),
+    "specfold_lm_head_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32]),
+    "specfold_lm_head_argmax": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_int32, _P, _P, _P,
+                                               _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "specfold_last_error": (ctypes.c_char_p, []),
     "specfold_version": (ctypes.c_int32, []),
 }
@@ -162,6 +165,23 @@ def specfold_pack(shape: Shape, recompute, src_node, packed_slot, slot_row, pack
     _check(lib().specfold_pack(ctypes.byref(shape), _ptr(recompute), _ptr(src_node),
                                _ptr(packed_slot), _ptr(slot_row), _ptr(packed_count),
                                _stream(stream)))
+
+
+def specfold_lm_head_workspace_bytes(shape: Shape, vocab: int) -> int:
+    n = int(lib().specfold_lm_head_workspace_bytes(ctypes.byref(shape), int(vocab)))
+    if n == 0:
+        raise SpecFoldError(SPECFOLD_ERR_INVALID_ARGUMENT, last_error())
+    return n
+
+
+def specfold_lm_head_argmax(shape: Shape, vocab: int, rms_final, w_lm, hidden, packed_slot,
+                            slot_row, packed_count, row_token, row_logit, token, workspace,
+                            workspace_bytes: int, stream=None):
+    _check(lib().specfold_lm_head_argmax(ctypes.byref(shape), int(vocab), _ptr(rms_final),
+                                         _ptr(w_lm), _ptr(hidden), _ptr(packed_slot),
+                                         _ptr(slot_row), _ptr(packed_count), _ptr(row_token),
+                                         _ptr(row_logit), _ptr(token), _ptr(workspace),
+                                         int(workspace_bytes), _stream(stream)))
 
 
 def specfold_layer_workspace_bytes(shape: Shape) -> int:

@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
   const int mb = ceil_div(M, kGemmBM), nt = ceil_div(p.N, BN);
   const int kiters = p.Kd / G::BK;
   const int tiles = mb * nt;
-  const int split = gemm_split(tiles, kiters);
+  const int split = EPI == kEpiArgmax ? 1 : gemm_split(tiles, kiters);
   const int units = tiles * split;
   const int per_xcd = ceil_div(units, 8);
 
@@ -204,7 +204,41 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
     }
 
     // epilogue: lane holds rows (g4*4 + r) and column l16 of every 16x16 tile
-    if (split == 1 && EPI != kEpiPartial) {
+    if (EPI == kEpiArgmax) {
+      // per row: the largest of this wave's 64 columns and its first column index (columns
+      // ascend with j within a lane; across the 16 lanes of a row ties go to the lower one)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float bv = -__builtin_inff();
+          int bi = 0x7fffffff;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wn * 64 + j * 16 + l16;
+            const float v = acc[i][j][r];
+            if (col < p.N && v > bv) {
+              bv = v;
+              bi = col;
+            }
+          }
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) {
+            const float ov = __shfl_xor(bv, o, 16);
+            const int oi = __shfl_xor(bi, o, 16);
+            if (ov > bv || (ov == bv && oi < bi)) {
+              bv = ov;
+              bi = oi;
+            }
+          }
+          const int row = m0 + wm * 64 + i * 16 + g4 * 4 + r;
+          if (l16 == 0 && row < M) {
+            const size_t at = (size_t)row * p.arg_ld + ntile * WN + wn;
+            p.arg_val[at] = bv;
+            p.arg_idx[at] = bi;
+          }
+        }
+    } else if (split == 1 && EPI != kEpiPartial) {
       T* C = (T*)p.C;
       if (EPI == kEpiSwiGLU) {
 #pragma unroll
@@ -545,7 +579,7 @@ template <typename T, int EPI, int BN>
 static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st) {
   gemm_kernel<T, EPI, BN><<<num_cu, BN * 2, 0, st>>>(p);
   // the reduction only runs when some row count could make the device choose split > 1
-  if (EPI != kEpiPartial &&
+  if (EPI != kEpiPartial && EPI != kEpiArgmax &&
       gemm_split(ceil_div(p.N, BN), p.Kd / (kGemmBKBytes / (int)sizeof(T))) > 1) {
     const int Nout = (EPI == kEpiSwiGLU) ? p.ff : p.N;
     const long total = (long)p.m_cap * (Nout / 4);
@@ -572,6 +606,7 @@ hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st)
     case kEpiResidual: return launch_gemm_epi<T, kEpiResidual>(p, num_cu, st);
     case kEpiSwiGLU: return launch_gemm_epi<T, kEpiSwiGLU>(p, num_cu, st);
     case kEpiPartial: return launch_gemm_epi<T, kEpiPartial>(p, num_cu, st);
+    case kEpiArgmax: return launch_gemm_epi<T, kEpiArgmax>(p, num_cu, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -44,7 +44,9 @@ hipError_t launch_combine(const void* h, const void* F, const int32_t* slot_row,
 // ---------------------------------------------------------------------------------------
 // kEpiPartial: always write fp32 partial sums (plane s of p.partial), even without split-K;
 // a row-wise finishing kernel applies the epilogue.
-enum GemmEpi { kEpiStore = 0, kEpiResidual = 1, kEpiSwiGLU = 2, kEpiPartial = 3 };
+// kEpiArgmax: no C; for every row, the maximum over each wave's 64 columns and its first
+// column index go to arg_val / arg_idx [row][arg_ld] (never split over K).
+enum GemmEpi { kEpiStore = 0, kEpiResidual = 1, kEpiSwiGLU = 2, kEpiPartial = 3, kEpiArgmax = 4 };
 
 struct GemmParams {
   const void* A;
@@ -65,6 +67,10 @@ struct GemmParams {
   // [0, a_rows_cap)); nullptr = row m
   const int32_t* a_rows;
   int a_rows_cap;
+  // kEpiArgmax outputs: [m_cap][arg_ld] partial maxima and their column indices
+  float* arg_val;
+  int32_t* arg_idx;
+  int arg_ld;
 };
 
 constexpr int kGemmBM = 128;
@@ -105,6 +111,31 @@ hipError_t launch_oproj_finish(const float* partial, int split, const void* H, v
 size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always = false);
 // N-tile width used for a GEMM with N output columns (256 for wide, 128 otherwise)
 int gemm_tile_n(int N);
+
+// Partials per row of a kEpiArgmax GEMM with N columns (two waves along each 128-column
+// tile).
+inline int gemm_argmax_partials(int N) { return ceil_div(N, 128) * 2; }
+
+// LM head + per-branch argmax over the final hidden states (see lm_head.hip).
+struct LmHeadParams {
+  const void* hidden;      // [S, d]
+  const void* rms;         // [d]
+  const void* w;           // [V, d]
+  const int32_t* packed_slot;
+  const int32_t* slot_row;
+  const int32_t* count;
+  int N, B, d, V;
+  float eps;
+  void* An;                // workspace: [S, ld_an] normalised rows
+  int ld_an;
+  float* arg_val;          // workspace: [S, P] partial maxima
+  int32_t* arg_idx;        // workspace: [S, P]
+  int32_t* row_token;      // [S] (first K used)
+  float* row_logit;        // [S] or nullptr
+  int32_t* token;          // [S]
+};
+template <typename T>
+hipError_t launch_lm_head(const LmHeadParams& q, int num_cu, hipStream_t st);
 
 // ---------------------------------------------------------------------------------------
 // Attention.  Prefix phase: online-softmax partials of every packed row's queries over the

@@ -1,0 +1,89 @@
+// LM head after the last folded layer: the logits of the final layer's packed rows and
+// every branch's predicted token at every position (the verify step compares the
+// branches' predictions; a folded position takes its resolved source's prediction, as it
+// takes the source's FFN output -- SpecFold explainer, the reuse path).
+//
+//   1. gate_kernel in its normalise-only mode: An[s] = RMSNorm(hidden[s]) * g for all slots;
+//   2. gemm_kernel<kEpiArgmax>: logits of the packed rows (gathered from An through
+//      packed_slot) against the [V, d] head, never stored: each wave keeps, per row, the
+//      largest of its 64 columns and the first such column;
+//   3. argmax_finish_kernel: one wave per packed row reduces those partials (first index
+//      of the maximum);
+//   4. token_gather_kernel: token[s] = row_token[slot_row[s]].
+#include "common.h"
+#include "kernels.h"
+
+namespace specfold {
+
+__global__ void __launch_bounds__(256) argmax_finish_kernel(const float* __restrict__ val,
+                                                            const int32_t* __restrict__ idx,
+                                                            int P, const int32_t* __restrict__ count,
+                                                            int cap, int V,
+                                                            int32_t* __restrict__ row_token,
+                                                            float* __restrict__ row_logit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = imin(*count, cap);
+  for (int k = blockIdx.x * 4 + wave; k < K; k += gridDim.x * 4) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+    const float* v = val + (size_t)k * P;
+    const int32_t* x = idx + (size_t)k * P;
+    for (int j = lane; j < P; j += 64) {
+      const float a = v[j];
+      const int b = x[j];
+      if (a > bv || (a == bv && b < bi)) {
+        bv = a;
+        bi = b;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      row_token[k] = (bi >= 0 && bi < V) ? bi : -1;   // -1: no finite logit in the row
+      if (row_logit) row_logit[k] = bv;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) token_gather_kernel(const int32_t* __restrict__ row_token,
+                                                           const int32_t* __restrict__ slot_row,
+                                                           const int32_t* __restrict__ count,
+                                                           int cap, int S,
+                                                           int32_t* __restrict__ token) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= S) return;
+  const int K = imin(*count, cap);
+  token[s] = K > 0 ? row_token[imin(imax(slot_row[s], 0), K - 1)] : -1;
+}
+
+template <typename T>
+hipError_t launch_lm_head(const LmHeadParams& q, int num_cu, hipStream_t st) {
+  const int S = q.N * q.B;
+  hipError_t e = launch_gate<T>(q.hidden, nullptr, q.N, q.B, q.d, 0.f, nullptr, nullptr, nullptr,
+                                q.rms, q.eps, q.An, q.ld_an, st);
+  if (e != hipSuccess) return e;
+  GemmParams gp{};
+  gp.A = q.An; gp.lda = q.ld_an; gp.a_rows = q.packed_slot; gp.a_rows_cap = S;
+  gp.W = q.w; gp.ldw = q.d; gp.m_dev = q.count; gp.m_cap = S; gp.N = q.V; gp.Kd = q.d;
+  gp.arg_val = q.arg_val; gp.arg_idx = q.arg_idx; gp.arg_ld = gemm_argmax_partials(q.V);
+  if ((e = launch_gemm<T>(gp, kEpiArgmax, num_cu, st)) != hipSuccess) return e;
+  const int fgrid = ceil_div(S, 4) < 4 * num_cu ? ceil_div(S, 4) : 4 * num_cu;
+  argmax_finish_kernel<<<fgrid, 256, 0, st>>>(q.arg_val, q.arg_idx, gp.arg_ld, q.count, S, q.V,
+                                               q.row_token, q.row_logit);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  token_gather_kernel<<<ceil_div(S, 256), 256, 0, st>>>(q.row_token, q.slot_row, q.count, S, S,
+                                                        q.token);
+  return hipGetLastError();
+}
+
+template hipError_t launch_lm_head<float>(const LmHeadParams&, int, hipStream_t);
+template hipError_t launch_lm_head<bf16>(const LmHeadParams&, int, hipStream_t);
+
+}  // namespace specfold

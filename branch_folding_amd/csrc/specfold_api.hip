@@ -164,6 +164,22 @@ struct NextGate {
   uint8_t* rec;
 };
 
+// Workspace of the LM head: normalised rows, then the argmax partials.
+struct LmLayout {
+  size_t an, val, idx, total, ld_an;
+};
+LmLayout lm_layout(const specfold_shape* s, int vocab) {
+  const size_t S = (size_t)s->num_nodes * s->block, eb = elem_bytes(s);
+  const size_t P = (size_t)gemm_argmax_partials(vocab);
+  LmLayout L{};
+  L.ld_an = padded_ld(s->hidden, eb);
+  L.an = 0;
+  L.val = align256(S * L.ld_an * eb);
+  L.idx = align256(L.val + S * P * 4);
+  L.total = align256(L.idx + S * P * 4);
+  return L;
+}
+
 template <typename T>
 specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights* w,
                           const specfold_kv_view* prefix, const void* hin, void* hout,
@@ -553,6 +569,49 @@ specfold_status specfold_stack_forward(const specfold_shape* shape, int32_t num_
     if (st != SPECFOLD_OK) return st;
     x = y;
   }
+  return ok();
+}
+
+size_t specfold_lm_head_workspace_bytes(const specfold_shape* shape, int32_t vocab) {
+  if (check_shape(shape, false) != SPECFOLD_OK) return 0;
+  if (vocab < 1) {
+    fail(SPECFOLD_ERR_INVALID_ARGUMENT, "vocab must be >= 1");
+    return 0;
+  }
+  g_last_error.clear();
+  return lm_layout(shape, vocab).total;
+}
+
+specfold_status specfold_lm_head_argmax(const specfold_shape* shape, int32_t vocab,
+                                        const void* rms_final, const void* w_lm,
+                                        const void* hidden, const int32_t* packed_slot,
+                                        const int32_t* slot_row, const int32_t* packed_count,
+                                        int32_t* row_token, float* row_logit, int32_t* token,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  specfold_status st = check_shape(shape, false);
+  if (st != SPECFOLD_OK) return st;
+  if (vocab < 1) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "vocab must be >= 1");
+  if (!rms_final || !w_lm || !hidden || !packed_slot || !slot_row || !packed_count ||
+      !row_token || !token)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
+                "rms_final, w_lm, hidden, packed_slot, slot_row, packed_count, row_token and "
+                "token are required");
+  if (!aligned16(rms_final) || !aligned16(w_lm) || !aligned16(hidden))
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "rms_final, w_lm and hidden must be 16-byte aligned");
+  const LmLayout L = lm_layout(shape, vocab);
+  if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SPECFOLD_OK) return st;
+  char* ws = (char*)workspace;
+  LmHeadParams q{};
+  q.hidden = hidden; q.rms = rms_final; q.w = w_lm; q.packed_slot = packed_slot;
+  q.slot_row = slot_row; q.count = packed_count; q.N = shape->num_nodes; q.B = shape->block;
+  q.d = shape->hidden; q.V = vocab; q.eps = shape->rms_eps; q.An = ws + L.an;
+  q.ld_an = (int)L.ld_an; q.arg_val = (float*)(ws + L.val); q.arg_idx = (int32_t*)(ws + L.idx);
+  q.row_token = row_token; q.row_logit = row_logit; q.token = token;
+  (void)hipGetLastError();
+  if (shape->dtype == SPECFOLD_BF16)
+    HIP_CHECK(launch_lm_head<bf16>(q, num_cus(), (hipStream_t)stream));
+  else
+    HIP_CHECK(launch_lm_head<float>(q, num_cus(), (hipStream_t)stream));
   return ok();
 }
 

@@ -277,6 +277,35 @@ typedef enum specfold_tensor {
  * stride in elements is stored to *ld_elems when ld_elems is non-NULL. */
 size_t specfold_workspace_offset(const specfold_shape* shape, int32_t which, int64_t* ld_elems);
 
+/* Bytes of device workspace specfold_lm_head_argmax needs (0 if the shape is invalid). */
+size_t specfold_lm_head_workspace_bytes(const specfold_shape* shape, int32_t vocab);
+
+/* LM head after the last folded layer, and every branch's predicted token (the verify
+ * step compares the branches' predictions; SpecFold explainer, the reuse path: a folded
+ * position takes its resolved source's result, here its prediction).
+ *   For packed row k < K = *packed_count (slot packed_slot[k]):
+ *     a_k = hidden[slot] / sqrt(mean(hidden[slot]^2) + rms_eps) * rms_final
+ *     logit[k, v] = a_k . w_lm[v]                      (fp32 accumulation)
+ *     row_token[k] = the first v of the largest logit;  row_logit[k] = that logit
+ *   token[n, i] = row_token[slot_row[n, i]] for every slot.
+ * The fold state (packed_slot, slot_row, packed_count) is the last layer's, as produced
+ * by specfold_layer_forward / specfold_stack_forward; with every slot packed (tau < 0)
+ * every slot gets its own prediction.  The logits are never stored.
+ *   shape:       num_nodes, block, hidden, rms_eps, dtype are used (hidden % 128 == 0)
+ *   rms_final:   [d] dtype;  w_lm: [vocab, d] dtype, row-major;  hidden: [N, B, d] dtype
+ *   row_token:   int32 [N*B] capacity, first K written (-1 if a row has no finite logit)
+ *   row_logit:   float [N*B] capacity or NULL;  token: int32 [N, B]
+ *   workspace:   specfold_lm_head_workspace_bytes(shape, vocab) bytes, 256-byte aligned
+ * Errors: SPECFOLD_ERR_INVALID_ARGUMENT for NULL / misaligned pointers or vocab < 1,
+ * SPECFOLD_ERR_UNSUPPORTED for unsupported shapes, SPECFOLD_ERR_WORKSPACE for a short
+ * workspace, SPECFOLD_ERR_HIP if a launch fails. */
+specfold_status specfold_lm_head_argmax(const specfold_shape* shape, int32_t vocab,
+                                        const void* rms_final, const void* w_lm,
+                                        const void* hidden, const int32_t* packed_slot,
+                                        const int32_t* slot_row, const int32_t* packed_count,
+                                        int32_t* row_token, float* row_logit, int32_t* token,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message of the last failed call on this host thread ("" if none). */
 const char* specfold_last_error(void);
 

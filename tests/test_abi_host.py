@@ -174,3 +174,31 @@ def test_stack_argument_errors():
     # no prefix views needed without a prefix
     sh0 = shape_of(CONFIGS[3], prefix_len=0)
     assert _stack(sh0, prefix=None, workspace_bytes=0)[0] == L.SPECFOLD_ERR_WORKSPACE
+
+
+def test_lm_head_workspace_and_argument_errors():
+    sh = shape_of(CONFIGS[1])
+    V = 152064
+    ws = L.specfold_lm_head_workspace_bytes(sh, V)
+    S, d = CONFIGS[1].slots, CONFIGS[1].hidden
+    P = -(-V // 128) * 2
+    assert ws >= S * (d + 64) * 2 + 2 * S * P * 4
+    assert L.lib().specfold_lm_head_workspace_bytes(ctypes.byref(sh), 0) == 0
+    args = [FAKE] * 9
+    # every case below fails in the host-side checks, before anything is enqueued
+    def call(vocab=V, ptrs=None, wsb=ws, shape=sh):
+        p = list(args if ptrs is None else ptrs)
+        assert len(p) == 9
+        return L.lib().specfold_lm_head_argmax(ctypes.byref(shape), vocab, *p, FAKE, wsb, None)
+    assert call(vocab=0) == L.SPECFOLD_ERR_INVALID_ARGUMENT
+    for i in (0, 1, 2, 3, 4, 5, 6, 8):        # every pointer but row_logit is required
+        bad = list(args)
+        bad[i] = None
+        assert call(ptrs=bad) == L.SPECFOLD_ERR_INVALID_ARGUMENT, i
+    bad = list(args)
+    bad[1] = FAKE + 8                         # misaligned weight
+    assert call(ptrs=bad) == L.SPECFOLD_ERR_INVALID_ARGUMENT
+    assert call(wsb=ws - 1) == L.SPECFOLD_ERR_WORKSPACE
+    odd = shape_of(CONFIGS[1])
+    odd.hidden = 3600
+    assert call(shape=odd) == L.SPECFOLD_ERR_UNSUPPORTED
