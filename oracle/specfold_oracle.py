@@ -175,7 +175,8 @@ def _softmax(z: np.ndarray) -> np.ndarray:
 def layer(weights: Dict[str, np.ndarray], H: np.ndarray, fold_src: np.ndarray, tau: float,
           prefix_k: np.ndarray, prefix_v: np.ndarray, *, n_q: int, n_kv: int,
           eps: float = 1e-6, dtype=np.float64, state: Optional[FoldState] = None,
-          slots: Optional[Iterable[Tuple[int, int]]] = None) -> Dict[str, np.ndarray]:
+          slots: Optional[Iterable[Tuple[int, int]]] = None,
+          attn: str = "correct") -> Dict[str, np.ndarray]:
     """One folded verify layer over the parent and all draft branches.
 
     weights: rms1 [d], w_qkv [(n_q+2n_kv)dh, d] (Q heads | K heads | V heads), w_o
@@ -185,6 +186,10 @@ def layer(weights: Dict[str, np.ndarray], H: np.ndarray, fold_src: np.ndarray, t
     instead of running the gate -- e.g. one taken from ``fold_state`` on other inputs.
     slots: evaluate only these (n, i) outputs (and what they depend on); other entries
     of the returned per-slot arrays are NaN.
+    attn: "correct" (a folded slot's attention runs against its own branch's keys and
+    values -- the correction of [SF]'s implementation memo) or "reuse" (a folded slot
+    takes its resolved source's attention output as it is, so only the packed rows need
+    the O projection; then y[n, i] - y[src, i] = H[n, i] - H[src, i] exactly).
 
     Steps ([SF] paragraphs on reuse, packing and the implementation memo; [SFa]):
       1-3. gate, provenance, packing;
@@ -244,6 +249,14 @@ def layer(weights: Dict[str, np.ndarray], H: np.ndarray, fold_src: np.ndarray, t
             q = Qp[rows[pos], h]                                          # [|pos|, dh]
             w = _softmax((q @ keys.T) * scale)
             o[n, pos, h] = w @ vals
+
+    if attn == "reuse":
+        for n in range(N):
+            for i in range(B):
+                if need_attn[n, i] and src[n, i] != n:
+                    o[n, i] = o[src[n, i], i]
+    elif attn != "correct":
+        raise ValueError(f"attn must be 'correct' or 'reuse', not {attn!r}")
 
     # (6) O projection + residual for every evaluated slot
     wo = weights["w_o"].astype(dt)

@@ -165,3 +165,38 @@ def test_online_softmax_merge_identity():
     L = sum(2.0 ** (x - M) for x in lse) + np.sum(2.0 ** (s2[P:] - M))
     O = sum(2.0 ** (x - M) * o for x, o in zip(lse, outs)) + (2.0 ** (s2[P:] - M)) @ vals[P:]
     np.testing.assert_allclose(O / L, ref, rtol=1e-12, atol=1e-13)
+
+
+def _layer_of(cfg, w, tau, attn, state=None):
+    pk, pv = w.prefix_kv(0)
+    return layer(w.weights[0], w.H, w.fold_src, tau, pk, pv, n_q=cfg.n_q, n_kv=cfg.n_kv,
+                 eps=cfg.rms_eps, attn=attn, state=state)
+
+
+def test_reuse_mode_closed_form_and_limits():
+    """REUSE variant: a folded slot takes its resolved source's attention output, so its
+    output differs from the source's by exactly its own input delta; with nothing folded
+    (tau < 0) and with everything folded onto the root (tau = inf, where every branch's
+    block keys are the root's rows) it equals the corrected layer; in between it does not."""
+    cfg = custom_config(name="reuse", num_nodes=7, block=6, hidden=64, n_q=4, n_kv=2,
+                        head_dim=64, ffn=128, prefix=9, graph="dag", reveal=(1, 2), seed=51)
+    w = make_workload(cfg)
+    st = fold_state(w.H, w.fold_src, 0.3)
+    assert 0 < int((~st["recompute"]).sum())
+    r = _layer_of(cfg, w, 0.3, "reuse", state=st)
+    src = st["src"]
+    for n in range(cfg.num_nodes):
+        for i in range(cfg.block):
+            m = src[n, i]
+            if m != n:
+                delta = w.H[n, i].astype(np.float64) - w.H[m, i].astype(np.float64)
+                np.testing.assert_allclose(r["y"][n, i] - r["y"][m, i], delta, rtol=0,
+                                           atol=1e-12)
+    c = _layer_of(cfg, w, 0.3, "correct", state=st)
+    assert np.max(np.abs(r["y"] - c["y"])) > 1e-6          # the correction matters here
+    for tau in (-1.0, math.inf):
+        a = _layer_of(cfg, w, tau, "reuse")
+        b = _layer_of(cfg, w, tau, "correct")
+        np.testing.assert_allclose(a["y"], b["y"], rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        _layer_of(cfg, w, 0.3, "other")
