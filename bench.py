@@ -151,6 +151,23 @@ def time_layer(dl, tau, steps, warmup, ev, stream, probe_step=None):
     return total / steps, per
 
 
+def time_reuse(dl, tau, steps, warmup, ev, stream):
+    """ms per step of the layer with the REUSE attention variant."""
+    import torch
+    for _ in range(warmup):
+        dl.forward(tau, stream=stream, reuse=True)
+    t0, t1 = ev.create(2)
+    torch.cuda.synchronize()
+    ev.record(t0, stream)
+    for _ in range(steps):
+        dl.forward(tau, stream=stream, reuse=True)
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    ev.destroy([t0, t1])
+    return ms
+
+
 def kernel_breakdown(dl, tau, reps, ev, stream):
     from branch_folding_amd import _lib as L
     out = {}
@@ -229,6 +246,9 @@ def main():
                          "branches, dense and folded")
     ap.add_argument("--gate-sweep", action="store_true",
                     help="also time specfold_gate alone on hidden states of 34 to 134 MB")
+    ap.add_argument("--reuse", action="store_true",
+                    help="also time the layer with the REUSE attention variant (folded slots "
+                         "take their source's attention output) and report the correction cost")
     ap.add_argument("--lm-head", action="store_true",
                     help="also time the LM head + per-branch argmax (vocab 152064) on the 7B "
                          "layer's packed rows")
@@ -310,6 +330,13 @@ def main():
     if args.gate_sweep:
         report["gate_sweep"] = gate_sweep(ev, stream)
         result["gate_sweep"] = report["gate_sweep"]
+    if args.reuse:
+        ms_r = time_reuse(dl, tau, args.steps, args.warmup, ev, stream)
+        result["reuse"] = dict(us_per_verify_layer=ms_r * 1e3,
+                               correction_cost_us=(ms - ms_r) * 1e3)
+        log(f"[bench] REUSE variant {ms_r * 1e3:.1f} us per verify layer; the correction "
+            f"(folded slots attending to their own branch, O projection on every slot) costs "
+            f"{(ms - ms_r) * 1e3:.1f} us")
     if args.lm_head:
         report["lm_head"] = lm_head_bench(cfg, w, dl, tau, ev, stream, args.steps, args.warmup)
         result["lm_head"] = report["lm_head"]

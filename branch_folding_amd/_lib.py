@@ -18,6 +18,7 @@ SPECFOLD_ERR_HIP = 4
 SPECFOLD_F32 = 0
 SPECFOLD_BF16 = 1
 SPECFOLD_FLAG_FOLD_STATE_IN = 1
+SPECFOLD_FLAG_REUSE_ATTENTION = 2
 SPECFOLD_T_QKV, SPECFOLD_T_ATTN, SPECFOLD_T_H, SPECFOLD_T_FFN = 0, 1, 2, 3
 
 _STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}

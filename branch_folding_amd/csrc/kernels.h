@@ -101,11 +101,13 @@ int gemm_host_split(int M, int N, int Kd, int elem_bytes);
 // Finish of the O projection: h[s] = H[s] + sum of `split` partial planes (rounded to T),
 // and for every packed slot s (packed_slot[slot_row[s]] == s) the FFN input
 // A2[slot_row[s]] = h[s] / sqrt(mean(h[s]^2) + eps) * g.  One workgroup per slot.
+// by_row: the partial planes hold the K packed rows (the GEMM's split re-derived on the
+// device from tiles_n column tiles and kiters k-iterations) and slot s adds row slot_row[s].
 template <typename T>
 hipError_t launch_oproj_finish(const float* partial, int split, const void* H, void* h, int S,
                                int d, const int32_t* slot_row, const int32_t* packed_slot,
                                const int32_t* count, const void* g, float eps, void* A2,
-                               int ld_a2, hipStream_t st);
+                               int ld_a2, bool by_row, int tiles_n, int kiters, hipStream_t st);
 // fp32 elements of split-K partial storage any GEMM with these bounds may use
 // (always: the GEMM writes partial planes even without split-K, as kEpiPartial does)
 size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always = false);

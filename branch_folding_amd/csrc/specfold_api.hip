@@ -186,7 +186,8 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
                           const int32_t* fold_src, float tau, float* ratio, uint8_t* rec,
                           int32_t* src, int32_t* packed, int32_t* slot_row, int32_t* count,
                           bool state_in, char* ws, const Layout& L, hipStream_t st,
-                          const specfold_probe* probe, bool gate_done, const NextGate* next) {
+                          const specfold_probe* probe, bool gate_done, const NextGate* next,
+                          bool reuse) {
   const int N = s->num_nodes, B = s->block, S = N * B, d = s->hidden, ff = s->ffn;
   const int dh = s->head_dim, nq = s->n_q_heads, nkv = s->n_kv_heads;
   const int qkvd = (nq + 2 * nkv) * dh, qd = nq * dh;
@@ -249,18 +250,24 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   HIP_CHECK(launch_attn_block<T>(ap, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_ATTN_BLOCK, false));
 
-  // O projection over every slot: fp32 partials, then one row pass adds the residual and
-  // computes the FFN's RMSNorm for the packed rows
+  // O projection over every slot (with the REUSE variant: over the packed rows, gathered
+  // by packed_slot, whose results every slot takes through slot_row): fp32 partials, then
+  // one row pass adds the residual and computes the FFN's RMSNorm for the packed rows
   gp = GemmParams{};
   gp.A = ATT; gp.lda = L.ld_q; gp.W = w->w_o; gp.ldw = qd; gp.C = nullptr; gp.ldc = d;
-  gp.partial = gpart; gp.m_dev = nullptr; gp.m_cap = S; gp.N = d; gp.Kd = qd;
+  gp.partial = gpart; gp.m_dev = reuse ? count : nullptr; gp.m_cap = S; gp.N = d; gp.Kd = qd;
+  if (reuse) {
+    gp.a_rows = packed;
+    gp.a_rows_cap = S;
+  }
   HIP_CHECK(mark(SPECFOLD_STEP_O_PROJ, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiPartial, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_O_PROJ, false));
   HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM2, true));
   HIP_CHECK(launch_oproj_finish<T>(gpart, gemm_host_split(S, d, qd, (int)sizeof(T)), hin, Hh, S, d,
                                    slot_row, packed, count, w->rms2, s->rms_eps, A2,
-                                   (int)L.ld_d, st));
+                                   (int)L.ld_d, reuse, ceil_div(d, gemm_tile_n(d)),
+                                   qd / (kGemmBKBytes / (int)sizeof(T)), st));
   HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM2, false));
 
   gp = GemmParams{};
@@ -289,7 +296,7 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
 }
 
 specfold_status check_flags(uint32_t flags) {
-  if (flags & ~SPECFOLD_FLAG_FOLD_STATE_IN)
+  if (flags & ~(SPECFOLD_FLAG_FOLD_STATE_IN | SPECFOLD_FLAG_REUSE_ATTENTION))
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
   return SPECFOLD_OK;
 }
@@ -371,7 +378,7 @@ specfold_status launch_layer(const specfold_shape* shape, const specfold_layer_w
                              const Layout& L, hipStream_t s, const specfold_probe* probe,
                              bool gate_done = false,
                              const specfold_layer_weights* next_weights = nullptr,
-                             specfold_fold_state* next_state = nullptr) {
+                             specfold_fold_state* next_state = nullptr, bool reuse = false) {
   auto pick = [&](auto* user, size_t off) {
     using P = decltype(user);
     return user ? user : (P)(ws + off);
@@ -394,10 +401,10 @@ specfold_status launch_layer(const specfold_shape* shape, const specfold_layer_w
   if (shape->dtype == SPECFOLD_BF16)
     return run_layer<bf16>(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, ratio,
                            rec, src, packed, slot_row, count, state_in, ws, L, s, probe,
-                           gate_done, next);
+                           gate_done, next, reuse);
   return run_layer<float>(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, ratio,
                           rec, src, packed, slot_row, count, state_in, ws, L, s, probe,
-                          gate_done, next);
+                          gate_done, next, reuse);
 }
 
 }  // namespace
@@ -506,7 +513,8 @@ specfold_status specfold_layer_forward_probed(const specfold_shape* shape,
   const Layout L = layout_of(shape);
   if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SPECFOLD_OK) return st;
   return launch_layer(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, state,
-                      state_in, (char*)workspace, L, (hipStream_t)stream, probe);
+                      state_in, (char*)workspace, L, (hipStream_t)stream, probe, false, nullptr,
+                      nullptr, (flags & SPECFOLD_FLAG_REUSE_ATTENTION) != 0);
 }
 
 size_t specfold_stack_workspace_bytes(const specfold_shape* shape) {
@@ -565,7 +573,8 @@ specfold_status specfold_stack_forward(const specfold_shape* shape, int32_t num_
     st = launch_layer(shape, &weights[l], prefix ? &prefix[l] : nullptr, x, y, fold_src, tau,
                       states ? &states[l] : nullptr, state_in, ws, L, (hipStream_t)stream,
                       nullptr, fuse && l > 0, fuse_next ? &weights[l + 1] : nullptr,
-                      fuse_next && states ? &states[l + 1] : nullptr);
+                      fuse_next && states ? &states[l + 1] : nullptr,
+                      (flags & SPECFOLD_FLAG_REUSE_ATTENTION) != 0);
     if (st != SPECFOLD_OK) return st;
     x = y;
   }

@@ -66,14 +66,15 @@ class DeviceLayer:
             self.H.copy_(to_device(H.reshape(self.H.shape), self.dt, self.device))
 
     def forward(self, tau: float, stream=None, state_in: Optional[Dict[str, np.ndarray]] = None,
-                out: Optional[torch.Tensor] = None, probe=None) -> torch.Tensor:
-        flags = 0
+                out: Optional[torch.Tensor] = None, probe=None, reuse: bool = False
+                ) -> torch.Tensor:
+        flags = L.SPECFOLD_FLAG_REUSE_ATTENTION if reuse else 0
         if state_in is not None:
             for k in ("recompute", "src_node", "packed_slot", "slot_row", "packed_count"):
                 v = np.asarray(state_in[k]).reshape(-1)
                 self.state[k].copy_(torch.from_numpy(v.astype(
                     np.uint8 if k == "recompute" else np.int32)).to(self.device))
-            flags = L.SPECFOLD_FLAG_FOLD_STATE_IN
+            flags |= L.SPECFOLD_FLAG_FOLD_STATE_IN
         o = self.out if out is None else out
         L.specfold_layer_forward(self.shape, self.w, self.prefix, self.H, o, self.fold_src, tau,
                                  self.state, flags, self.ws, self.ws_bytes, stream, probe)

@@ -127,6 +127,14 @@ typedef struct specfold_fold_state {
  * decide nothing). */
 #define SPECFOLD_FLAG_FOLD_STATE_IN 1u
 
+/* REUSE variant of folded attention: a folded slot takes its resolved source's attention
+ * output as it is, instead of attending with its own branch's block keys and values (the
+ * correction of the SpecFold explainer's implementation memo).  Only the packed rows then
+ * need the O projection, h[s] = H[s] + (o W_o^T)[slot_row[s]], so the output of a folded
+ * slot differs from its source's by its own input delta, y[n,i] = y[src,i] + H[n,i] -
+ * H[src,i] (up to rounding).  Timing both modes measures what the correction costs. */
+#define SPECFOLD_FLAG_REUSE_ATTENTION 2u
+
 /* Gate (SpecFold explainer, paragraph on measuring the relative difference at the layer
  * input; iitog.ru summary, "token-level residual gating").
  * For every child n >= 1 and position i:

@@ -249,3 +249,49 @@ def test_budget_sweep_ends(n, tau):
         slots += [(int(rng.integers(0, n)), int(rng.integers(0, cfg.block)))
                   for _ in range(20)]
     _check_layer(cfg, w, tau, L, DeviceLayer, slots=slots)
+
+
+@pytest.mark.parametrize("cfg,tau", [(EDGE[2], 0.3), (EDGE[5], 0.05), (CONFIGS[0], 0.05),
+                                     (CONFIGS[1], 0.05)],
+                         ids=["ragged-bf16-dag", "star-f32", "tiny-f32", "7b-layer"])
+def test_layer_reuse_attention(cfg, tau):
+    """REUSE variant (SPECFOLD_FLAG_REUSE_ATTENTION): a folded slot takes its resolved
+    source's attention output; the O projection runs on the packed rows only.  Compared
+    with the oracle's attn="reuse" layer, and on the GPU output itself the closed form
+    y[n,i] - y[src,i] = H[n,i] - H[src,i] within the output tolerance."""
+    L, DeviceLayer = _dev()
+    w = _workload(cfg)
+    _say(f"[gpu] reuse layer {cfg.name} tau={tau}")
+    dl = DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src)
+    dl.forward(tau, reuse=True)
+    torch.cuda.synchronize()
+    gst = dl.fold_state()
+    ost = oracle_state(w, tau)
+    st = ost
+    if not assert_fold_state_equal(gst, ost, tau):
+        dl.forward(tau, reuse=True,
+                   state_in=dict(recompute=ost["recompute"], src_node=ost["src"],
+                                 packed_slot=np.pad(ost["packed_slot"], (0, cfg.slots - ost["K"])),
+                                 slot_row=ost["slot_row"], packed_count=np.array([ost["K"]])))
+        torch.cuda.synchronize()
+    y = dl.output_numpy()
+    ref = oracle_layer(w, tau, state=st, attn="reuse")
+    tol = TOL[cfg.dtype]
+    err = max_abs_rel(y, ref["y"])
+    _say(f"[gpu]   K={st['K']} max-abs-rel={err:.3e} (tol {tol})")
+    assert err <= tol
+    src = st["src"]
+    scale = np.max(np.abs(y))
+    worst = 0.0
+    for n in range(cfg.num_nodes):
+        for i in range(cfg.block):
+            m = int(src[n, i])
+            if m != n:
+                d = (y[n, i] - y[m, i]) - (w.H[n, i].astype(np.float64) - w.H[m, i])
+                worst = max(worst, float(np.max(np.abs(d))) / scale)
+    assert worst <= tol, worst
+    # the corrected and the reused layer differ once anything folds next to a recomputed key
+    dl.forward(tau)
+    torch.cuda.synchronize()
+    if (~st["recompute"]).any():
+        assert np.max(np.abs(dl.output_numpy() - y)) > 0
