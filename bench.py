@@ -536,12 +536,26 @@ def stack_bench(ev, stream, steps, warmup):
     ev.record(t1, stream)
     torch.cuda.synchronize()
     ms = ev.ms(t0, t1) / steps
-    ev.destroy([t0, t1])
     log(f"[bench] stack: {ms * 1e3:.0f} us per verify step ({ms * 1e3 / ds.num_layers:.1f} "
         f"us per layer), K per layer {Ks}")
+    # the same step captured as one HIP graph and replayed
+    g = ds.capture(cfg.tau, record_states=False)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev.record(t0, stream)
+    for _ in range(steps):
+        g.replay()
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    ms_g = ev.ms(t0, t1) / steps
+    ev.destroy([t0, t1])
+    del g
+    log(f"[bench] stack as one HIP graph: {ms_g * 1e3:.0f} us per verify step")
     res = dict(workload=cfg.name, layers=ds.num_layers, tau=cfg.tau, us_per_verify_step=ms * 1e3,
                us_per_layer=ms * 1e3 / ds.num_layers, packed_rows_per_layer=Ks,
-               slots=cfg.slots, branch_tokens_per_s=cfg.slots / (ms * 1e-3))
+               slots=cfg.slots, branch_tokens_per_s=cfg.slots / (ms * 1e-3),
+               us_per_verify_step_graph=ms_g * 1e3)
     del ds
     torch.cuda.empty_cache()
     return res

@@ -162,6 +162,15 @@ class DeviceStack:
                                  self.ws, self.ws_bytes, stream)
         return self.out
 
+    def capture(self, tau: float, record_states: bool = True) -> "torch.cuda.CUDAGraph":
+        """The whole stack (one specfold_stack_forward) captured as one HIP graph; replay()
+        re-runs every layer's gate, packing and kernels on the current contents of H.  The
+        library records no memset or allocation, only kernel launches."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(tau, record_states=record_states)
+        return g
+
     def layer_forward(self, l: int, x, tau: float, stream=None, state_in=None) -> torch.Tensor:
         """Layer l alone (specfold_layer_forward) on hidden state x, with the stack's
         buffers; the fold state goes to (or, given state_in, comes from) layer l's state

@@ -207,6 +207,36 @@ def test_stack_equals_chained_layer_calls(nl):
     assert not torch.equal(ds.out, ds.H)
 
 
+def test_stack_graph_replay():
+    """The stack captured as one HIP graph and replayed three times, with eager work and
+    synchronisations between the replays (the outputs and fold states are overwritten with
+    junk first): every replay equals the eager run bit for bit, fold states included."""
+    L, runner = _dev()
+    cfg = SMALL[1]
+    nl = 3
+    _say(f"[gpu] stack graph replay {cfg.name} layers={nl}")
+    ds = _device_stack(runner, cfg, nl)
+    ds.forward(0.05)
+    torch.cuda.synchronize()
+    ref = ds.out.clone()
+    ref_states = ds.fold_states()
+    g = ds.capture(0.05)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ds.out.fill_(7.0)
+        for st in ds.states:
+            for v in st.values():
+                v.fill_(3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ds.out, ref), rep
+        for a, b in zip(ds.fold_states(), ref_states):
+            for k in ("recompute", "src", "packed_slot", "slot_row", "K"):
+                np.testing.assert_array_equal(a[k], b[k])
+            np.testing.assert_array_equal(a["ratio"], b["ratio"])
+
+
 def test_stack_7b_shape_two_layers():
     """The 28-layer stack's shape (7B layer, 1+31 branches, prefix 4096) on its first
     two layers; the full depth runs in test_stack_7b_full_depth."""
