@@ -62,13 +62,13 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 
 constexpr int kGemmStages = 3;
 
-template <typename T, int EPI, int BN>
-__global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
+template <typename T, int EPI, int BN, int BM>
+__global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
   using G = GemmTile<T>;
-  constexpr int NT = BN * 2;                 // threads
+  constexpr int NT = BM * BN / 64;           // threads: one wave per 64 x 64 wave tile
   constexpr int NW = NT / 64;                // waves
   constexpr int WN = BN / 64;                // waves along N
-  constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
+  constexpr int A_BYTES = BM * kGemmBKBytes;
   constexpr int W_BYTES = BN * kGemmBKBytes;
   constexpr int AQ = A_BYTES / 1024 / NW;    // A load instructions per wave per k-iteration
   constexpr int WQ = W_BYTES / 1024 / NW;    // W load instructions per wave per k-iteration
@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
 
   const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
   if (M <= 0) return;
-  const int mb = ceil_div(M, kGemmBM), nt = ceil_div(p.N, BN);
+  const int mb = ceil_div(M, BM), nt = ceil_div(p.N, BN);
   const int kiters = p.Kd / G::BK;
   const int tiles = mb * nt;
   const int split = EPI == kEpiArgmax ? 1 : gemm_split(tiles, kiters);
@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(BN * 2) gemm_kernel(GemmParams p) {
     const int s = v / (mb * nt), vt = v - s * (mb * nt);
     const int band = vt / (8 * nt), bh = imin(8, mb - band * 8), vb = vt - band * 8 * nt;
     const int mt = band * 8 + vb % bh, ntile = vb / bh;
-    const int m0 = mt * kGemmBM, n0 = ntile * BN;
+    const int m0 = mt * BM, n0 = ntile * BN;
     const int kb = (int)((long)s * kiters / split), ke = (int)((long)(s + 1) * kiters / split);
 
     const char* a_src[AQ];
@@ -504,7 +504,7 @@ template <typename T, int EPI, int BN>
 __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
   const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
   if (M <= 0) return;
-  const int mb = ceil_div(M, kGemmBM), nt = ceil_div(p.N, BN);
+  const int mb = ceil_div(M, gemm_tile_m(p.m_cap)), nt = ceil_div(p.N, BN);
   const int kiters = p.Kd / (kGemmBKBytes / (int)sizeof(T));
   const int split = gemm_split(mb * nt, kiters);
   if (split == 1) return;
@@ -557,7 +557,8 @@ int gemm_tile_n(int) { return 128; }
 
 int gemm_host_split(int M, int N, int Kd, int elem_bytes) {
   const int BN = gemm_tile_n(N);
-  return gemm_split(ceil_div(M, kGemmBM) * ceil_div(N, BN), Kd / (kGemmBKBytes / elem_bytes));
+  return gemm_split(ceil_div(M, gemm_tile_m(M)) * ceil_div(N, BN),
+                    Kd / (kGemmBKBytes / elem_bytes));
 }
 
 size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always) {
@@ -565,10 +566,11 @@ size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always)
   const int kiters = Kd / (kGemmBKBytes / elem_bytes);
   const int nt = ceil_div(N, BN);
   size_t best = 0;
-  for (int mb = 1; mb <= ceil_div(m_cap, kGemmBM); ++mb) {
+  const int BM = gemm_tile_m(m_cap);
+  for (int mb = 1; mb <= ceil_div(m_cap, BM); ++mb) {
     const int split = gemm_split(mb * nt, kiters);
     if (split > 1 || always) {
-      const size_t e = (size_t)split * (size_t)(mb * kGemmBM < m_cap ? mb * kGemmBM : m_cap) * N;
+      const size_t e = (size_t)split * (size_t)(mb * BM < m_cap ? mb * BM : m_cap) * N;
       if (e > best) best = e;
     }
   }
@@ -577,7 +579,10 @@ size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always)
 
 template <typename T, int EPI, int BN>
 static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st) {
-  gemm_kernel<T, EPI, BN><<<num_cu, BN * 2, 0, st>>>(p);
+  if (gemm_tile_m(p.m_cap) == 256)
+    gemm_kernel<T, EPI, BN, 256><<<num_cu, 256 * BN / 64, 0, st>>>(p);
+  else
+    gemm_kernel<T, EPI, BN, 128><<<num_cu, 128 * BN / 64, 0, st>>>(p);
   // the reduction only runs when some row count could make the device choose split > 1
   if (EPI != kEpiPartial && EPI != kEpiArgmax &&
       gemm_split(ceil_div(p.N, BN), p.Kd / (kGemmBKBytes / (int)sizeof(T))) > 1) {

@@ -73,7 +73,13 @@ struct GemmParams {
   int arg_ld;
 };
 
-constexpr int kGemmBM = 128;
+constexpr int kGemmBM = 128;      // row tile of the SwiGLU slabs
+// Row tile of the split-K GEMM for calls of at most m_cap rows: with 2048+ rows possible,
+// 256-row tiles (8 waves, two per SIMD): per flop a 256 x 128 tile loads 3/4 of the bytes
+// of a 128 x 128 one, and the MFMA-bound GEMMs of big verify steps are held by the load
+// rate per CU.  Every kernel that re-derives a GEMM's split uses this same function.
+constexpr int kGemmTallFrom = 2048;
+__host__ __device__ inline int gemm_tile_m(int m_cap) { return m_cap >= kGemmTallFrom ? 256 : 128; }
 constexpr int kGemmBKBytes = 128;
 constexpr int kGemmMaxSplit = 24;
 // Split-K keeps units >= this many k-iterations long, so a unit's fp32 partial plane stays

@@ -78,6 +78,18 @@ LONG_PREFIX = [
 ]
 
 
+# 2048+ slots: the split-K GEMMs run 256-row tiles (8 waves); every slot compared, with
+# dense (2048 packed rows = 8 row tiles) and folded (a ragged last row tile) packings.
+TALL = [
+    custom_config(name="tall-bf16", num_nodes=64, block=32, hidden=256, n_q=4, n_kv=2,
+                  head_dim=64, ffn=512, prefix=100, dtype="bf16", graph="tree3",
+                  reveal=(1, 2), seed=61),
+    custom_config(name="tall-f32", num_nodes=32, block=72, hidden=128, n_q=2, n_kv=1,
+                  head_dim=64, ffn=256, prefix=33, dtype="f32", graph="dag", reveal=(1, 3),
+                  seed=62),
+]
+
+
 def _check_layer(cfg, w, tau, L, DeviceLayer, slots=None):
     _say(f"[gpu] layer {cfg.name} tau={tau} S={cfg.slots}")
     dl = DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src)
@@ -295,3 +307,27 @@ def test_layer_reuse_attention(cfg, tau):
     torch.cuda.synchronize()
     if (~st["recompute"]).any():
         assert np.max(np.abs(dl.output_numpy() - y)) > 0
+
+
+@pytest.mark.parametrize("cfg", TALL, ids=lambda c: c.name)
+@pytest.mark.parametrize("tau", [-1.0, 0.05])
+def test_layer_tall_row_tiles(cfg, tau):
+    L, DeviceLayer = _dev()
+    assert cfg.slots >= 2048
+    _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
+
+
+def test_layer_tall_row_tiles_reuse():
+    """The REUSE variant at 2048 slots: the O projection over the packed rows with 256-row
+    tiles and the split re-derived on the device by the O finish."""
+    L, DeviceLayer = _dev()
+    cfg = TALL[0]
+    w = _workload(cfg)
+    dl = DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src)
+    dl.forward(0.05, reuse=True)
+    torch.cuda.synchronize()
+    ost = oracle_state(w, 0.05)
+    assert assert_fold_state_equal(dl.fold_state(), ost, 0.05)
+    err = max_abs_rel(dl.output_numpy(), oracle_layer(w, 0.05, state=ost, attn="reuse")["y"])
+    _say(f"[gpu] tall reuse K={ost['K']} max-abs-rel={err:.3e}")
+    assert err <= TOL[cfg.dtype]
