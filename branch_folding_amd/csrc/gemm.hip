@@ -596,7 +596,7 @@ static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st
 
 template <typename T, int EPI>
 static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t st) {
-  if (EPI == kEpiSwiGLU) {
+  if (EPI == kEpiSwiGLU && gemm_tile_m(p.m_cap) == 128) {
     const int slabs = swiglu_slabs(p.ff, num_cu);
     swiglu_slab_kernel<T><<<slabs, kSlabThreads, 0, st>>>(p, slabs);
     return hipGetLastError();
