@@ -93,6 +93,10 @@ constexpr int kGemmMinUnitIters = 8;
 __host__ __device__ inline int gemm_split(int tiles, int kiters) {
   if (tiles <= 0) return 1;
   int s = kPlanCUs / tiles;
+  // Between half a round and a full round of tiles, one unit per tile leaves CUs idle; 3 or 4
+  // splits finish in 2 of 3 or 3 of 4 unit-rounds (129..170 tiles: 3; 171..192: 4).
+  if (s == 1 && 3 * tiles <= 2 * kPlanCUs) s = 3;
+  else if (s == 1 && 4 * tiles <= 3 * kPlanCUs) s = 4;
   const int smax = kiters / kGemmMinUnitIters;
   if (s > smax) s = smax;
   if (s > kGemmMaxSplit) s = kGemmMaxSplit;
