@@ -323,7 +323,7 @@ __global__ void __launch_bounds__(kFinishThreads) oproj_finish_kernel(
     const float* __restrict__ partial, int split, const T* __restrict__ H, T* __restrict__ h,
     int S, int d, const int32_t* __restrict__ slot_row, const int32_t* __restrict__ packed_slot,
     const int32_t* __restrict__ count, const T* __restrict__ g, float eps, T* __restrict__ A2,
-    int ld_a2, bool by_row, int tiles_n, int kiters) {
+    int ld_a2, bool by_row, int tiles_n, int kiters, int bm) {
   __shared__ float red[kFinishThreads / 64];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int s = blockIdx.x;
@@ -334,7 +334,7 @@ __global__ void __launch_bounds__(kFinishThreads) oproj_finish_kernel(
   // device; slot s adds the projection of its packed row slot_row[s]
   if (by_row && K <= 0) return;
   const int rows = by_row ? K : S;
-  if (by_row) split = gemm_split(ceil_div(K, gemm_tile_m(S)) * tiles_n, kiters);
+  if (by_row) split = gemm_split(ceil_div(K, bm) * tiles_n, kiters);
   const size_t plane = (size_t)rows * d;
   const size_t row = (size_t)s * d;
   const size_t prow = by_row ? (size_t)imin(imax(slot_row[s], 0), K - 1) * d : row;
@@ -475,21 +475,22 @@ template <typename T>
 hipError_t launch_oproj_finish(const float* partial, int split, const void* H, void* h, int S,
                                int d, const int32_t* slot_row, const int32_t* packed_slot,
                                const int32_t* count, const void* g, float eps, void* A2,
-                               int ld_a2, bool by_row, int tiles_n, int kiters, hipStream_t st) {
+                               int ld_a2, bool by_row, int tiles_n, int kiters, int bm,
+                               hipStream_t st) {
   oproj_finish_kernel<T><<<S, kFinishThreads, 0, st>>>(partial, split, (const T*)H, (T*)h, S, d,
                                                           slot_row, packed_slot, count,
                                                           (const T*)g, eps, (T*)A2, ld_a2,
-                                                          by_row, tiles_n, kiters);
+                                                          by_row, tiles_n, kiters, bm);
   return hipGetLastError();
 }
 template hipError_t launch_oproj_finish<float>(const float*, int, const void*, void*, int, int,
                                                const int32_t*, const int32_t*, const int32_t*,
                                                const void*, float, void*, int, bool, int, int,
-                                               hipStream_t);
+                                               int, hipStream_t);
 template hipError_t launch_oproj_finish<bf16>(const float*, int, const void*, void*, int, int,
                                               const int32_t*, const int32_t*, const int32_t*,
                                               const void*, float, void*, int, bool, int, int,
-                                              hipStream_t);
+                                              int, hipStream_t);
 
 template hipError_t launch_gate<float>(const void*, const int32_t*, int, int, int, float, float*,
                                        uint8_t*, const uint8_t*, const void*, float, void*, int,

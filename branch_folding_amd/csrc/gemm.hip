@@ -504,7 +504,7 @@ template <typename T, int EPI, int BN>
 __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
   const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
   if (M <= 0) return;
-  const int mb = ceil_div(M, gemm_tile_m(p.m_cap)), nt = ceil_div(p.N, BN);
+  const int mb = ceil_div(M, gemm_bm(p)), nt = ceil_div(p.N, BN);
   const int kiters = p.Kd / (kGemmBKBytes / (int)sizeof(T));
   const int split = gemm_split(mb * nt, kiters);
   if (split == 1) return;
@@ -555,9 +555,9 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
 // than re-reading the (L2-resident) activation tile for twice as many column tiles.
 int gemm_tile_n(int) { return 128; }
 
-int gemm_host_split(int M, int N, int Kd, int elem_bytes) {
+int gemm_host_split(int M, int N, int Kd, int elem_bytes, int bm) {
   const int BN = gemm_tile_n(N);
-  return gemm_split(ceil_div(M, gemm_tile_m(M)) * ceil_div(N, BN),
+  return gemm_split(ceil_div(M, bm) * ceil_div(N, BN),
                     Kd / (kGemmBKBytes / elem_bytes));
 }
 
@@ -566,20 +566,20 @@ size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always)
   const int kiters = Kd / (kGemmBKBytes / elem_bytes);
   const int nt = ceil_div(N, BN);
   size_t best = 0;
-  const int BM = gemm_tile_m(m_cap);
-  for (int mb = 1; mb <= ceil_div(m_cap, BM); ++mb) {
-    const int split = gemm_split(mb * nt, kiters);
-    if (split > 1 || always) {
-      const size_t e = (size_t)split * (size_t)(mb * BM < m_cap ? mb * BM : m_cap) * N;
-      if (e > best) best = e;
+  for (int BM = 128; BM <= 256; BM *= 2)            // either row tile may run
+    for (int mb = 1; mb <= ceil_div(m_cap, BM); ++mb) {
+      const int split = gemm_split(mb * nt, kiters);
+      if (split > 1 || always) {
+        const size_t e = (size_t)split * (size_t)(mb * BM < m_cap ? mb * BM : m_cap) * N;
+        if (e > best) best = e;
+      }
     }
-  }
   return best;
 }
 
 template <typename T, int EPI, int BN>
 static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st) {
-  if (gemm_tile_m(p.m_cap) == 256)
+  if (gemm_bm(p) == 256)
     gemm_kernel<T, EPI, BN, 256><<<num_cu, 256 * BN / 64, 0, st>>>(p);
   else
     gemm_kernel<T, EPI, BN, 128><<<num_cu, 128 * BN / 64, 0, st>>>(p);
@@ -596,7 +596,7 @@ static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st
 
 template <typename T, int EPI>
 static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t st) {
-  if (EPI == kEpiSwiGLU && gemm_tile_m(p.m_cap) == 128) {
+  if (EPI == kEpiSwiGLU && gemm_bm(p) == 128) {
     const int slabs = swiglu_slabs(p.ff, num_cu);
     swiglu_slab_kernel<T><<<slabs, kSlabThreads, 0, st>>>(p, slabs);
     return hipGetLastError();

@@ -71,6 +71,8 @@ struct GemmParams {
   float* arg_val;
   int32_t* arg_idx;
   int arg_ld;
+  // row tile, 128 or 256 (gemm_tile_m); 0 = gemm_tile_m(m_cap)
+  int bm;
 };
 
 constexpr int kGemmBM = 128;      // row tile of the SwiGLU slabs
@@ -78,8 +80,18 @@ constexpr int kGemmBM = 128;      // row tile of the SwiGLU slabs
 // 256-row tiles (8 waves, two per SIMD): per flop a 256 x 128 tile loads 3/4 of the bytes
 // of a 128 x 128 one, and the MFMA-bound GEMMs of big verify steps are held by the load
 // rate per CU.  Every kernel that re-derives a GEMM's split uses this same function.
+// A call whose row count is known to be m_cap (every slot packed) takes them from
+// kGemmTallExactFrom rows on.
 constexpr int kGemmTallFrom = 2048;
-__host__ __device__ inline int gemm_tile_m(int m_cap) { return m_cap >= kGemmTallFrom ? 256 : 128; }
+constexpr int kGemmTallExactFrom = 512;
+__host__ __device__ inline int gemm_tile_m(int m_cap, bool exact = false) {
+  return (m_cap >= kGemmTallFrom || (exact && m_cap >= kGemmTallExactFrom)) ? 256 : 128;
+}
+// the row tile a GEMM call runs with
+__host__ __device__ inline int gemm_bm(const GemmParams& p) {
+  return p.bm ? p.bm : gemm_tile_m(p.m_cap);
+}
+
 constexpr int kGemmBKBytes = 128;
 constexpr int kGemmMaxSplit = 24;
 // Split-K keeps units >= this many k-iterations long, so a unit's fp32 partial plane stays
@@ -94,9 +106,12 @@ __host__ __device__ inline int gemm_split(int tiles, int kiters) {
   if (tiles <= 0) return 1;
   int s = kPlanCUs / tiles;
   // Between half a round and a full round of tiles, one unit per tile leaves CUs idle; 3 or 4
-  // splits finish in 2 of 3 or 3 of 4 unit-rounds (129..170 tiles: 3; 171..192: 4).
-  if (s == 1 && 3 * tiles <= 2 * kPlanCUs) s = 3;
-  else if (s == 1 && 4 * tiles <= 3 * kPlanCUs) s = 4;
+  // splits finish in 2 of 3 or 3 of 4 unit-rounds (129..170 tiles: 3; 171..192: 4).  Only for
+  // long k-loops, where the extra fp32 partial planes are small next to the work (the stress
+  // layer's down projection, 224 k-iterations, gains 15%; an O projection of 48 k-iterations
+  // over 1024 rows lost 10% to its four partial planes).
+  if (s == 1 && kiters >= 128 && 3 * tiles <= 2 * kPlanCUs) s = 3;
+  else if (s == 1 && kiters >= 128 && 4 * tiles <= 3 * kPlanCUs) s = 4;
   const int smax = kiters / kGemmMinUnitIters;
   if (s > smax) s = smax;
   if (s > kGemmMaxSplit) s = kGemmMaxSplit;
@@ -106,18 +121,20 @@ __host__ __device__ inline int gemm_split(int tiles, int kiters) {
 template <typename T>
 hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st);
 // split-K factor the GEMM uses when the row count M is known on the host
-int gemm_host_split(int M, int N, int Kd, int elem_bytes);
+int gemm_host_split(int M, int N, int Kd, int elem_bytes, int bm);
 
 // Finish of the O projection: h[s] = H[s] + sum of `split` partial planes (rounded to T),
 // and for every packed slot s (packed_slot[slot_row[s]] == s) the FFN input
 // A2[slot_row[s]] = h[s] / sqrt(mean(h[s]^2) + eps) * g.  One workgroup per slot.
 // by_row: the partial planes hold the K packed rows (the GEMM's split re-derived on the
-// device from tiles_n column tiles and kiters k-iterations) and slot s adds row slot_row[s].
+// device from its row tile bm, tiles_n column tiles and kiters k-iterations) and slot s adds
+// row slot_row[s].
 template <typename T>
 hipError_t launch_oproj_finish(const float* partial, int split, const void* H, void* h, int S,
                                int d, const int32_t* slot_row, const int32_t* packed_slot,
                                const int32_t* count, const void* g, float eps, void* A2,
-                               int ld_a2, bool by_row, int tiles_n, int kiters, hipStream_t st);
+                               int ld_a2, bool by_row, int tiles_n, int kiters, int bm,
+                               hipStream_t st);
 // fp32 elements of split-K partial storage any GEMM with these bounds may use
 // (always: the GEMM writes partial planes even without split-K, as kEpiPartial does)
 size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always = false);

@@ -192,6 +192,11 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   const int dh = s->head_dim, nq = s->n_q_heads, nkv = s->n_kv_heads;
   const int qkvd = (nq + 2 * nkv) * dh, qd = nq * dh;
   const int cus = num_cus();
+  // row tile of the GEMMs: with tau < 0 every slot is packed, so the row count is S.  (The O
+  // projection always has S rows, but below 2048 slots its 256-row tiles would double the
+  // partial planes its finish reads for no gain: at the 7B layer -2 us in the GEMM, +2.5 us
+  // in the finish.)
+  const int bm = gemm_tile_m(S, !state_in && tau < 0.f);
   // a failure left behind by some earlier, unrelated HIP call on this thread must not be
   // reported as a failure of these launches
   (void)hipGetLastError();
@@ -229,7 +234,7 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   // packed rows of A1 are gathered by the GEMM's loads
   GemmParams gp{};
   gp.A = A2; gp.lda = L.ld_d; gp.a_rows = packed; gp.a_rows_cap = S; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = L.ld_qkv;
-  gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = qkvd; gp.Kd = d;
+  gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = qkvd; gp.Kd = d; gp.bm = bm;
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, false));
@@ -256,6 +261,7 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   gp = GemmParams{};
   gp.A = ATT; gp.lda = L.ld_q; gp.W = w->w_o; gp.ldw = qd; gp.C = nullptr; gp.ldc = d;
   gp.partial = gpart; gp.m_dev = reuse ? count : nullptr; gp.m_cap = S; gp.N = d; gp.Kd = qd;
+  gp.bm = bm;
   if (reuse) {
     gp.a_rows = packed;
     gp.a_rows_cap = S;
@@ -264,22 +270,23 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   HIP_CHECK(launch_gemm<T>(gp, kEpiPartial, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_O_PROJ, false));
   HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM2, true));
-  HIP_CHECK(launch_oproj_finish<T>(gpart, gemm_host_split(S, d, qd, (int)sizeof(T)), hin, Hh, S, d,
-                                   slot_row, packed, count, w->rms2, s->rms_eps, A2,
+  HIP_CHECK(launch_oproj_finish<T>(gpart, gemm_host_split(S, d, qd, (int)sizeof(T), gp.bm), hin,
+                                   Hh, S, d, slot_row, packed, count, w->rms2, s->rms_eps, A2,
                                    (int)L.ld_d, reuse, ceil_div(d, gemm_tile_n(d)),
-                                   qd / (kGemmBKBytes / (int)sizeof(T)), st));
+                                   qd / (kGemmBKBytes / (int)sizeof(T)), gp.bm, st));
   HIP_CHECK(mark(SPECFOLD_STEP_RMSNORM2, false));
 
   gp = GemmParams{};
   gp.A = A2; gp.lda = L.ld_d; gp.W = w->w_gate_up; gp.ldw = d; gp.C = G; gp.ldc = L.ld_ff;
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = 2 * ff; gp.Kd = d; gp.ff = ff;
+  gp.bm = bm;
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiSwiGLU, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, false));
 
   gp = GemmParams{};
   gp.A = G; gp.lda = L.ld_ff; gp.W = w->w_down; gp.ldw = ff; gp.C = F; gp.ldc = d;
-  gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = d; gp.Kd = ff;
+  gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = d; gp.Kd = ff; gp.bm = bm;
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_DOWN, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_DOWN, false));
