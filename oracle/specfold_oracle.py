@@ -47,7 +47,7 @@ import numpy as np
 __all__ = [
     "gate", "resolve", "pack", "rms_norm", "silu", "layer", "serial_layer",
     "bruteforce_provenance", "FoldState", "fold_state", "round_to_bf16", "stack",
-    "lm_head_argmax",
+    "lm_head_argmax", "rope",
 ]
 
 
@@ -172,11 +172,24 @@ def _softmax(z: np.ndarray) -> np.ndarray:
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
+def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotary position embedding, rotate-half form: x [..., rows, heads, dh] at positions
+    pos [rows]; element j of the first half and element j of the second half form a pair
+    turned by the angle pos * theta^(-2j/dh)."""
+    dh = x.shape[-1]
+    half = dh // 2
+    inv = np.asarray(theta, dtype=np.float64) ** (-2.0 * np.arange(half) / dh)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]          # [rows, half]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
 def layer(weights: Dict[str, np.ndarray], H: np.ndarray, fold_src: np.ndarray, tau: float,
           prefix_k: np.ndarray, prefix_v: np.ndarray, *, n_q: int, n_kv: int,
           eps: float = 1e-6, dtype=np.float64, state: Optional[FoldState] = None,
           slots: Optional[Iterable[Tuple[int, int]]] = None,
-          attn: str = "correct") -> Dict[str, np.ndarray]:
+          attn: str = "correct", rope_theta: float = 0.0) -> Dict[str, np.ndarray]:
     """One folded verify layer over the parent and all draft branches.
 
     weights: rms1 [d], w_qkv [(n_q+2n_kv)dh, d] (Q heads | K heads | V heads), w_o
@@ -186,6 +199,10 @@ def layer(weights: Dict[str, np.ndarray], H: np.ndarray, fold_src: np.ndarray, t
     instead of running the gate -- e.g. one taken from ``fold_state`` on other inputs.
     slots: evaluate only these (n, i) outputs (and what they depend on); other entries
     of the returned per-slot arrays are NaN.
+    weights["b_qkv"] (optional): a bias added to the Q/K/V projections.
+    rope_theta > 0: the Q and K heads of a packed row at block position i are rotated at
+    absolute position P + i (the block follows the P prefix tokens, whose cached keys are
+    stored already rotated); a folded slot's query is its source's, at the same position.
     attn: "correct" (a folded slot's attention runs against its own branch's keys and
     values -- the correction of [SF]'s implementation memo) or "reuse" (a folded slot
     takes its resolved source's attention output as it is, so only the packed rows need
@@ -215,9 +232,15 @@ def layer(weights: Dict[str, np.ndarray], H: np.ndarray, fold_src: np.ndarray, t
     # (4) packed Q/K/V
     A1 = rms_norm(Hf[packed_slot], weights["rms1"].astype(dt), eps)
     qkv = A1 @ wqkv.T                                        # [K, (n_q+2n_kv) dh]
+    if weights.get("b_qkv") is not None:
+        qkv = qkv + weights["b_qkv"].astype(dt)
     Qp = qkv[:, : n_q * dh].reshape(K, n_q, dh)
     Kp = qkv[:, n_q * dh:(n_q + n_kv) * dh].reshape(K, n_kv, dh)
     Vp = qkv[:, (n_q + n_kv) * dh:].reshape(K, n_kv, dh)
+    if rope_theta:
+        pos = prefix_k.shape[0] + np.asarray(packed_slot) % B
+        Qp = rope(Qp, pos, rope_theta)
+        Kp = rope(Kp, pos, rope_theta)
 
     # which slots to evaluate
     if slots is None:

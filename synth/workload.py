@@ -62,6 +62,8 @@ class Config:
     rms_eps: float = 1e-6
     max_depth: int = 0      # dag_deep only
     weight_std: float = 0.02  # std of the linear weights
+    rope_theta: float = 0.0   # rotary embedding base (0: none)
+    qkv_bias: bool = False    # QKV projection bias ~ N(0, 0.1^2)
 
     @property
     def slots(self) -> int:
@@ -260,7 +262,7 @@ def make_layer_weights(cfg: Config, rng: np.random.Generator) -> Dict[str, np.nd
     def lin(o, i):
         return _storage(cfg, rng.standard_normal((o, i), dtype=np.float32) * std)
 
-    return {
+    out = {
         "rms1": np.ones(d, dtype=np.float32),
         "w_qkv": lin(cfg.qkv_dim, d),
         "w_o": lin(d, cfg.n_q * dh),
@@ -268,6 +270,10 @@ def make_layer_weights(cfg: Config, rng: np.random.Generator) -> Dict[str, np.nd
         "w_gate_up": lin(2 * f, d),
         "w_down": lin(d, f),
     }
+    if cfg.qkv_bias:          # drawn last, so the other weights do not change
+        out["b_qkv"] = _storage(cfg, rng.standard_normal(cfg.qkv_dim, dtype=np.float32) *
+                                np.float32(0.1))
+    return out
 
 
 def prefix_cache(cfg: Config, rng: np.random.Generator, pad_tokens: int = 64) -> np.ndarray:

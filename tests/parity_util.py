@@ -33,7 +33,7 @@ def oracle_layer(w, tau, state=None, slots=None, layer_idx=0, H=None, attn="corr
     pk, pv = w.prefix_kv(layer_idx)
     return layer(w.weights[layer_idx], w.H if H is None else H, w.fold_src, tau, pk, pv,
                  n_q=cfg.n_q, n_kv=cfg.n_kv, eps=cfg.rms_eps, state=state, slots=slots,
-                 attn=attn)
+                 attn=attn, rope_theta=cfg.rope_theta)
 
 
 def assert_fold_state_equal(gpu, ora, tau, ratio_rtol=2e-5):
