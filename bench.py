@@ -249,6 +249,9 @@ def main():
     ap.add_argument("--reuse", action="store_true",
                     help="also time the layer with the REUSE attention variant (folded slots "
                          "take their source's attention output) and report the correction cost")
+    ap.add_argument("--rope-bias", action="store_true",
+                    help="also time the layer with the rotary embedding (base 10^6) and QKV "
+                         "bias of the 7B model family")
     ap.add_argument("--lm-head", action="store_true",
                     help="also time the LM head + per-branch argmax (vocab 152064) on the 7B "
                          "layer's packed rows")
@@ -337,6 +340,16 @@ def main():
         log(f"[bench] REUSE variant {ms_r * 1e3:.1f} us per verify layer; the correction "
             f"(folded slots attending to their own branch, O projection on every slot) costs "
             f"{(ms - ms_r) * 1e3:.1f} us")
+    if args.rope_bias:
+        crb = cfg.with_(name=cfg.name + "-rope-bias", rope_theta=1.0e6, qkv_bias=True)
+        _, dlr = build_layer(crb)
+        ms_rb, _ = time_layer(dlr, tau, args.steps, args.warmup, ev, stream)
+        result["rope_bias"] = dict(us_per_verify_layer=ms_rb * 1e3,
+                                   extra_us=(ms_rb - ms) * 1e3)
+        log(f"[bench] with rotary embedding + QKV bias: {ms_rb * 1e3:.1f} us per verify layer "
+            f"({(ms_rb - ms) * 1e3:+.1f} us)")
+        del dlr
+        torch.cuda.empty_cache()
     if args.lm_head:
         report["lm_head"] = lm_head_bench(cfg, w, dl, tau, ev, stream, args.steps, args.warmup)
         result["lm_head"] = report["lm_head"]

@@ -35,7 +35,8 @@ class Shape(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("ffn", ctypes.c_int32), ("prefix_len", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float)]
 
 
 class KVView(ctypes.Structure):
@@ -46,7 +47,7 @@ class KVView(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [("rms1", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p),
                 ("rms2", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p),
-                ("w_down", ctypes.c_void_p)]
+                ("w_down", ctypes.c_void_p), ("b_qkv", ctypes.c_void_p)]
 
 
 class Probe(ctypes.Structure):
@@ -146,9 +147,10 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_shape(num_nodes, block, hidden, n_q, n_kv, head_dim, ffn, prefix, dtype,
-               rms_eps=1e-6) -> Shape:
+               rms_eps=1e-6, rope_theta=0.0) -> Shape:
     dt = {"f32": SPECFOLD_F32, "bf16": SPECFOLD_BF16}.get(dtype, dtype)
-    return Shape(num_nodes, block, hidden, n_q, n_kv, head_dim, ffn, prefix, rms_eps, dt)
+    return Shape(num_nodes, block, hidden, n_q, n_kv, head_dim, ffn, prefix, rms_eps, dt,
+                 rope_theta)
 
 
 def specfold_gate(shape: Shape, hidden, fold_src, tau: float, ratio, recompute, stream=None):
@@ -206,7 +208,10 @@ _STATE_KEYS = ("ratio", "recompute", "src_node", "packed_slot", "slot_row", "pac
 
 
 def _weights(weights: dict) -> LayerWeights:
-    return LayerWeights(*[_ptr(weights[k]) for k in _WEIGHT_KEYS])
+    w = LayerWeights(*[_ptr(weights[k]) for k in _WEIGHT_KEYS])
+    if weights.get("b_qkv") is not None:
+        w.b_qkv = _ptr(weights["b_qkv"])
+    return w
 
 
 def _kv(prefix) -> KVView:

@@ -406,6 +406,49 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ h,
 }
 
 // ------------------------------------------------------------------------------------
+// QKV bias and rotary embedding on the packed Q|K|V rows, in place (model families with
+// both, e.g. Qwen / Llama style).  One thread per (packed row, head, pair j): the bias is
+// added to elements j and j + dh/2 of every head; Q and K heads are then rotated by the
+// angle pos * theta^(-2j/dh), pos = prefix length + the row's block position.  The angle and
+// its sine and cosine are taken in double: at positions of ~17K an fp32 angle would be off
+// by ~1e-3 rad.
+// ------------------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) qkv_rope_bias_kernel(
+    T* __restrict__ qkv, long ld, const int32_t* __restrict__ count, int cap,
+    const int32_t* __restrict__ packed_slot, int B, int P, int n_q, int n_kv, int dh,
+    const T* __restrict__ bias, float theta) {
+  const int K = imin(*count, cap);
+  const int half = dh / 2, heads = n_q + 2 * n_kv;
+  const long total = (long)K * heads * half;
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (long)gridDim.x * blockDim.x) {
+    const int k = (int)(idx / (heads * half));
+    const int rem = (int)(idx - (long)k * heads * half);
+    const int hd = rem / half, j = rem - hd * half;
+    T* row = qkv + (size_t)k * ld + (size_t)hd * dh;
+    float x1 = to_f32(row[j]), x2 = to_f32(row[j + half]);
+    if (bias) {
+      x1 += to_f32(bias[hd * dh + j]);
+      x2 += to_f32(bias[hd * dh + j + half]);
+    }
+    if (theta > 0.f && hd < n_q + n_kv) {
+      const int ps = imin(imax(packed_slot[k], 0), cap - 1);
+      const double pos = (double)(P + ps % B);
+      const double ang = pos * pow((double)theta, -2.0 * j / dh);
+      double sn, cs;
+      sincos(ang, &sn, &cs);
+      const float c = (float)cs, s = (float)sn;
+      const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
+      x1 = y1;
+      x2 = y2;
+    }
+    row[j] = from_f32<T>(x1);
+    row[j + half] = from_f32<T>(x2);
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Host launchers.
 // ------------------------------------------------------------------------------------
 template <typename T>
@@ -470,6 +513,23 @@ hipError_t launch_combine(const void* h, const void* F, const int32_t* slot_row,
                                             d, (T*)y);
   return hipGetLastError();
 }
+
+template <typename T>
+hipError_t launch_qkv_rope_bias(void* qkv, long ld, const int32_t* count, int cap,
+                                const int32_t* packed_slot, int B, int P, int n_q, int n_kv,
+                                int dh, const void* bias, float theta, hipStream_t st) {
+  const long total = (long)cap * (n_q + 2 * n_kv) * (dh / 2);
+  const long blocks = (total + 255) / 256;
+  qkv_rope_bias_kernel<T><<<(int)(blocks < 4096 ? blocks : 4096), 256, 0, st>>>(
+      (T*)qkv, ld, count, cap, packed_slot, B, P, n_q, n_kv, dh, (const T*)bias, theta);
+  return hipGetLastError();
+}
+template hipError_t launch_qkv_rope_bias<float>(void*, long, const int32_t*, int, const int32_t*,
+                                                int, int, int, int, int, const void*, float,
+                                                hipStream_t);
+template hipError_t launch_qkv_rope_bias<bf16>(void*, long, const int32_t*, int, const int32_t*,
+                                               int, int, int, int, int, const void*, float,
+                                               hipStream_t);
 
 template <typename T>
 hipError_t launch_oproj_finish(const float* partial, int split, const void* H, void* h, int S,

@@ -29,6 +29,13 @@ hipError_t launch_combine_gate(const void* h, const void* F, const int32_t* slot
                                const int32_t* count, int cap, void* y, const int32_t* fold_src,
                                int N, int B, int d, float tau, float* ratio, uint8_t* recompute,
                                const void* g, float eps, void* An, int ld_an, hipStream_t st);
+// QKV bias (bias may be nullptr) and rotary embedding (theta > 0) on the K packed rows of
+// the Q|K|V buffer [cap, ld], in place; the packed row k sits at block position
+// packed_slot[k] % B, absolute position P + that.
+template <typename T>
+hipError_t launch_qkv_rope_bias(void* qkv, long ld, const int32_t* count, int cap,
+                                const int32_t* packed_slot, int B, int P, int n_q, int n_kv,
+                                int dh, const void* bias, float theta, hipStream_t st);
 size_t resolve_pack_lds_bytes(int S);
 hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,
                                const int32_t* src_in, int N, int B, int mode, int32_t* src_out,

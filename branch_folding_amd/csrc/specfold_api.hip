@@ -79,6 +79,8 @@ specfold_status check_shape(const specfold_shape* s, bool layer) {
                 s->n_q_heads, s->n_kv_heads);
   if (s->prefix_len < 0) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "prefix_len < 0");
   if (!(s->rms_eps >= 0.f)) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "rms_eps must be >= 0");
+  if (!(s->rope_theta >= 0.f) || s->rope_theta == __builtin_inff())
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "rope_theta must be finite and >= 0");
   return SPECFOLD_OK;
 }
 
@@ -237,6 +239,9 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = qkvd; gp.Kd = d; gp.bm = bm;
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
+  if (w->b_qkv || s->rope_theta > 0.f)
+    HIP_CHECK(launch_qkv_rope_bias<T>(QKV, L.ld_qkv, count, S, packed, B, s->prefix_len, nq,
+                                      nkv, dh, w->b_qkv, s->rope_theta, st));
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, false));
 
   AttnParams ap{};
@@ -321,9 +326,9 @@ specfold_status check_layer_params(const specfold_shape* shape,
   if (!weights || !weights->rms1 || !weights->w_qkv || !weights->w_o || !weights->rms2 ||
       !weights->w_gate_up || !weights->w_down)
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "every layer weight pointer is required%s", at);
-  const void* wp[6] = {weights->rms1, weights->w_qkv, weights->w_o, weights->rms2,
-                       weights->w_gate_up, weights->w_down};
-  for (int i = 0; i < 6; ++i)
+  const void* wp[7] = {weights->rms1, weights->w_qkv, weights->w_o, weights->rms2,
+                       weights->w_gate_up, weights->w_down, weights->b_qkv};
+  for (int i = 0; i < 7; ++i)
     if (!aligned16(wp[i]))
       return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "weight pointer %d is not 16-byte aligned%s", i,
                   at);

@@ -26,7 +26,7 @@ def to_device(x: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
 def shape_of(cfg, prefix_len: Optional[int] = None) -> L.Shape:
     return L.make_shape(cfg.num_nodes, cfg.block, cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim,
                         cfg.ffn, cfg.prefix if prefix_len is None else prefix_len, cfg.dtype,
-                        cfg.rms_eps)
+                        cfg.rms_eps, cfg.rope_theta)
 
 
 class DeviceLayer:

@@ -75,7 +75,12 @@ typedef enum specfold_dtype {
 
 /* Shape of one verify layer.  Supported: num_nodes >= 1, 1 <= block <= 1024,
  * num_nodes * block <= 16384, hidden and ffn multiples of 128, head_dim 64 or 128,
- * n_q_heads a multiple of n_kv_heads, prefix_len >= 0, rms_eps >= 0. */
+ * n_q_heads a multiple of n_kv_heads, prefix_len >= 0, rms_eps >= 0, rope_theta >= 0.
+ * rope_theta > 0 turns on the rotary position embedding (rotate-half form, as in the
+ * Llama / Qwen model families): after the QKV projection, the Q and K heads of the packed
+ * row of block position i are rotated at absolute position prefix_len + i, the pair
+ * (j, j + head_dim/2) by the angle (prefix_len + i) * rope_theta^(-2j/head_dim).  The
+ * prefix cache must hold keys that are already rotated.  0 = no rotary embedding. */
 typedef struct specfold_shape {
   int32_t num_nodes;
   int32_t block;
@@ -87,6 +92,7 @@ typedef struct specfold_shape {
   int32_t prefix_len;
   float rms_eps;
   int32_t dtype;       /* specfold_dtype */
+  float rope_theta;    /* rotary embedding base; 0 = none */
 } specfold_shape;
 
 /* Zero-copy strided view of the shared prefix cache (SpecFold explainer: the shared cache
@@ -106,6 +112,7 @@ typedef struct specfold_layer_weights {
   const void* rms2;
   const void* w_gate_up;
   const void* w_down;
+  const void* b_qkv;   /* [(n_q + 2 n_kv) dh] bias of the Q/K/V projections, or NULL */
 } specfold_layer_weights;
 
 /* Fold state of one layer (device buffers, S = num_nodes * block entries each).

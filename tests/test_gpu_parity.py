@@ -331,3 +331,33 @@ def test_layer_tall_row_tiles_reuse():
     err = max_abs_rel(dl.output_numpy(), oracle_layer(w, 0.05, state=ost, attn="reuse")["y"])
     _say(f"[gpu] tall reuse K={ost['K']} max-abs-rel={err:.3e}")
     assert err <= TOL[cfg.dtype]
+
+
+# Rotary embedding and QKV bias (model families with both): fp32 and bf16, dense and folded,
+# head_dim 64 and 128, a long prefix (the 256-query prefix kernel) with rope only.
+ROPE = [
+    custom_config(name="rope-bias-f32", num_nodes=6, block=10, hidden=128, n_q=2, n_kv=1,
+                  head_dim=64, ffn=128, prefix=21, dtype="f32", graph="dag", reveal=(1, 2),
+                  seed=81, rope_theta=10000.0, qkv_bias=True),
+    custom_config(name="rope-bias-bf16", num_nodes=9, block=24, hidden=256, n_q=4, n_kv=2,
+                  head_dim=128, ffn=256, prefix=70, dtype="bf16", graph="tree3",
+                  reveal=(1, 2), seed=82, rope_theta=1.0e6, qkv_bias=True),
+    custom_config(name="rope-longp-bf16", num_nodes=6, block=24, hidden=256, n_q=4, n_kv=2,
+                  head_dim=64, ffn=256, prefix=2100, dtype="bf16", graph="chain",
+                  reveal=(1, 2), seed=83, rope_theta=10000.0),
+]
+
+
+@pytest.mark.parametrize("cfg", ROPE, ids=lambda c: c.name)
+@pytest.mark.parametrize("tau", [-1.0, 0.05])
+def test_layer_rope_bias(cfg, tau):
+    L, DeviceLayer = _dev()
+    _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
+
+
+def test_cfg1_rope_bias_full_size():
+    """The 7B-shaped layer with the rotary embedding (base 10^6) and QKV bias of its model
+    family, every slot compared."""
+    L, DeviceLayer = _dev()
+    cfg = CONFIGS[1].with_(name="7b-layer-1+15-rope-bias", rope_theta=1.0e6, qkv_bias=True)
+    _check_layer(cfg, _workload(cfg), cfg.tau, L, DeviceLayer)
