@@ -7,7 +7,7 @@
 //   2. gemm_kernel<kEpiArgmax>: logits of the packed rows (gathered from An through
 //      packed_slot) against the [V, d] head, never stored: each wave keeps, per row, the
 //      largest of its 64 columns and the first such column;
-//   3. argmax_finish_kernel: one wave per packed row reduces those partials (first index
+//   3. argmax_finish_kernel: one block per packed row reduces those partials (first index
 //      of the maximum);
 //   4. token_gather_kernel: token[s] = row_token[slot_row[s]].
 #include "common.h"
@@ -15,40 +15,61 @@
 
 namespace specfold {
 
+// One 256-thread block per packed row: every thread scans P/256 partials (loads four at a
+// time), then the wave and the block reduce (first index of the maximum on ties).
+__device__ __forceinline__ void argmax_take(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
 __global__ void __launch_bounds__(256) argmax_finish_kernel(const float* __restrict__ val,
                                                             const int32_t* __restrict__ idx,
                                                             int P, const int32_t* __restrict__ count,
                                                             int cap, int V,
                                                             int32_t* __restrict__ row_token,
                                                             float* __restrict__ row_logit) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int K = imin(*count, cap);
-  for (int k = blockIdx.x * 4 + wave; k < K; k += gridDim.x * 4) {
+  for (int k = blockIdx.x; k < K; k += gridDim.x) {
     float bv = -__builtin_inff();
     int bi = 0x7fffffff;
     const float* v = val + (size_t)k * P;
     const int32_t* x = idx + (size_t)k * P;
-    for (int j = lane; j < P; j += 64) {
-      const float a = v[j];
-      const int b = x[j];
-      if (a > bv || (a == bv && b < bi)) {
-        bv = a;
-        bi = b;
+    for (int j0 = t; j0 < P; j0 += 4 * 256) {
+      float a[4];
+      int b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = imin(j0 + u * 256, P - 1);
+        a[u] = v[j];
+        b[u] = x[j];
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u * 256 < P) argmax_take(bv, bi, a[u], b[u]);
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float ov = __shfl_xor(bv, o, 64);
       const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+      argmax_take(bv, bi, ov, oi);
     }
     if (lane == 0) {
+      sv[wave] = bv;
+      si[wave] = bi;
+    }
+    __syncthreads();
+    if (t == 0) {
+#pragma unroll
+      for (int w = 1; w < 4; ++w) argmax_take(bv, bi, sv[w], si[w]);
       row_token[k] = (bi >= 0 && bi < V) ? bi : -1;   // -1: no finite logit in the row
       if (row_logit) row_logit[k] = bv;
     }
+    __syncthreads();
   }
 }
 
@@ -74,7 +95,7 @@ hipError_t launch_lm_head(const LmHeadParams& q, int num_cu, hipStream_t st) {
   gp.W = q.w; gp.ldw = q.d; gp.m_dev = q.count; gp.m_cap = S; gp.N = q.V; gp.Kd = q.d;
   gp.arg_val = q.arg_val; gp.arg_idx = q.arg_idx; gp.arg_ld = gemm_argmax_partials(q.V);
   if ((e = launch_gemm<T>(gp, kEpiArgmax, num_cu, st)) != hipSuccess) return e;
-  const int fgrid = ceil_div(S, 4) < 4 * num_cu ? ceil_div(S, 4) : 4 * num_cu;
+  const int fgrid = S < 4 * num_cu ? S : 4 * num_cu;
   argmax_finish_kernel<<<fgrid, 256, 0, st>>>(q.arg_val, q.arg_idx, gp.arg_ld, q.count, S, q.V,
                                                q.row_token, q.row_logit);
   if ((e = hipGetLastError()) != hipSuccess) return e;
