@@ -203,9 +203,10 @@ __global__ void __launch_bounds__(256) combine_gate_kernel(
 // ------------------------------------------------------------------------------------
 // Provenance + packing in one workgroup (SpecFold explainer, implementation memo: the
 // provenance kernel follows fold chains; the gate's packing compacts all branches'
-// recompute positions).  Provenance runs one thread per position along the nodes in
-// topological order; packing is a block-wide stable compaction (ballot + popcount +
-// per-wave offsets) in ascending slot id.  Working arrays live in LDS.
+// recompute positions).  Provenance follows every slot's fold chain at once by pointer
+// jumping (log2 of the chain length in rounds, not one step per node); packing is a
+// block-wide stable compaction (ballot + popcount + per-wave offsets) in ascending slot id.
+// Working arrays live in LDS.
 // ------------------------------------------------------------------------------------
 constexpr int kPackThreads = 1024;
 
@@ -244,7 +245,7 @@ __global__ void __launch_bounds__(kPackThreads) resolve_pack_kernel(
       else ps = f * B + (s - n * B);
     }
     rec_l[s] = own ? 1 : 0;
-    if (do_resolve) rank_l[s] = ps;
+    if (do_resolve) rank_l[s] = own ? s : ps;          // an own-row slot ends its chain
     else {
       int v = src_in[s];
       // a source must be an earlier-or-equal node; anything else is treated as the slot
@@ -255,14 +256,19 @@ __global__ void __launch_bounds__(kPackThreads) resolve_pack_kernel(
   }
   __syncthreads();
   if (do_resolve) {
-    // one thread per position walks the nodes in topological order, in LDS only
-    for (int i = t; i < B; i += kPackThreads) {
-      src_l[i] = 0;
-      for (int n = 1; n < N; ++n) {
-        const int s = n * B + i;
-        src_l[s] = rec_l[s] ? n : src_l[rank_l[s]];
-      }
+    // Pointer jumping: each slot points at its parent slot, a slot computing its own row at
+    // itself.  A parent has a smaller node id, so a chain has at most N-1 links; the first
+    // pointers skip one link and each round doubles that, so after ceil(log2(N-1)) rounds
+    // every pointer sits on the own-row slot its chain ends in.  The rounds ping-pong between
+    // rank_l and src_l (every pointer stays a valid slot id throughout).
+    int32_t* cur = rank_l;
+    int32_t* nxt = src_l;
+    for (int span = 1; span < N - 1; span <<= 1) {
+      for (int s = t; s < S; s += kPackThreads) nxt[s] = cur[cur[s]];
+      __syncthreads();
+      int32_t* tmp = cur; cur = nxt; nxt = tmp;
     }
+    for (int s = t; s < S; s += kPackThreads) src_l[s] = cur[s] / B;   // slot -> node
     __syncthreads();
     if (src_out)
       for (int s = t; s < S; s += kPackThreads) src_out[s] = src_l[s];

@@ -212,6 +212,50 @@ def test_pack_maximum_slots():
     np.testing.assert_array_equal(sr.cpu().numpy().reshape(256, 64), sr_o)
 
 
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 16, 17, 64, 256])
+def test_resolve_longest_chains(N):
+    """Provenance on a chain (node n folds onto n-1) with B = 64 positions: position i
+    recomputes at node n with probability i/64, so position 0 folds all the way to the root
+    (a chain of N-1 links, the longest there can be) and the rest cover every shorter length.
+    A second call gives one node a malformed fold source (not in [0, n)): resolve must treat
+    it as computing its own row at every position, so the oracle gets that node marked for
+    recompute; the pack takes that marked mask, as the gate hands it over in the layer."""
+    L, _ = _dev()
+    from branch_folding_amd.runner import shape_of
+    from oracle import pack, resolve
+    B = 64
+    cfg = custom_config(num_nodes=N, block=B, hidden=128)
+    sh = shape_of(cfg)
+    rng = np.random.default_rng(100 + N)
+    fs = np.arange(-1, N - 1, dtype=np.int32)
+    rec = rng.random((N, B)) < (np.arange(B) / B)[None, :]
+    rec[0] = True
+    cases = [(fs, rec, rec)]
+    if N >= 3:
+        bad = fs.copy()
+        bad[N // 2] = N // 2 if N % 2 else -7           # itself (not < n) or negative
+        rec_o = rec.copy()
+        rec_o[N // 2] = True
+        cases.append((bad, rec, rec_o))
+    for fs_dev, rec_dev, rec_oracle in cases:
+        _say(f"[gpu] resolve chain N={N}")
+        src = torch.empty(N * B, dtype=torch.int32, device="cuda")
+        ps = torch.empty(N * B, dtype=torch.int32, device="cuda")
+        sr = torch.empty(N * B, dtype=torch.int32, device="cuda")
+        cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+        rec_d = torch.from_numpy(rec_dev.reshape(-1).astype(np.uint8)).cuda()
+        L.specfold_resolve(sh, rec_d, torch.from_numpy(fs_dev).cuda(), src)
+        rec_p = torch.from_numpy(rec_oracle.reshape(-1).astype(np.uint8)).cuda()
+        L.specfold_pack(sh, rec_p, src, ps, sr, cnt)
+        torch.cuda.synchronize()
+        src_o = resolve(rec_oracle, np.arange(-1, N - 1, dtype=np.int32))
+        ps_o, sr_o, K = pack(rec_oracle, src_o)
+        np.testing.assert_array_equal(src.cpu().numpy().reshape(N, B), src_o)
+        assert int(cnt.item()) == K
+        np.testing.assert_array_equal(ps.cpu().numpy()[:K], ps_o)
+        np.testing.assert_array_equal(sr.cpu().numpy().reshape(N, B), sr_o)
+
+
 def test_cfg1_full_size():
     """The 7B-shaped layer (1 + 15 branches, tau = 0.05) in the benchmark's launch
     configuration, every output slot compared."""
