@@ -132,6 +132,24 @@ __device__ __forceinline__ void store_kv(T* Ks, T* Vt, const KVRegs<T, DH>& r) {
 // the normal range flush towards 0, which only drops weights under 2^-126 of the maximum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Prefix partial outputs (each split's normalised output rows) are stored in the model dtype:
+// the block phase re-reads a packed row's partials once for every slot that takes that row,
+// so bf16 layers halve those reads.  Four consecutive elements per access.
+__device__ __forceinline__ void st_part4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void st_part4(bf16* p, float a, float b, float c, float d) {
+  const bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ float4 ld_part4(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+__device__ __forceinline__ float4 ld_part4(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+
 // Online-softmax update of one 64-key tile for the lane's query: sc[t][r] holds the raw
 // score of key t*16 + (lane/16)*4 + r and becomes its unnormalised weight
 // 2^(score * scale_log2 - m).  Keys >= nkeys (a ragged last tile) get weight 0.  The
@@ -299,12 +317,11 @@ __global__ void __launch_bounds__(256, 2) attn_prefix_kernel(AttnParams p) {
     if (valid) {
       const float inv = st.l > 0.f ? 1.0f / st.l : 0.f;
       const float lse = st.l > 0.f ? st.m + log2f(st.l) : -__builtin_inff();
-      float* po = p.part_o + (((size_t)s * K + k) * p.n_q + h) * DH;
+      T* po = (T*)p.part_o + (((size_t)s * K + k) * p.n_q + h) * DH;
 #pragma unroll
-      for (int nt = 0; nt < A::NT; ++nt) {
-        float4 v = make_float4(o[nt][0] * inv, o[nt][1] * inv, o[nt][2] * inv, o[nt][3] * inv);
-        *reinterpret_cast<float4*>(po + nt * 16 + g4 * 4) = v;
-      }
+      for (int nt = 0; nt < A::NT; ++nt)
+        st_part4(po + nt * 16 + g4 * 4, o[nt][0] * inv, o[nt][1] * inv, o[nt][2] * inv,
+                 o[nt][3] * inv);
       if (g4 == 0) p.part_lse[((size_t)s * K + k) * p.n_q + h] = lse;
     }
   }
@@ -581,13 +598,11 @@ __global__ void __launch_bounds__(kTrWaves * 64, 1) attn_prefix_tr_kernel(AttnPa
       if (!valid[b]) continue;
       const float inv = st[b].l > 0.f ? 1.0f / st[b].l : 0.f;
       const float lse = st[b].l > 0.f ? st[b].m + log2f(st[b].l) : -__builtin_inff();
-      float* po = p.part_o + (((size_t)s * K + krow[b]) * p.n_q + hq[b]) * DH;
+      bf16* po = (bf16*)p.part_o + (((size_t)s * K + krow[b]) * p.n_q + hq[b]) * DH;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float4 v = make_float4(o[b][nt][0] * inv, o[b][nt][1] * inv, o[b][nt][2] * inv,
-                                     o[b][nt][3] * inv);
-        *reinterpret_cast<float4*>(po + nt * 16 + g4 * 4) = v;
-      }
+      for (int nt = 0; nt < NT; ++nt)
+        st_part4(po + nt * 16 + g4 * 4, o[b][nt][0] * inv, o[b][nt][1] * inv,
+                 o[b][nt][2] * inv, o[b][nt][3] * inv);
       if (g4 == 0) p.part_lse[((size_t)s * K + krow[b]) * p.n_q + hq[b]] = lse;
     }
   }
@@ -608,7 +623,7 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-template <int DH>
+template <typename T, int DH>
 __device__ __forceinline__ void merge_row(const AttnParams& p, int K, int ns, int row, int lane) {
   constexpr int E = DH / 64;                  // output elements per lane
   constexpr int SB = 8;                       // splits per batch of loads
@@ -628,9 +643,9 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, int K, int ns, in
         const int sb = imin(s0 + b, ns - 1);
         ws[b] = s0 + b < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sb))
                             : 0.f;
-        const float* po = p.part_o + ((size_t)sb * plane_l + row) * DH + lane * E;
+        const T* po = (const T*)p.part_o + ((size_t)sb * plane_l + row) * DH + lane * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[b][e] = po[e];
+        for (int e = 0; e < E; ++e) v[b][e] = to_f32(po[e]);
       }
 #pragma unroll
       for (int b = 0; b < SB; ++b)
@@ -638,10 +653,10 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, int K, int ns, in
         for (int e = 0; e < E; ++e) acc[e] += ws[b] * v[b][e];
     }
   }
-  float* po = p.part_o + (size_t)row * DH + lane * E;
+  T* po = (T*)p.part_o + (size_t)row * DH + lane * E;
   const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) po[e] = acc[e] * inv;
+  for (int e = 0; e < E; ++e) po[e] = from_f32<T>(acc[e] * inv);
   if (lane == 0) p.part_lse[row] = l > 0.f ? m + log2f(l) : -__builtin_inff();
 }
 
@@ -654,7 +669,7 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnParams p) {
   const int ns = attn_splits(K, g, p.n_kv, p.P, DH, EB);
   const int lane = threadIdx.x & 63;
   for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < K * p.n_q; row += gridDim.x * 4)
-    merge_row<DH>(p, K, ns, row, lane);
+    merge_row<T, DH>(p, K, ns, row, lane);
 }
 
 // ------------------------------------------------------------------------------------
@@ -717,10 +732,9 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
         const int sb = imin(s0 + b, ns - 1);
         const size_t prow = ((size_t)sb * K + k) * p.n_q + h;
         ls[b] = (s0 + b < ns) ? p.part_lse[prow] : -__builtin_inff();
-        const float* pp = p.part_o + prow * DH;
+        const T* pp = (const T*)p.part_o + prow * DH;
 #pragma unroll
-        for (int nt = 0; nt < A::NT; ++nt)
-          po[b][nt] = *reinterpret_cast<const float4*>(pp + nt * 16 + g4 * 4);
+        for (int nt = 0; nt < A::NT; ++nt) po[b][nt] = ld_part4(pp + nt * 16 + g4 * 4);
       }
       float mb = st.m;
 #pragma unroll

@@ -189,7 +189,7 @@ struct AttnParams {
   long stride_tok, stride_head;
   int P;
   float scale_log2;
-  float* part_o;         // [nsplit][K][n_q][dh]  (K = device packed count)
+  void* part_o;          // [nsplit][K][n_q][dh] in the model dtype (K = device packed count)
   float* part_lse;       // [nsplit][K][n_q]
   int S;
   const int32_t* slot_row;

@@ -251,7 +251,7 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   ap.stride_tok = prefix ? prefix->stride_tok : 0; ap.stride_head = prefix ? prefix->stride_head : 0;
   ap.P = s->prefix_len;
   ap.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
-  ap.part_o = (float*)(ws + L.part_o); ap.part_lse = (float*)(ws + L.part_lse);
+  ap.part_o = ws + L.part_o; ap.part_lse = (float*)(ws + L.part_lse);
   ap.S = S; ap.slot_row = slot_row; ap.N = N; ap.B = B; ap.out = ATT; ap.ld_out = L.ld_q;
   HIP_CHECK(mark(SPECFOLD_STEP_ATTN_PREFIX, true));
   HIP_CHECK(launch_attn_prefix<T>(ap, cus, st));
