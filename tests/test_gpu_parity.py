@@ -90,6 +90,18 @@ TALL = [
 ]
 
 
+# Rows longer than the gate's register-held part (512 16-byte chunks: hidden > 2048 in fp32,
+# > 4096 in bf16): the gate's tail loop for the ratio sums and the normalised rows.
+WIDE = [
+    custom_config(name="wide-f32", num_nodes=4, block=12, hidden=2304, n_q=2, n_kv=1,
+                  head_dim=64, ffn=256, prefix=20, dtype="f32", graph="tree3", reveal=(1, 2),
+                  seed=71),
+    custom_config(name="wide-bf16", num_nodes=5, block=9, hidden=4224, n_q=4, n_kv=2,
+                  head_dim=64, ffn=384, prefix=33, dtype="bf16", graph="dag", reveal=(1, 2),
+                  seed=72),
+]
+
+
 def _check_layer(cfg, w, tau, L, DeviceLayer, slots=None):
     _say(f"[gpu] layer {cfg.name} tau={tau} S={cfg.slots}")
     dl = DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src)
@@ -135,6 +147,13 @@ def test_layer_small(cfg, tau):
     L, DeviceLayer = _dev()
     w = _workload(cfg)
     _check_layer(cfg, w, tau, L, DeviceLayer)
+
+
+@pytest.mark.parametrize("cfg", WIDE, ids=lambda c: c.name)
+@pytest.mark.parametrize("tau", [-1.0, 0.05, 0.3, math.inf])
+def test_layer_wide_rows(cfg, tau):
+    L, DeviceLayer = _dev()
+    _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
 
 
 @pytest.mark.parametrize("cfg", LONG_PREFIX, ids=lambda c: c.name)

@@ -163,7 +163,7 @@ def _check_stack(cfg, nl, tau, L, runner):
 
 
 # small stacks: fp32 and bf16, benchmark-strength (0.02) and stronger weights that move
-# the recompute set from layer to layer, ragged blocks, no prefix
+# the recompute set from layer to layer, ragged blocks, no prefix, wide rows
 SMALL = [
     custom_config(name="stack-f32", num_nodes=6, block=8, hidden=128, n_q=2, n_kv=1,
                   head_dim=64, ffn=256, prefix=16, graph="tree3", reveal=(1, 2), layers=4,
@@ -174,6 +174,12 @@ SMALL = [
     custom_config(name="stack-bf16-noprefix", num_nodes=7, block=16, hidden=128, n_q=2,
                   n_kv=2, head_dim=64, ffn=128, prefix=0, dtype="bf16", graph="chain",
                   reveal=(1, 2), layers=3, seed=43),
+    # rows of more than 512 16-byte chunks: combine and the next gate run as two kernels.
+    # Weight std 0.02: at hidden 4224 a std of 0.06 makes attention scores reach ~40, where
+    # the bf16 rounding of q and k alone moves the softmax beyond the bf16 tolerance.
+    custom_config(name="stack-wide-bf16", num_nodes=4, block=8, hidden=4224, n_q=2, n_kv=1,
+                  head_dim=64, ffn=256, prefix=16, dtype="bf16", graph="tree3",
+                  reveal=(1, 2), layers=3, seed=44, weight_std=0.02),
 ]
 
 
