@@ -255,6 +255,16 @@ __device__ __forceinline__ void attend_tile(const T* Ks, const T* Vt, int nkeys,
 // ------------------------------------------------------------------------------------
 // Prefix phase.
 // ------------------------------------------------------------------------------------
+// The prefix phase records its split count and the merge decision for this call's packed
+// count (one thread of workgroup 0), so the later attention kernels need not evaluate the
+// cost model again in every workgroup.  Without a prefix the phase is not launched and the
+// readers use ns = 0.
+__device__ __forceinline__ void write_plan(const AttnParams& p, int K, int g, int ns, int dh,
+                                           int eb) {
+  p.plan[0] = ns;
+  p.plan[1] = attn_merge_on(K, g, p.n_kv, p.P, p.S, dh, eb) ? 1 : 0;
+}
+
 // fp32 and short bf16 prefixes: 64-query units, K/V tiles staged through registers (V
 // transposed on the way into LDS), two workgroups per CU.
 template <typename T, int DH>
@@ -266,6 +276,7 @@ __global__ void __launch_bounds__(256, 2) attn_prefix_kernel(AttnParams p) {
   const int K = imin(*p.count, p.cap);
   const int g = p.n_q / p.n_kv;
   const int ns = attn_splits(K, g, p.n_kv, p.P, DH, (int)sizeof(T));
+  if (blockIdx.x == 0 && threadIdx.x == 0) write_plan(p, K, g, ns, DH, (int)sizeof(T));
   if (ns == 0) return;
   const int qtiles = ceil_div(K * g, kQRows);
   const int units = p.n_kv * qtiles * ns;
@@ -465,6 +476,7 @@ __global__ void __launch_bounds__(kTrWaves * 64, 1) attn_prefix_tr_kernel(AttnPa
   const int K = imin(*p.count, p.cap);
   const int g = p.n_q / p.n_kv;
   const int ns = attn_splits(K, g, p.n_kv, p.P, DH, 2);
+  if (blockIdx.x == 0 && threadIdx.x == 0) write_plan(p, K, g, ns, DH, 2);
   if (ns == 0) return;
   const int rows = K * g;
   const int qtiles = ceil_div(rows, kTrQRows);
@@ -663,10 +675,8 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, int K, int ns, in
 template <typename T, int DH>
 __global__ void __launch_bounds__(256) attn_merge_kernel(AttnParams p) {
   const int K = imin(*p.count, p.cap);
-  const int g = p.n_q / p.n_kv;
-  constexpr int EB = (int)sizeof(T);
-  if (!attn_merge_on(K, g, p.n_kv, p.P, p.S, DH, EB)) return;
-  const int ns = attn_splits(K, g, p.n_kv, p.P, DH, EB);
+  if (p.P <= 0 || K <= 0 || p.plan[1] == 0) return;
+  const int ns = p.plan[0];
   const int lane = threadIdx.x & 63;
   for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < K * p.n_q; row += gridDim.x * 4)
     merge_row<T, DH>(p, K, ns, row, lane);
@@ -681,12 +691,13 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
   constexpr int VE = A::VE;
   __shared__ __attribute__((aligned(16))) T Ks[kKeys * A::LDK];
   __shared__ __attribute__((aligned(16))) T Vt[DH * A::LDV];
+  // the plan is loaded with the count (without a prefix it is not written and not used)
+  const int plan_ns = p.plan[0], plan_merged = p.plan[1];
   const int K = imin(*p.count, p.cap);
   if (K <= 0) return;
   const int g = p.n_q / p.n_kv;
   // plane 0 holds all prefix splits when attn_merge_kernel merged them
-  constexpr int EB = (int)sizeof(T);
-  const int ns = attn_merge_on(K, g, p.n_kv, p.P, p.S, DH, EB) ? 1 : attn_splits(K, g, p.n_kv, p.P, DH, EB);
+  const int ns = p.P <= 0 ? 0 : (plan_merged ? 1 : plan_ns);
   const int qtiles = ceil_div(p.B * g, kQRows);
   const int units = p.N * p.n_kv * qtiles;
   const int kchunks = ceil_div(p.B, kKeys);

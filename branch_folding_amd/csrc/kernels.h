@@ -196,6 +196,10 @@ struct AttnParams {
   int N, B;
   void* out;             // [S, n_q dh]
   long ld_out;
+  // [2] workspace: the prefix splits and whether they are merged before the block phase, for
+  // the packed count of this call.  The prefix phase writes it; the split merge and the block
+  // phase load it next to the count instead of re-deriving both in every workgroup.
+  int32_t* plan;
 };
 
 constexpr int kAttnMaxSplit = 32;

@@ -108,7 +108,7 @@ size_t padded_ld(size_t cols, size_t eb) { return cols + 128 / eb; }
 // Workspace layout of one layer.
 struct Layout {
   size_t ratio, rec, src, packed, slot_row, count;
-  size_t qkv, part_o, part_lse, attn, h, a2, G, F, gpart;
+  size_t qkv, part_o, part_lse, attn, h, a2, G, F, gpart, plan;
   size_t total;
   size_t ld_d, ld_qkv, ld_q, ld_ff;   // padded row strides (elements)
 };
@@ -143,6 +143,7 @@ Layout layout_of(const specfold_shape* s) {
   L.packed = take(S * 4);
   L.slot_row = take(S * 4);
   L.count = take(256);
+  L.plan = take(256);
   L.qkv = take(S * L.ld_qkv * eb);
   L.part_o = take(prow * qd * 4);
   L.part_lse = take(prow * (size_t)s->n_q_heads * 4);
@@ -252,6 +253,7 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   ap.P = s->prefix_len;
   ap.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
   ap.part_o = ws + L.part_o; ap.part_lse = (float*)(ws + L.part_lse);
+  ap.plan = (int32_t*)(ws + L.plan);
   ap.S = S; ap.slot_row = slot_row; ap.N = N; ap.B = B; ap.out = ATT; ap.ld_out = L.ld_q;
   HIP_CHECK(mark(SPECFOLD_STEP_ATTN_PREFIX, true));
   HIP_CHECK(launch_attn_prefix<T>(ap, cus, st));
