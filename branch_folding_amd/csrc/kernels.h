@@ -218,16 +218,21 @@ struct AttnPlan {
 __host__ __device__ inline AttnPlan attn_plan(int elem_bytes, int P) {
   return attn_use_tr(elem_bytes, P) ? AttnPlan{256, kPlanCUs} : AttnPlan{64, 2 * kPlanCUs};
 }
-// Prefix key splits per (KV head, query tile) unit, a power of two.  A unit streams
-// ceil(chunks / s) key tiles and the grid runs `slots` units at a time (a power of two), so
-// the prefix phase takes about ceil(units * s / slots) rounds of that many tiles.  Each
-// split also costs its partial rows: K*g*n_kv rows of dh+1 floats written, merged and read
-// again, about rows*(dh+1) / 2^18 quarter tiles at the measured tile time and partial
-// traffic rate.  s minimises the sum (in quarter tiles).  Every workgroup of the attention
-// kernels evaluates this on the device, so it uses shifts only.
+// Prefix key splits per (KV head, query tile) unit.  A unit streams ceil(chunks / s) key
+// tiles and the grid runs `slots` units at a time (a power of two), so the prefix phase
+// takes about ceil(units * s / slots) rounds of that many tiles.  Each split also costs its
+// partial rows: K*g*n_kv rows of dh+1 values written, merged and read again, about
+// rows*(dh+1) / 2^18 quarter tiles at the measured tile time and partial traffic rate.  s
+// minimises the sum (in quarter tiles) over a short candidate list: powers of two and the
+// counts between them that can fill the last round (at 1+63 branches over a 16384-key prefix,
+// 5 splits make 760 units, three full rounds of 256, where 8 make 4.75 rounds).  The prefix
+// phase evaluates this in every workgroup, so it costs one 32-bit division per candidate.
 __host__ __device__ inline int attn_splits(int K, int g, int n_kv, int P, int dh,
                                            int elem_bytes) {
   if (P <= 0 || K <= 0) return 0;
+  constexpr int kCands[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32};
+  static_assert(kCands[sizeof(kCands) / sizeof(kCands[0]) - 1] <= kAttnMaxSplit,
+                "split candidates exceed the merge's lane count");
   const AttnPlan pl = attn_plan(elem_bytes, P);
   const int lslots = pl.slots == 2 * kPlanCUs ? 9 : 8;   // log2 of 512 / 256
   const int units = n_kv * ((K * g + pl.qrows - 1) / pl.qrows);
@@ -236,10 +241,11 @@ __host__ __device__ inline int attn_splits(int K, int g, int n_kv, int P, int dh
   const int split_cost = per_split < 1 ? 1 : (int)per_split;
   int best = 1;
   long best_cost = -1;
-  for (int ls = 0; (1 << ls) <= kAttnMaxSplit && ((1 << ls) <= chunks / 2 || ls == 0); ++ls) {
-    const int s = 1 << ls;
+  for (int c = 0; c < (int)(sizeof(kCands) / sizeof(kCands[0])); ++c) {
+    const int s = kCands[c];
+    if (s > 1 && s > chunks / 2) break;                  // every split keeps >= 2 tiles
     const long rounds = ((long)units * s + (1 << lslots) - 1) >> lslots;
-    const long cost = rounds * ((chunks + s - 1) >> ls) * 4 + (long)s * split_cost;
+    const long cost = rounds * ((chunks + s - 1) / s) * 4 + (long)s * split_cost;
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
       best = s;
