@@ -216,11 +216,41 @@ __device__ __forceinline__ bool node_ok(const int32_t* fold_src, int n) {
   return p >= 0 && p < n;
 }
 
+// Workgroups 1.. of the provenance + packing launch have nothing to pack: each reads one
+// slice of the next GEMM's weights once and discards it, so those bytes sit in the
+// memory-side cache when that GEMM starts (the packing itself occupies one CU).  16 MB is
+// what the other CUs read in about the time the packing takes: at the 7B layer the QKV GEMM
+// gets 1.6 us faster and the launch no longer; the whole 33 MB made the launch 4 us longer.
+constexpr long kPackPrefetchBytes = 16L << 20;
+
+__device__ __forceinline__ void prefetch_slice(const uint4* __restrict__ src, long n16,
+                                               int part, int parts, int* sink) {
+  const long per = (n16 + parts - 1) / parts;
+  const long b = (long)part * per, e = b + per < n16 ? b + per : n16;
+  uint32_t acc = 0;
+  for (long i0 = b + threadIdx.x; i0 < e; i0 += 8L * kPackThreads) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const long i = i0 + (long)j * kPackThreads;
+      v[j] = i < e ? src[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].w;
+  }
+  if (sink != nullptr && acc == 0x9e3779b9u) *sink = (int)acc;   // keeps the loads (sink is null)
+}
+
 __global__ void __launch_bounds__(kPackThreads) resolve_pack_kernel(
     const uint8_t* __restrict__ recompute, const int32_t* __restrict__ fold_src,
     const int32_t* __restrict__ src_in, int N, int B, int mode,
     int32_t* __restrict__ src_out, int32_t* __restrict__ packed_slot,
-    int32_t* __restrict__ slot_row, int32_t* __restrict__ packed_count) {
+    int32_t* __restrict__ slot_row, int32_t* __restrict__ packed_count,
+    const uint4* __restrict__ pf, long pf_n16, int* pf_sink) {
+  if (blockIdx.x > 0) {
+    prefetch_slice(pf, pf_n16, blockIdx.x - 1, gridDim.x - 1, pf_sink);
+    return;
+  }
   extern __shared__ int32_t lds[];
   const int S = N * B;
   int32_t* src_l = lds;                               // [S] source node of each slot
@@ -497,6 +527,7 @@ size_t resolve_pack_lds_bytes(int S) {
 hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,
                                const int32_t* src_in, int N, int B, int mode, int32_t* src_out,
                                int32_t* packed_slot, int32_t* slot_row, int32_t* count,
+                               const void* prefetch, size_t prefetch_bytes, int num_cu,
                                hipStream_t st) {
   const size_t lds = resolve_pack_lds_bytes(N * B);
   if (lds > 64 * 1024) {
@@ -504,8 +535,13 @@ hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  resolve_pack_kernel<<<1, kPackThreads, lds, st>>>(recompute, fold_src, src_in, N, B, mode,
-                                                     src_out, packed_slot, slot_row, count);
+  long n16 = (long)((prefetch_bytes < (size_t)kPackPrefetchBytes ? prefetch_bytes
+                                                               : (size_t)kPackPrefetchBytes) / 16);
+  if (prefetch == nullptr || (((uintptr_t)prefetch) & 15u) != 0) n16 = 0;
+  const int grid = n16 > 0 ? num_cu : 1;
+  resolve_pack_kernel<<<grid, kPackThreads, lds, st>>>(recompute, fold_src, src_in, N, B, mode,
+                                                        src_out, packed_slot, slot_row, count,
+                                                        (const uint4*)prefetch, n16, nullptr);
   return hipGetLastError();
 }
 

@@ -37,9 +37,12 @@ hipError_t launch_qkv_rope_bias(void* qkv, long ld, const int32_t* count, int ca
                                 const int32_t* packed_slot, int B, int P, int n_q, int n_kv,
                                 int dh, const void* bias, float theta, hipStream_t st);
 size_t resolve_pack_lds_bytes(int S);
+// prefetch (may be nullptr): up to a fixed number of its bytes are read by otherwise idle
+// workgroups of the same launch, so the following kernel finds them in the memory-side cache.
 hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src,
                                const int32_t* src_in, int N, int B, int mode, int32_t* src_out,
                                int32_t* packed_slot, int32_t* slot_row, int32_t* count,
+                               const void* prefetch, size_t prefetch_bytes, int num_cu,
                                hipStream_t st);
 template <typename T>
 hipError_t launch_combine(const void* h, const void* F, const int32_t* slot_row,

@@ -223,7 +223,8 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   if (!state_in) {
     HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, true));
     HIP_CHECK(launch_resolve_pack(rec, fold_src, nullptr, N, B, kResolve | kPack, src, packed,
-                                  slot_row, count, st));
+                                  slot_row, count, w->w_qkv, (size_t)qkvd * d * sizeof(T), cus,
+                                  st));
     HIP_CHECK(mark(SPECFOLD_STEP_RESOLVE_PACK, false));
   }
   void* QKV = ws + L.qkv;
@@ -454,7 +455,7 @@ specfold_status specfold_resolve(const specfold_shape* shape, const uint8_t* rec
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "recompute, fold_src and src_node are required");
   (void)hipGetLastError();
   HIP_CHECK(launch_resolve_pack(recompute, fold_src, nullptr, shape->num_nodes, shape->block,
-                                kResolve, src_node, nullptr, nullptr, nullptr,
+                                kResolve, src_node, nullptr, nullptr, nullptr, nullptr, 0, 0,
                                 (hipStream_t)stream));
   return ok();
 }
@@ -469,8 +470,8 @@ specfold_status specfold_pack(const specfold_shape* shape, const uint8_t* recomp
                 "recompute, src_node, packed_slot, slot_row and packed_count are required");
   (void)hipGetLastError();
   HIP_CHECK(launch_resolve_pack(recompute, nullptr, src_node, shape->num_nodes, shape->block,
-                                kPack, nullptr, packed_slot, slot_row, packed_count,
-                                (hipStream_t)stream));
+                                kPack, nullptr, packed_slot, slot_row, packed_count, nullptr, 0,
+                                0, (hipStream_t)stream));
   return ok();
 }
 
