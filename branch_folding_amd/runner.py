@@ -109,36 +109,43 @@ class DeviceStack:
 
     def __init__(self, cfg, layers, H: np.ndarray, fold_src: np.ndarray, device="cuda:0"):
         """layers: iterable of (weights dict, interleaved prefix cache) per layer; each is
-        uploaded as it is produced, so host memory holds one layer at a time."""
+        uploaded as it is produced, so host memory holds one layer at a time.  More layers
+        can be appended with add_layer() before the first call."""
         self.cfg = cfg
         self.device = torch.device(device)
         dt = torch_dtype(cfg)
         self.dt = dt
         self.shape = shape_of(cfg)
-        self.w, self.caches, self.prefix = [], [], []
-        n_kv, dh = cfg.n_kv, cfg.head_dim
-        for weights, cache in layers:
-            self.w.append({k: to_device(v, dt, self.device) for k, v in weights.items()})
-            c = to_device(cache, dt, self.device)
-            self.caches.append(c)
-            self.prefix.append((c[0, 0].data_ptr(), c[0, 1].data_ptr(), 2 * n_kv * dh, dh))
-        self.num_layers = len(self.w)
+        self.w, self.caches, self.prefix, self.states = [], [], [], []
         S, d = cfg.slots, cfg.hidden
         self.H = to_device(H.reshape(S, d), dt, self.device)
         self.out = torch.empty((S, d), dtype=dt, device=self.device)
         self.fold_src = torch.from_numpy(np.asarray(fold_src, dtype=np.int32)).to(self.device)
-        self.states = []
-        for _ in range(self.num_layers):
-            self.states.append({
-                "ratio": torch.empty(S, dtype=torch.float32, device=self.device),
-                "recompute": torch.empty(S, dtype=torch.uint8, device=self.device),
-                "src_node": torch.empty(S, dtype=torch.int32, device=self.device),
-                "packed_slot": torch.empty(S, dtype=torch.int32, device=self.device),
-                "slot_row": torch.empty(S, dtype=torch.int32, device=self.device),
-                "packed_count": torch.zeros(1, dtype=torch.int32, device=self.device),
-            })
+        for weights, cache in layers:
+            self.add_layer(weights, cache)
         self.ws_bytes = L.specfold_stack_workspace_bytes(self.shape)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+
+    @property
+    def num_layers(self) -> int:
+        return len(self.w)
+
+    def add_layer(self, weights: Dict[str, np.ndarray], cache: np.ndarray) -> None:
+        """Upload one more layer's weights and prefix cache, with its fold-state buffers."""
+        cfg, dt, S = self.cfg, self.dt, self.cfg.slots
+        n_kv, dh = cfg.n_kv, cfg.head_dim
+        self.w.append({k: to_device(v, dt, self.device) for k, v in weights.items()})
+        c = to_device(cache, dt, self.device)
+        self.caches.append(c)
+        self.prefix.append((c[0, 0].data_ptr(), c[0, 1].data_ptr(), 2 * n_kv * dh, dh))
+        self.states.append({
+            "ratio": torch.empty(S, dtype=torch.float32, device=self.device),
+            "recompute": torch.empty(S, dtype=torch.uint8, device=self.device),
+            "src_node": torch.empty(S, dtype=torch.int32, device=self.device),
+            "packed_slot": torch.empty(S, dtype=torch.int32, device=self.device),
+            "slot_row": torch.empty(S, dtype=torch.int32, device=self.device),
+            "packed_count": torch.zeros(1, dtype=torch.int32, device=self.device),
+        })
 
     def load_states(self, states) -> None:
         """Copy per-layer fold states (recompute, src_node, packed_slot, slot_row,

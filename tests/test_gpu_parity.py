@@ -102,6 +102,40 @@ WIDE = [
 ]
 
 
+def _check_intermediates(dl, cfg, ref, K, L, tag, attn_slots=None):
+    """Every intermediate the workspace keeps, element-wise against the oracle's, each to
+    the output tolerance (max-abs-rel over the entries the oracle evaluated):
+      * the packed Q|K|V rows (after bias and rotary embedding, if any), first K rows;
+      * the attention output o of every slot -- a folded slot's o is corrected against
+        its own branch's block keys and values, which y alone cannot show (the residual
+        stream dominates y);
+      * h = H + o W_o^T of every slot;
+      * the packed FFN output rows F.
+    attn_slots: bool [N, B] restricting the o check (REUSE: the packed slots)."""
+    S, tol = cfg.slots, TOL[cfg.dtype]
+
+    def host(which):
+        return dl.intermediate(which).float().cpu().numpy().astype(np.float64)
+
+    qkv_ref = np.concatenate([ref["Q"].reshape(K, -1), ref["K_"].reshape(K, -1),
+                              ref["V"].reshape(K, -1)], axis=1)
+    o_ref = ref["o"].reshape(S, -1).copy()
+    if attn_slots is not None:
+        o_ref[~attn_slots.reshape(-1)] = np.nan
+    checks = [("qkv", host(L.SPECFOLD_T_QKV)[:K], qkv_ref),
+              ("o", host(L.SPECFOLD_T_ATTN), o_ref),
+              ("h", host(L.SPECFOLD_T_H), ref["h"].reshape(S, -1)),
+              ("F", host(L.SPECFOLD_T_FFN)[:K], ref["F"].reshape(K, -1))]
+    msg = []
+    for name, got, want in checks:
+        rows = np.all(np.isfinite(want), axis=1)        # rows the oracle evaluated
+        assert rows.any(), name
+        err = max_abs_rel(got[rows], want[rows])
+        msg.append(f"{name}={err:.2e}")
+        assert err <= tol, (tag, name, err, tol)
+    _say(f"[gpu]   {tag} intermediates " + " ".join(msg))
+
+
 def _check_layer(cfg, w, tau, L, DeviceLayer, slots=None):
     _say(f"[gpu] layer {cfg.name} tau={tau} S={cfg.slots}")
     dl = DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src)
@@ -112,12 +146,13 @@ def _check_layer(cfg, w, tau, L, DeviceLayer, slots=None):
     masks_agree = assert_fold_state_equal(gst, ost, tau)
     y_gpu = dl.output_numpy()
     tol = TOL[cfg.dtype]
+    ref = oracle_layer(w, tau, state=ost, slots=slots)
+    sel = np.ones(y_gpu.shape[:2], bool) if slots is None else _slot_mask(cfg, slots)
     if masks_agree:
-        ref = oracle_layer(w, tau, state=ost, slots=slots)
-        sel = np.ones(y_gpu.shape[:2], bool) if slots is None else _slot_mask(cfg, slots)
         err = max_abs_rel(y_gpu[sel], ref["y"][sel])
         _say(f"[gpu]   K={gst['K']} max-abs-rel={err:.3e} (tol {tol})")
         assert err <= tol
+        _check_intermediates(dl, cfg, ref, ost["K"], L, "own-state")
     # conditioned on the oracle's fold state
     y_in = dl.forward(tau, state_in=dict(recompute=ost["recompute"], src_node=ost["src"],
                                          packed_slot=np.pad(ost["packed_slot"],
@@ -126,11 +161,10 @@ def _check_layer(cfg, w, tau, L, DeviceLayer, slots=None):
                                          packed_count=np.array([ost["K"]])))
     torch.cuda.synchronize()
     y_in = y_in.float().cpu().numpy().reshape(y_gpu.shape)
-    ref = oracle_layer(w, tau, state=ost, slots=slots)
-    sel = np.ones(y_gpu.shape[:2], bool) if slots is None else _slot_mask(cfg, slots)
     err = max_abs_rel(y_in[sel], ref["y"][sel])
     _say(f"[gpu]   state-in max-abs-rel={err:.3e}")
     assert err <= tol
+    _check_intermediates(dl, cfg, ref, ost["K"], L, "state-in")
     return dl, gst, ost
 
 
@@ -355,6 +389,8 @@ def test_layer_reuse_attention(cfg, tau):
     err = max_abs_rel(y, ref["y"])
     _say(f"[gpu]   K={st['K']} max-abs-rel={err:.3e} (tol {tol})")
     assert err <= tol
+    # the O projection reads only the packed rows' attention output here
+    _check_intermediates(dl, cfg, ref, st["K"], L, "reuse", attn_slots=st["recompute"])
     src = st["src"]
     scale = np.max(np.abs(y))
     worst = 0.0
@@ -424,3 +460,78 @@ def test_cfg1_rope_bias_full_size():
     L, DeviceLayer = _dev()
     cfg = CONFIGS[1].with_(name="7b-layer-1+15-rope-bias", rope_theta=1.0e6, qkv_bias=True)
     _check_layer(cfg, _workload(cfg), cfg.tau, L, DeviceLayer)
+
+
+def _golden_gate_rows(hidden):
+    """The hand-built rows of tests/golden/gate_cases.json (exact rational ratios from
+    Pythagorean triples; zero-norm parents), spread over a `hidden`-wide row at columns
+    that fall into different lanes and 16-byte chunks (zero columns change neither norm),
+    plus rows that are not in that file: a NaN in the child, a NaN in the parent, and an
+    identical pair that must fold at tau = 0.  Returns (parent rows, child rows, exact
+    ratios as (num, den), den = 0 for +inf and None for NaN)."""
+    import json
+    import os
+    spec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "gate_cases.json")))
+    cols = [0, 37, 64, hidden - 1]
+    par, chi, want = [], [], []
+    for case in spec["cases"]:
+        p = np.zeros(hidden, np.float32)
+        c = np.zeros(hidden, np.float32)
+        p[cols] = case["parent"]
+        c[cols] = case["child"]
+        par.append(p)
+        chi.append(c)
+        want.append((case["r_num"], case["r_den"]))
+    base = np.zeros(hidden, np.float32)
+    base[cols] = [3, 4, 12, 0]                            # ||p|| = 13
+    nan_c = base.copy()
+    nan_c[5] = np.nan
+    nan_p = base.copy()
+    nan_p[70] = np.nan
+    for p, c, r in ((base, nan_c, None), (nan_p, base, None), (base, base.copy(), (0, 1))):
+        par.append(p)
+        chi.append(c)
+        want.append(r)
+    return np.stack(par), np.stack(chi), want
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gate_golden_cases(dtype):
+    """specfold_gate on the hand-built rows: the ratio of every finite case equals the
+    exact rational to fp32 rounding, a zero-norm parent gives 0 (equal rows) or +inf, a
+    NaN anywhere in either row gives NaN and recomputes, and the decision fold iff
+    r <= tau holds at tau = 0 (identical rows fold), at tau equal to a case's exact
+    ratio (1 and 1/2 fold), between ratios, at +inf (every finite ratio folds) and below
+    zero (nothing folds).  The root's rows always recompute with r = +inf."""
+    L, _ = _dev()
+    from branch_folding_amd.runner import shape_of
+    d = 128
+    par, chi, want = _golden_gate_rows(d)
+    B = len(want)
+    cfg = custom_config(num_nodes=2, block=B, hidden=d, dtype=dtype)
+    sh = shape_of(cfg)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    H = torch.from_numpy(np.concatenate([par, chi])).to(tdt).cuda()    # every value is bf16-exact
+    fs = torch.tensor([-1, 0], dtype=torch.int32, device="cuda")
+    exact = np.array([np.nan if r is None else (math.inf if r[1] == 0 else r[0] / r[1])
+                      for r in want])
+    for tau in (1.0, 0.5, 0.0, 0.75, math.inf, -1.0):
+        _say(f"[gpu] gate golden {dtype} tau={tau}")
+        ratio = torch.empty(2 * B, device="cuda")
+        rec = torch.empty(2 * B, dtype=torch.uint8, device="cuda")
+        L.specfold_gate(sh, H, fs, tau, ratio, rec)
+        torch.cuda.synchronize()
+        r = ratio.cpu().numpy().reshape(2, B)
+        m = rec.cpu().numpy().reshape(2, B) != 0
+        assert m[0].all() and np.isinf(r[0]).all() and (r[0] > 0).all()
+        got = r[1].astype(np.float64)
+        nan = np.isnan(exact)
+        assert np.isnan(got[nan]).all()
+        inf = np.isinf(exact)
+        assert np.isinf(got[inf]).all()
+        fin = ~nan & ~inf
+        # the fp32 ratio of exactly representable inputs: within one fp32 rounding step
+        np.testing.assert_allclose(got[fin], exact[fin], rtol=2.0 ** -23, atol=0)
+        with np.errstate(invalid="ignore"):
+            expect = ~(exact <= tau)
+        np.testing.assert_array_equal(m[1], expect)

@@ -2,8 +2,9 @@
 
 Layer l runs on layer l-1's output.  After the first layer the GPU's inputs differ from
 the oracle's by the rounding of the GPU's fp32/bf16 arithmetic (the oracle's layers run in
-float64 and hand bf16 models' outputs on in bf16).  Each element of such an input sits
-about one unit in the last place of the storage format away from the oracle's, which
+float64 -- float32 for the 28-layer stack, whose rounding is still far below the bf16
+tolerance -- and hand bf16 models' outputs on in bf16).  Each element of such an input
+sits about one unit in the last place of the storage format away from the oracle's, which
 moves a ratio r = ||c - p|| / ||p|| by at most about 2 ulp * (1 + r).  So:
   * every layer on its own: the GPU layer entry point fed the oracle's input of layer l
     decides bit-exactly outside the tie band and matches the oracle's layer-l output to
@@ -14,11 +15,11 @@ moves a ratio r = ||c - p|| / ||p|| by at most about 2 ulp * (1 + r).  So:
     per-layer rounding errors (bf16 h and y on the GPU) are independent and add up like
     a random walk over the L layers; the sqrt(L) widening is that walk's growth;
   * the stack running its own gates: layer 0 decides bit-exactly outside the tie band;
-    later layers may differ only where the oracle's ratio lies within the drift of tau,
-    and where none does the output bound above holds as well;
+    later layers may differ only where the oracle's ratio lies within the drift of tau;
+    every node whose own and whose fold-source ancestors' decisions all agree meets the
+    output bound above;
   * the stack equals chaining specfold_layer_forward calls, bit for bit."""
 import math
-import os
 
 import numpy as np
 import pytest
@@ -48,15 +49,20 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _oracle_stack(cfg, layers, tau, states=None):
+def _oracle_and_device_stack(runner, cfg, nl, tau, oracle_dtype=np.float64):
+    """Draw every layer once: upload it to a DeviceStack and feed it to the oracle's stack
+    (one layer's weights on the host at a time)."""
+    ds = runner.DeviceStack(cfg, (), _hidden(cfg), _graph(cfg))
+
     def params():
-        for l, w, c in layers():
-            if l % 4 == 0:
-                _say(f"[gpu]   oracle layer {l}")
+        for l, w, c in iter_layers(cfg, nl, workers=8):
+            ds.add_layer(w, c)
+            _say(f"[gpu]   layer {l} drawn and uploaded; oracle layer {l}")
             yield w, c[:cfg.prefix, 0], c[:cfg.prefix, 1]
-    return stack(params(), _hidden(cfg), _graph(cfg), tau, n_q=cfg.n_q, n_kv=cfg.n_kv,
-                 eps=cfg.rms_eps, carry="bf16" if cfg.dtype == "bf16" else None,
-                 states=states, keep_inputs=True)
+    ora = stack(params(), _hidden(cfg), _graph(cfg), tau, n_q=cfg.n_q, n_kv=cfg.n_kv,
+                eps=cfg.rms_eps, dtype=oracle_dtype,
+                carry="bf16" if cfg.dtype == "bf16" else None, keep_inputs=True)
+    return ora, ds
 
 
 _WL = {}
@@ -77,10 +83,6 @@ def _graph(cfg):
     return _base(cfg).fold_src
 
 
-def _layers(cfg, nl):
-    return lambda: iter_layers(cfg, nl, workers=8)
-
-
 def _device_stack(runner, cfg, nl):
     return runner.DeviceStack(cfg, ((w, c) for _, w, c in iter_layers(cfg, nl, workers=8)),
                               _hidden(cfg), _graph(cfg))
@@ -92,10 +94,10 @@ def _gpu_states_as_input(ora_states):
             for s in ora_states]
 
 
-def _check_stack(cfg, nl, tau, L, runner):
+def _check_stack(cfg, nl, tau, L, runner, oracle_dtype=np.float64):
     _say(f"[gpu] stack {cfg.name} layers={nl} tau={tau} S={cfg.slots}")
-    ora = _oracle_stack(cfg, _layers(cfg, nl), tau)
-    ds = _device_stack(runner, cfg, nl)
+    ora, ds = _oracle_and_device_stack(runner, cfg, nl, tau, oracle_dtype)
+    assert ds.num_layers == nl
     tol = TOL[cfg.dtype]
     tol_stack = tol * math.sqrt(nl)
     drift = DRIFT[cfg.dtype]
@@ -115,8 +117,9 @@ def _check_stack(cfg, nl, tau, L, runner):
         got = y.float().cpu().numpy().reshape(want.shape)
         err = max_abs_rel(got, want)
         worst = max(worst, err)
+        _say(f"[gpu]   layer {l} alone: K={ora['K'][l]} max_abs_rel={err:.3e}")
         assert err <= tol, (l, err)
-    _say(f"[gpu]   per layer: max_abs_rel <= {worst:.3e} over {nl} layers")
+    _say(f"[gpu]   per layer: max_abs_rel <= {worst:.3e} over {nl} layers (tol {tol})")
 
     # (1) oracle decisions fed in: outputs and the GPU's own ratios at every layer
     ds.load_states(_gpu_states_as_input(ora["states"]))
@@ -136,28 +139,38 @@ def _check_stack(cfg, nl, tau, L, runner):
         assert np.all(d <= (2e-5 if l == 0 else drift)), (l, float(d.max()))
     _say(f"[gpu]   ratio drift max={worst:.3e} (bound {drift:.1e})")
 
-    # (2) the GPU's own decisions
+    # (2) the GPU's own decisions.  Layer 0 decides bit-exactly outside the tie band; a
+    # later layer may differ only where the oracle's ratio lies within the drift of tau.
+    # A node's outputs depend only on its own slots and those of its fold-source
+    # ancestors (gate, provenance, its block keys and values, its source's FFN row), so
+    # every node none of whose decisions -- nor any ancestor's -- differed at any layer is
+    # compared against the oracle's output.
     ds.forward(tau)
     torch.cuda.synchronize()
     gst = ds.fold_states()
     assert_fold_state_equal(gst[0], ora["states"][0], tau)
-    all_equal = True
+    N = cfg.num_nodes
+    fs = _graph(cfg)
+    tainted = np.zeros(N, dtype=bool)
     for l in range(1, nl):
         o, g = ora["states"][l], gst[l]
         diff = g["recompute"] != o["recompute"]
         if diff.any():
-            all_equal = False
             near = np.abs(o["r64"] - tau) <= drift * (1 + o["r64"])
             assert not (diff & ~near).any(), f"layer {l}: decision differs away from tau"
-            _say(f"[gpu]   layer {l}: {int(diff.sum())} near-tau decisions differ; later "
-                 "layers not compared")
-            break
-        np.testing.assert_array_equal(g["slot_row"], o["slot_row"])
-        assert g["K"] == o["K"]
-    if all_equal:
-        err = max_abs_rel(ds.output_numpy(), ora["y"])
-        _say(f"[gpu]   free: max_abs_rel={err:.3e}")
-        assert err <= tol_stack
+            _say(f"[gpu]   layer {l}: {int(diff.sum())} near-tau decisions differ at nodes "
+                 f"{sorted(set(np.nonzero(diff)[0].tolist()))}")
+            tainted |= diff.any(axis=1)
+        elif not tainted.any():
+            np.testing.assert_array_equal(g["slot_row"], o["slot_row"])
+            assert g["K"] == o["K"]
+    for n in range(1, N):                       # nodes are numbered topologically
+        tainted[n] |= tainted[fs[n]]
+    keep = ~tainted
+    assert keep[0]
+    err = max_abs_rel(ds.output_numpy()[keep], ora["y"][keep])
+    _say(f"[gpu]   free: {int(keep.sum())} of {N} nodes compared, max_abs_rel={err:.3e}")
+    assert err <= tol_stack
     del ds
     torch.cuda.empty_cache()
 
@@ -251,9 +264,12 @@ def test_stack_7b_shape_two_layers():
     _check_stack(cfg, 2, cfg.tau, L, runner)
 
 
-@pytest.mark.skipif(os.environ.get("SPECFOLD_FULL_STACK") != "1",
-                    reason="all 28 layers take minutes of oracle time; set SPECFOLD_FULL_STACK=1")
+@pytest.mark.timeout(1200)
 def test_stack_7b_full_depth():
+    """All 28 layers of the 7B-shaped stack (1+31 branches, prefix 4096, tau = 0.05) in
+    the benchmark's launch configuration.  The oracle runs its layers in float32 here
+    (about a second per layer on the host) rather than float64; its rounding stays four
+    orders of magnitude below the bf16 tolerance."""
     L, runner = _dev()
     cfg = CONFIGS[3]
-    _check_stack(cfg, cfg.layers, cfg.tau, L, runner)
+    _check_stack(cfg, cfg.layers, cfg.tau, L, runner, oracle_dtype=np.float32)
