@@ -9,8 +9,15 @@ input already resident in HBM.  The default workload is the 7B-shaped layer (hid
 1 + 15 nodes, tau = 0.05).  `value` is branch-tokens verified per second per layer
 (N*B slots per step); `us_per_verify_layer` is the same number as latency.
 
+The default run also reports, in the same JSON line: per-step p10/p50/p90, per-kernel
+times and roofline fractions, selection cost (gate + provenance/packing) and correction
+cost (against the REUSE variant), the tau sweep of the 3B-shaped DAG layer (recompute
+fraction against time), the 28-layer 7B-shaped stack's step time, on-box measured HBM
+copy and bf16 GEMM rates beside the published peaks, and the CPU oracle's rate at all
+host cores and at one BLAS thread.
+
 Prints exactly one JSON line on stdout; progress goes to stderr.  --report PATH writes
-the extended results (per-kernel times, tau sweep) as JSON."""
+the extended results (per-kernel times per tau, per-step samples) as JSON."""
 import argparse
 import ctypes
 import json
@@ -23,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, public spec
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "ffn_gate_up_7b_layer_traffic.json")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "dominant_kernel_traffic.json")
 COPY_BYTES = 256 << 20         # calibration copy: bytes read (and written) per launch
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, public spec
 FP32_PEAK_TFLOPS = 157.3       # dense fp32
@@ -178,13 +185,16 @@ def kernel_breakdown(dl, tau, reps, ev, stream):
     return out
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
-    record, or None when the GEMM source has changed since the counters were taken."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` at `workload` from the committed rocprofv3 counter
+    record, or None when there is no record for that kernel and workload or the kernel's
+    source has changed since the counters were taken."""
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_RECORD))
     except (OSError, ValueError):
+        return None
+    if rec.get("kernel") != kernel or rec.get("workload") != workload:
         return None
     src = os.path.join(ROOT, rec.get("source", ""))
     try:
@@ -205,15 +215,8 @@ def calibration_copy(reps=3):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(w, tau, budget_s):
-    """The oracle as it stands on the host cores, on whole verify layers of the same
-    workload, repeated until the time budget is used."""
+def _oracle_rate(w, tau, budget_s):
     from oracle import layer
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:
-        cores = os.cpu_count()
     cfg = w.cfg
     pk, pv = w.prefix_kv(0)
     runs, t0 = 0, time.time()
@@ -224,10 +227,102 @@ def cpu_baseline(w, tau, budget_s):
         el = time.time() - t0
         if el >= budget_s:
             break
-    return dict(value=cfg.slots * runs / el, unit="branch-tokens/s", cores=int(cores),
-                kind="oracle",
+    return cfg.slots * runs / el, runs, el
+
+
+def cpu_baseline(w, tau, budget_s):
+    """The oracle as it stands on the host cores, on whole verify layers of the same
+    workload, repeated until the time budget is used: once with the BLAS pool at every
+    core it starts with, once limited to one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    v, runs, el = _oracle_rate(w, tau, budget_s)
+    with threadpool_limits(limits=1):
+        v1, runs1, el1 = _oracle_rate(w, tau, budget_s)
+    cfg = w.cfg
+    return dict(value=v, unit="branch-tokens/s", cores=int(cores), kind="oracle",
                 sample=f"{runs} whole {cfg.name} verify layers (tau={tau}), numpy float64 "
-                       f"oracle, {el:.1f}s wall, {os.cpu_count()} host CPUs visible")
+                       f"oracle, {el:.1f}s wall at {cores} BLAS threads; "
+                       f"{os.cpu_count()} host CPUs visible",
+                value_1_thread=v1,
+                sample_1_thread=f"{runs1} whole layers, {el1:.1f}s wall at 1 BLAS thread")
+
+
+def step_distribution(dl, tau, steps, ev, stream):
+    """Per-step durations (us) from a separate pass with an event pair around every step
+    (the timed pass that gives `value` carries no events inside)."""
+    import torch
+    evs = ev.create(2 * steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev.record(evs[2 * i], stream)
+        dl.forward(tau, stream=stream)
+        ev.record(evs[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    per = sorted(ev.ms(evs[2 * i], evs[2 * i + 1]) * 1e3 for i in range(steps))
+    ev.destroy(evs)
+
+    def q(f):
+        return per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+    return dict(p10=q(0.1), p50=q(0.5), p90=q(0.9), min=per[0], max=per[-1], n=len(per))
+
+
+def measured_peaks(ev, stream):
+    """On-box reference rates beside the published peaks: a 1 GiB device-to-device copy
+    (bytes read + written per second) and an 8192^3 bf16 GEMM through torch (hipBLASLt)."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    x = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    out = {}
+    for name, fn, work in (("hbm_copy_GBps", lambda: b.copy_(a), 2 * n / 1e9),
+                           ("bf16_gemm_TFLOPs", lambda: torch.mm(x, y), 2 * 8192 ** 3 / 1e12)):
+        for _ in range(3):
+            fn()
+        t0, t1 = ev.create(2)
+        torch.cuda.synchronize()
+        ev.record(t0, stream)
+        reps = 10
+        for _ in range(reps):
+            fn()
+        ev.record(t1, stream)
+        torch.cuda.synchronize()
+        out[name] = work * reps / (ev.ms(t0, t1) * 1e-3)
+        ev.destroy([t0, t1])
+    del a, b, x, y
+    torch.cuda.empty_cache()
+    out["hbm_copy_frac_of_peak"] = out["hbm_copy_GBps"] / HBM_PEAK_GBS
+    out["bf16_gemm_frac_of_peak"] = out["bf16_gemm_TFLOPs"] / BF16_PEAK_TFLOPS
+    return out
+
+
+# probe steps that are a single kernel (or a GEMM and its own split-K reduction) with an
+# algorithmic byte / flop count: candidates for the roofline of the dominant kernel
+ROOFLINE_STEPS = ("gate", "resolve_pack", "qkv", "attn_prefix", "attn_block", "ffn_gate_up",
+                  "ffn_down", "combine")
+
+
+def roofline_of(cfg, K, name, us, workload):
+    """Roofline object of one kernel: HBM-bound if its algorithmic arithmetic intensity is
+    below the ridge point of its dtype, else MFMA-bound."""
+    a = algorithmic(cfg, K)[name]
+    peak_tf = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ai = a["flops"] / max(a["bytes"], 1)
+    if ai < ridge:
+        achieved = a["bytes"] / (us * 1e-6) / 1e9
+        out = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                   frac=achieved / HBM_PEAK_GBS)
+    else:
+        achieved = a["flops"] / (us * 1e-6) / 1e12
+        out = dict(bound="mfma", achieved=achieved, peak=peak_tf, unit="TFLOP/s",
+                   frac=achieved / peak_tf)
+    out.update(traffic=measured_traffic(name, workload), kernel=name, avg_us=us,
+               algorithmic_bytes=a["bytes"], algorithmic_flops=a["flops"],
+               arithmetic_intensity=ai, ridge=ridge)
+    return out
 
 
 def main():
@@ -236,27 +331,29 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4],
-                    help="configuration id (1 = the 7B-shaped headline layer)")
+                    help="configuration id (1 = the 7B-shaped headline layer; 3 times one "
+                         "layer of the 28-layer stack's shape)")
     ap.add_argument("--tau", type=float, default=None)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time budget per thread setting (all cores, then one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true", help="also run the tau sweep of config 2")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the tau sweep of the 3B-shaped DAG layer")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 28-layer stack's end-to-end step time")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the on-box copy and GEMM reference rates")
     ap.add_argument("--budget-sweep", action="store_true",
                     help="also run the draft-budget sweep: the 7B layer at 1+{3,7,15,31,63} "
                          "branches, dense and folded")
     ap.add_argument("--gate-sweep", action="store_true",
                     help="also time specfold_gate alone on hidden states of 34 to 134 MB")
-    ap.add_argument("--reuse", action="store_true",
-                    help="also time the layer with the REUSE attention variant (folded slots "
-                         "take their source's attention output) and report the correction cost")
     ap.add_argument("--rope-bias", action="store_true",
                     help="also time the layer with the rotary embedding (base 10^6) and QKV "
                          "bias of the 7B model family")
     ap.add_argument("--lm-head", action="store_true",
                     help="also time the LM head + per-branch argmax (vocab 152064) on the 7B "
                          "layer's packed rows")
-    ap.add_argument("--stack", action="store_true",
-                    help="also time the 28-layer stack (config 3) end to end")
     ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--report", default=None)
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel probes")
@@ -285,24 +382,34 @@ def main():
     K = dl.fold_state()["K"]
     log(f"[bench] K={K} of S={cfg.slots} packed rows")
 
-    dom = L.STEPS.index("ffn_gate_up")
-    # the timed steps carry no probe events; the dominant kernel's launch duration is
-    # measured in a second pass of the same length with events around that launch only
+    # the timed steps carry no probe events
     ms, _ = time_layer(dl, tau, args.steps, args.warmup, ev, stream)
     log(f"[bench] {ms * 1e3:.1f} us per verify layer")
-    _, per = time_layer(dl, tau, args.steps, 2, ev, stream, probe_step=dom)
-    dom_ms = sum(per) / len(per)
-    alg = algorithmic(cfg, K)
-    dom_bytes = alg["ffn_gate_up"]["bytes"]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    dist = step_distribution(dl, tau, args.steps, ev, stream)
+    log(f"[bench] per step p10/p50/p90 {dist['p10']:.1f} / {dist['p50']:.1f} / "
+        f"{dist['p90']:.1f} us (event pair around every step)")
     kernels = {} if args.no_breakdown else kernel_breakdown(dl, tau, 20, ev, stream)
     if kernels:
         log("[bench] per-kernel us: " + ", ".join(f"{k}={v:.1f}" for k, v in kernels.items()))
+    # the dominant kernel (the longest single-kernel step) is timed again in a pass of the
+    # same length with events around its launch only
+    cand = {k: v for k, v in kernels.items() if k in ROOFLINE_STEPS}
+    dom_name = max(cand, key=cand.get) if cand else "ffn_gate_up"
+    _, per = time_layer(dl, tau, args.steps, 2, ev, stream, probe_step=L.STEPS.index(dom_name))
+    dom_us = sum(per) / len(per) * 1e3
+    roof = roofline_of(cfg, K, dom_name, dom_us, cfg.name)
+    log(f"[bench] dominant kernel {dom_name}: {dom_us:.1f} us, {roof['achieved']:.0f} "
+        f"{roof['unit']} ({roof['frac'] * 100:.1f}% of the {roof['bound']} peak)")
     if args.calibrate_copy:
         calibration_copy()
+    ms_r = time_reuse(dl, tau, args.steps, args.warmup, ev, stream)
+    log(f"[bench] REUSE variant {ms_r * 1e3:.1f} us per verify layer")
 
+    unit_metric = ("branch-tokens verified/s per layer "
+                   f"({cfg.name}: hidden {cfg.hidden}, {cfg.num_nodes} nodes x block "
+                   f"{cfg.block}, prefix {cfg.prefix}, tau {tau}); us/verify-layer")
     result = {
-        "metric": "branch-tokens verified/s per layer (7B shape, 1+15 branches); us/verify-layer",
+        "metric": unit_metric,
         "value": cfg.slots / (ms * 1e-3),
         "unit": "branch-tokens/s",
         "n_gpus": 1,
@@ -318,28 +425,24 @@ def main():
                    "hidden": cfg.hidden, "heads": f"{cfg.n_q}q/{cfg.n_kv}kv x {cfg.head_dim}",
                    "ffn": cfg.ffn, "prefix": cfg.prefix, "tau": tau, "graph": cfg.graph},
         "us_per_verify_layer": ms * 1e3,
+        "us_per_step_dist": dist,
         "packed_rows": K,
         "recompute_fraction": K / cfg.slots,
         "kernels_us": kernels,
         "kernels_roofline": kernel_rooflines(cfg, K, kernels) if kernels else {},
-        "roofline": {"bound": "hbm", "kernel": "ffn_gate_up", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(), "avg_us": dom_ms * 1e3,
-                     "algorithmic_bytes": dom_bytes},
+        "selection_us": (kernels.get("gate", 0.0) + kernels.get("resolve_pack", 0.0)
+                         if kernels else None),
+        "reuse": dict(us_per_verify_layer=ms_r * 1e3, correction_cost_us=(ms - ms_r) * 1e3),
+        "roofline": roof,
     }
     report = {"main": result}
-    if args.sweep:
-        report["tau_sweep"] = tau_sweep(ev, stream, args.steps, args.warmup)
+    if not args.no_peaks:
+        result["measured_peaks"] = measured_peaks(ev, stream)
+        log("[bench] on-box reference rates: " + ", ".join(
+            f"{k}={v:.3g}" for k, v in result["measured_peaks"].items()))
     if args.gate_sweep:
         report["gate_sweep"] = gate_sweep(ev, stream)
         result["gate_sweep"] = report["gate_sweep"]
-    if args.reuse:
-        ms_r = time_reuse(dl, tau, args.steps, args.warmup, ev, stream)
-        result["reuse"] = dict(us_per_verify_layer=ms_r * 1e3,
-                               correction_cost_us=(ms - ms_r) * 1e3)
-        log(f"[bench] REUSE variant {ms_r * 1e3:.1f} us per verify layer; the correction "
-            f"(folded slots attending to their own branch, O projection on every slot) costs "
-            f"{(ms - ms_r) * 1e3:.1f} us")
     if args.rope_bias:
         crb = cfg.with_(name=cfg.name + "-rope-bias", rope_theta=1.0e6, qkv_bias=True)
         _, dlr = build_layer(crb)
@@ -353,23 +456,26 @@ def main():
     if args.lm_head:
         report["lm_head"] = lm_head_bench(cfg, w, dl, tau, ev, stream, args.steps, args.warmup)
         result["lm_head"] = report["lm_head"]
+    del dl
+    torch.cuda.empty_cache()
     if args.budget_sweep:
-        del dl
-        torch.cuda.empty_cache()
         report["budget_sweep"] = budget_sweep(w, ev, stream, args.steps, args.warmup)
         result["budget_sweep"] = [{k: r[k] for k in ("branches", "tau", "K", "us",
                                                      "branch_tokens_per_s")}
                                   for r in report["budget_sweep"]]
-    if args.stack:
-        if not args.budget_sweep:
-            del dl
-        torch.cuda.empty_cache()
+    if not args.no_sweep:
+        report["tau_sweep"] = tau_sweep(ev, stream, args.steps, args.warmup)
+        result["tau_sweep"] = {"workload": CONFIGS[2].name,
+                               "rows": [{k: r[k] for k in ("tau", "K", "recompute_fraction",
+                                                           "us", "speedup_vs_dense")}
+                                        for r in report["tau_sweep"]]}
+    if not args.no_stack:
         report["stack"] = stack_bench(ev, stream, args.stack_steps, 3)
         result["stack"] = {k: report["stack"][k] for k in
                            ("workload", "layers", "us_per_verify_step", "us_per_layer",
-                            "packed_rows_per_layer")}
+                            "us_per_verify_step_graph", "packed_rows_per_layer", "weights")}
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle ...")
+        log("[bench] timing the CPU oracle (all BLAS threads, then one) ...")
         result["cpu_baseline"] = cpu_baseline(w, tau, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
@@ -393,8 +499,11 @@ def tau_sweep(ev, stream, steps, warmup):
         ms, _ = time_layer(dl, tau, steps, warmup, ev, stream)
         kern = kernel_breakdown(dl, tau, 10, ev, stream)
         rows.append(dict(tau=tau, K=K, recompute_fraction=K / cfg.slots, us=ms * 1e3,
+                         speedup_vs_dense=rows[0]["us"] / (ms * 1e3) if rows else 1.0,
                          kernels_us=kern))
         log(f"[bench] sweep tau={tau}: K={K} ({K / cfg.slots:.3f}) {ms * 1e3:.1f} us")
+    del dl
+    torch.cuda.empty_cache()
     return rows
 
 
@@ -522,19 +631,44 @@ def budget_sweep(w1, ev, stream, steps, warmup):
     return rows
 
 
+def device_layers(cfg):
+    """Per-layer weights and prefix caches of `cfg` drawn on the device (seeded torch
+    generator, same distributions as the host generator: linear weights N(0, 0.02^2),
+    RMSNorm gains 1, prefix K/V N(0, (0.02 sqrt(d))^2), rounded to bf16).  Drawing 13 GB
+    of 28-layer weights on the host would take minutes; the timing does not depend on
+    which seeded values the weights hold."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    d, f, dh = cfg.hidden, cfg.ffn, cfg.head_dim
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def lin(o, i):
+        return (torch.randn(o, i, device="cuda", generator=g) * cfg.weight_std).to(dt)
+
+    for _ in range(cfg.layers):
+        w = {"rms1": torch.ones(d, device="cuda", dtype=dt), "w_qkv": lin(cfg.qkv_dim, d),
+             "w_o": lin(d, cfg.n_q * dh), "rms2": torch.ones(d, device="cuda", dtype=dt),
+             "w_gate_up": lin(2 * f, d), "w_down": lin(d, f)}
+        cache = (torch.randn(cfg.prefix + 64, 2, cfg.n_kv, dh, device="cuda", generator=g)
+                 * (0.02 * math.sqrt(d))).to(dt)
+        yield w, cache
+
+
 def stack_bench(ev, stream, steps, warmup):
     """End-to-end time of one verify step through the 28-layer 7B-shaped stack (1+31
     branches, prefix 4096): every layer gates, packs and runs on the previous layer's
-    output inside one specfold_stack_forward call."""
+    output inside one specfold_stack_forward call.  Hidden states and draft graph come
+    from the host generator; weights and prefix caches are drawn on the device."""
     import torch
     from branch_folding_amd.runner import DeviceStack
-    from synth import CONFIGS, iter_layers, make_workload
+    from synth import CONFIGS, make_workload
     cfg = CONFIGS[3]
     t = time.time()
     base = make_workload(cfg, layers=1, weights=False)
-    ds = DeviceStack(cfg, ((w, c) for _, w, c in iter_layers(cfg, workers=8)), base.H,
-                     base.fold_src)
-    log(f"[bench] stack {cfg.name}: {ds.num_layers} layers drawn and uploaded in "
+    ds = DeviceStack(cfg, device_layers(cfg), base.H, base.fold_src)
+    torch.cuda.synchronize()
+    log(f"[bench] stack {cfg.name}: {ds.num_layers} layers drawn on the device in "
         f"{time.time() - t:.1f}s")
     ds.forward(cfg.tau, stream=stream)
     torch.cuda.synchronize()
@@ -568,7 +702,8 @@ def stack_bench(ev, stream, steps, warmup):
     res = dict(workload=cfg.name, layers=ds.num_layers, tau=cfg.tau, us_per_verify_step=ms * 1e3,
                us_per_layer=ms * 1e3 / ds.num_layers, packed_rows_per_layer=Ks,
                slots=cfg.slots, branch_tokens_per_s=cfg.slots / (ms * 1e-3),
-               us_per_verify_step_graph=ms_g * 1e3)
+               us_per_verify_step_graph=ms_g * 1e3,
+               weights="drawn on the device: N(0, 0.02^2) linear weights, bf16")
     del ds
     torch.cuda.empty_cache()
     return res

@@ -23,6 +23,14 @@ def to_device(x: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device=device, dtype=dtype)
 
 
+def _as_device(x, dtype: torch.dtype, device) -> torch.Tensor:
+    """A host array uploaded exactly, or a tensor already drawn on the device (converted
+    to the layer's dtype)."""
+    if isinstance(x, torch.Tensor):
+        return x.to(device=device, dtype=dtype).contiguous()
+    return to_device(x, dtype, device)
+
+
 def shape_of(cfg, prefix_len: Optional[int] = None) -> L.Shape:
     return L.make_shape(cfg.num_nodes, cfg.block, cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim,
                         cfg.ffn, cfg.prefix if prefix_len is None else prefix_len, cfg.dtype,
@@ -131,11 +139,12 @@ class DeviceStack:
         return len(self.w)
 
     def add_layer(self, weights: Dict[str, np.ndarray], cache: np.ndarray) -> None:
-        """Upload one more layer's weights and prefix cache, with its fold-state buffers."""
+        """Upload one more layer's weights and prefix cache (host arrays, or tensors drawn
+        on the device), with its fold-state buffers."""
         cfg, dt, S = self.cfg, self.dt, self.cfg.slots
         n_kv, dh = cfg.n_kv, cfg.head_dim
-        self.w.append({k: to_device(v, dt, self.device) for k, v in weights.items()})
-        c = to_device(cache, dt, self.device)
+        self.w.append({k: _as_device(v, dt, self.device) for k, v in weights.items()})
+        c = _as_device(cache, dt, self.device)
         self.caches.append(c)
         self.prefix.append((c[0, 0].data_ptr(), c[0, 1].data_ptr(), 2 * n_kv * dh, dh))
         self.states.append({
@@ -161,12 +170,14 @@ class DeviceStack:
             dev[k][: v.size].copy_(torch.from_numpy(v).to(self.device))
 
     def forward(self, tau: float, stream=None, state_in: bool = False,
-                record_states: bool = True) -> torch.Tensor:
+                record_states: bool = True, num_layers: Optional[int] = None) -> torch.Tensor:
+        """The first num_layers layers (default: all) on H; the last one's output lands
+        in self.out."""
         flags = L.SPECFOLD_FLAG_FOLD_STATE_IN if state_in else 0
         L.specfold_stack_forward(self.shape, self.w, self.prefix if self.cfg.prefix else None,
                                  self.H, self.out, self.fold_src, tau,
                                  self.states if (record_states or state_in) else None, flags,
-                                 self.ws, self.ws_bytes, stream)
+                                 self.ws, self.ws_bytes, stream, num_layers=num_layers)
         return self.out
 
     def capture(self, tau: float, record_states: bool = True) -> "torch.cuda.CUDAGraph":

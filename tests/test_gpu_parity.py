@@ -114,18 +114,19 @@ def _check_intermediates(dl, cfg, ref, K, L, tag, attn_slots=None):
     attn_slots: bool [N, B] restricting the o check (REUSE: the packed slots)."""
     S, tol = cfg.slots, TOL[cfg.dtype]
 
-    def host(which):
-        return dl.intermediate(which).float().cpu().numpy().astype(np.float64)
+    def host(which, rows):
+        # rows past K of a packed tensor were never written in this call
+        return dl.intermediate(which)[:rows].float().cpu().numpy().astype(np.float64)
 
     qkv_ref = np.concatenate([ref["Q"].reshape(K, -1), ref["K_"].reshape(K, -1),
                               ref["V"].reshape(K, -1)], axis=1)
     o_ref = ref["o"].reshape(S, -1).copy()
     if attn_slots is not None:
         o_ref[~attn_slots.reshape(-1)] = np.nan
-    checks = [("qkv", host(L.SPECFOLD_T_QKV)[:K], qkv_ref),
-              ("o", host(L.SPECFOLD_T_ATTN), o_ref),
-              ("h", host(L.SPECFOLD_T_H), ref["h"].reshape(S, -1)),
-              ("F", host(L.SPECFOLD_T_FFN)[:K], ref["F"].reshape(K, -1))]
+    checks = [("qkv", host(L.SPECFOLD_T_QKV, K), qkv_ref),
+              ("o", host(L.SPECFOLD_T_ATTN, S), o_ref),
+              ("h", host(L.SPECFOLD_T_H, S), ref["h"].reshape(S, -1)),
+              ("F", host(L.SPECFOLD_T_FFN, K), ref["F"].reshape(K, -1))]
     msg = []
     for name, got, want in checks:
         rows = np.all(np.isfinite(want), axis=1)        # rows the oracle evaluated
