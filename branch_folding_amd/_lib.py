@@ -81,6 +81,11 @@ _SIGS = {
                                                      ctypes.c_float, ctypes.POINTER(FoldState),
                                                      ctypes.c_uint32, _P, ctypes.c_size_t, _P,
                                                      ctypes.POINTER(Probe)]),
+    "specfold_layer_forward_static": (ctypes.c_int, [ctypes.POINTER(Shape),
+                                                     ctypes.POINTER(LayerWeights),
+                                                     ctypes.POINTER(KVView), _P, _P, _P,
+                                                     ctypes.c_float, ctypes.POINTER(FoldState),
+                                                     ctypes.c_uint32, _P]),
     "specfold_workspace_offset": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32,
                                                      ctypes.POINTER(ctypes.c_int64)]),
     "specfold_stack_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
@@ -244,6 +249,23 @@ def specfold_layer_forward(shape: Shape, weights: dict, prefix, hidden_in, hidde
         _check(lib().specfold_layer_forward(*args))
     else:
         _check(lib().specfold_layer_forward_probed(*args, ctypes.byref(probe)))
+
+
+SPECFOLD_STATIC_WORKSPACE_BYTES = 128 << 20
+
+
+def specfold_layer_forward_static(shape: Shape, weights: dict, prefix, hidden_in, hidden_out,
+                                  fold_src, tau: float, state: Optional[dict] = None,
+                                  flags: int = 0, stream=None):
+    """specfold_layer_forward with the library's static device workspace (no workspace
+    argument; the call allocates nothing)."""
+    lw = _weights(weights)
+    kv = _kv(prefix)
+    st = None if state is None else _state(state)
+    _check(lib().specfold_layer_forward_static(
+        ctypes.byref(shape), ctypes.byref(lw), ctypes.byref(kv), _ptr(hidden_in),
+        _ptr(hidden_out), _ptr(fold_src), float(tau),
+        ctypes.byref(st) if st is not None else None, int(flags), _stream(stream)))
 
 
 def specfold_stack_workspace_bytes(shape: Shape) -> int:

@@ -1,13 +1,15 @@
 // C ABI of the folded multi-branch verify layer: argument checks, workspace carving and
 // the launch sequence.  Everything is enqueued on the caller's stream; nothing here
-// synchronises, allocates device memory or keeps global mutable state besides a per-device
-// cache of the compute-unit count.
+// synchronises or allocates device memory.  Global state: per-device caches of the
+// compute-unit count and of the static workspace's device address, and the static
+// workspace itself (specfold_layer_forward_static).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/specfold.h"
@@ -15,6 +17,18 @@
 #include "kernels.h"
 
 using namespace specfold;
+
+// Workspace of specfold_layer_forward_static: a statically allocated device array, one
+// copy per GPU, held until the process ends.  Host code never passes `specfold_scratch`
+// itself to a kernel (its name stands for a host-side shadow, not a device address).
+// It has external linkage on purpose: in a build without relocatable device code the
+// device code object exports only externally linked variables in its dynamic symbol
+// table, where hipGetSymbolAddress resolves names; a `static` array stays a local entry
+// of .symtab that the runtime cannot find.  The library-specific name keeps its host
+// shadow from colliding with another library's symbol.  `used` keeps the device
+// compilation from dropping it, since no kernel names it.
+static_assert(SPECFOLD_STATIC_WORKSPACE_BYTES % 256 == 0, "static workspace granularity");
+__device__ __align__(256) __attribute__((used)) char specfold_scratch[SPECFOLD_STATIC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -422,6 +436,29 @@ specfold_status launch_layer(const specfold_shape* shape, const specfold_layer_w
                           gate_done, next, reuse);
 }
 
+// Device address of the static workspace on each device, looked up once per device with
+// that device current (hipGetSymbolAddress); host code passes only this address on.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+specfold_status static_workspace(char** out) {
+  int dev = -1;
+  HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64)
+    return fail(SPECFOLD_ERR_UNSUPPORTED, "device ordinal %d is beyond the 64 the static "
+                "workspace tracks", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(specfold_scratch)));
+    if (p == nullptr || ((uintptr_t)p & 255u) != 0)
+      return fail(SPECFOLD_ERR_HIP, "static workspace of device %d has no usable address", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return SPECFOLD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -530,6 +567,37 @@ specfold_status specfold_layer_forward_probed(const specfold_shape* shape,
   return launch_layer(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, state,
                       state_in, (char*)workspace, L, (hipStream_t)stream, probe, false, nullptr,
                       nullptr, (flags & SPECFOLD_FLAG_REUSE_ATTENTION) != 0);
+}
+
+specfold_status specfold_layer_forward_static(const specfold_shape* shape,
+                                              const specfold_layer_weights* weights,
+                                              const specfold_kv_view* prefix,
+                                              const void* hidden_in, void* hidden_out,
+                                              const int32_t* fold_src, float tau,
+                                              specfold_fold_state* state, uint32_t flags,
+                                              void* stream) {
+  specfold_status st = check_shape(shape, true);
+  if (st != SPECFOLD_OK) return st;
+  if ((st = check_flags(flags)) != SPECFOLD_OK) return st;
+  const bool state_in = (flags & SPECFOLD_FLAG_FOLD_STATE_IN) != 0;
+  if ((st = check_layer_params(shape, weights, prefix, -1)) != SPECFOLD_OK) return st;
+  if ((st = check_hidden(shape, hidden_in, hidden_out)) != SPECFOLD_OK) return st;
+  if (!state_in && !fold_src)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "fold_src is required unless the fold state is an input");
+  if (state_in && (st = check_state_in(state, -1)) != SPECFOLD_OK) return st;
+  const Layout L = layout_of(shape);
+  if (L.total > (size_t)SPECFOLD_STATIC_WORKSPACE_BYTES)
+    return fail(SPECFOLD_ERR_WORKSPACE,
+                "this shape needs %zu bytes of workspace, more than the %zu-byte static "
+                "workspace; call specfold_layer_forward with a caller workspace",
+                L.total, (size_t)SPECFOLD_STATIC_WORKSPACE_BYTES);
+  char* ws = nullptr;
+  if ((st = static_workspace(&ws)) != SPECFOLD_OK) return st;
+  // nothing in the workspace has to start at zero: every launch writes what a later
+  // launch of the same call reads
+  return launch_layer(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, state,
+                      state_in, ws, L, (hipStream_t)stream, nullptr, false, nullptr, nullptr,
+                      (flags & SPECFOLD_FLAG_REUSE_ATTENTION) != 0);
 }
 
 size_t specfold_stack_workspace_bytes(const specfold_shape* shape) {

@@ -210,6 +210,30 @@ specfold_status specfold_layer_forward(const specfold_shape* shape,
                                        void* workspace, size_t workspace_bytes,
                                        void* stream);
 
+/* Allocation-free variant of specfold_layer_forward, for callers that cannot allocate
+ * device memory around the call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks, launches and results as
+ * specfold_layer_forward, but the workspace is a static device array inside the library:
+ * SPECFOLD_STATIC_WORKSPACE_BYTES per GPU, reserved when the library's code is loaded on
+ * that GPU and held until the process ends.  The call itself allocates and frees nothing.
+ *   - Shapes whose specfold_layer_workspace_bytes exceeds SPECFOLD_STATIC_WORKSPACE_BYTES
+ *     are rejected with SPECFOLD_ERR_WORKSPACE before anything is enqueued (the 7B-shaped
+ *     layer with 1+15 branches needs about 85 MiB).
+ *   - Every call on one GPU shares that GPU's array, and it keeps the last call's
+ *     contents (nothing in it needs to start at zero).  Calls that overlap in time on one
+ *     GPU -- on different streams, or from different host threads without ordering --
+ *     race on it; order them on one stream.
+ *   - The first call on each device looks the array's device address up once
+ *     (hipGetSymbolAddress); a failure there returns SPECFOLD_ERR_HIP.              */
+#define SPECFOLD_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+specfold_status specfold_layer_forward_static(const specfold_shape* shape,
+                                              const specfold_layer_weights* weights,
+                                              const specfold_kv_view* prefix,
+                                              const void* hidden_in, void* hidden_out,
+                                              const int32_t* fold_src, float tau,
+                                              specfold_fold_state* state, uint32_t flags,
+                                              void* stream);
+
 /* Bytes of device workspace specfold_stack_forward needs for `shape`: one layer's
  * workspace followed by one spare [N, B, d] hidden-state buffer (0 if the shape is
  * invalid or unsupported).  The layer part has the layout that specfold_workspace_offset
