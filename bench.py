@@ -343,6 +343,11 @@ def main():
                     help="skip the 28-layer stack's end-to-end step time")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the on-box copy and GEMM reference rates")
+    ap.add_argument("--no-reuse", action="store_true",
+                    help="skip timing the REUSE variant (the correction cost)")
+    ap.add_argument("--only-layer", action="store_true",
+                    help="time the selected layer only: no sweep, stack, reference rates, "
+                         "REUSE variant or CPU baseline (for profiler runs)")
     ap.add_argument("--budget-sweep", action="store_true",
                     help="also run the draft-budget sweep: the 7B layer at 1+{3,7,15,31,63} "
                          "branches, dense and folded")
@@ -360,6 +365,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help=f"also run a {COPY_BYTES >> 20} MiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.only_layer:
+        args.no_sweep = args.no_stack = args.no_peaks = args.no_reuse = True
+        args.no_cpu_baseline = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the folded verify layer is measured on one "
               "MI355X (multi-GPU sharding is a design note, not built)", file=sys.stderr)
@@ -402,8 +410,9 @@ def main():
         f"{roof['unit']} ({roof['frac'] * 100:.1f}% of the {roof['bound']} peak)")
     if args.calibrate_copy:
         calibration_copy()
-    ms_r = time_reuse(dl, tau, args.steps, args.warmup, ev, stream)
-    log(f"[bench] REUSE variant {ms_r * 1e3:.1f} us per verify layer")
+    ms_r = None if args.no_reuse else time_reuse(dl, tau, args.steps, args.warmup, ev, stream)
+    if ms_r is not None:
+        log(f"[bench] REUSE variant {ms_r * 1e3:.1f} us per verify layer")
 
     unit_metric = ("branch-tokens verified/s per layer "
                    f"({cfg.name}: hidden {cfg.hidden}, {cfg.num_nodes} nodes x block "
@@ -432,7 +441,8 @@ def main():
         "kernels_roofline": kernel_rooflines(cfg, K, kernels) if kernels else {},
         "selection_us": (kernels.get("gate", 0.0) + kernels.get("resolve_pack", 0.0)
                          if kernels else None),
-        "reuse": dict(us_per_verify_layer=ms_r * 1e3, correction_cost_us=(ms - ms_r) * 1e3),
+        "reuse": (None if ms_r is None else
+                  dict(us_per_verify_layer=ms_r * 1e3, correction_cost_us=(ms - ms_r) * 1e3)),
         "roofline": roof,
     }
     report = {"main": result}

@@ -255,6 +255,25 @@ __device__ __forceinline__ void attend_tile(const T* Ks, const T* Vt, int nkeys,
 // ------------------------------------------------------------------------------------
 // Prefix phase.
 // ------------------------------------------------------------------------------------
+// Order of the prefix units over the grid.  Workgroups are dispatched to the 8 XCDs round
+// robin (workgroup b runs on XCD b % 8), and each XCD has its own L2.  The units are
+// numbered (KV head, key split) major and query tile fastest, and XCD x takes the
+// contiguous range [x * per, (x + 1) * per) of them: the query tiles that share one KV
+// head's key range run side by side on one XCD and stream its K/V tiles through that
+// XCD's L2 instead of each XCD fetching every key range from HBM.  A grid that is not a
+// multiple of 8 walks the units in plain order.
+struct PrefixWalk {
+  int v, end, step;
+  __device__ PrefixWalk(int units) {
+    const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
+    const int per = (units + nx - 1) / nx;
+    const int x = blockIdx.x % nx;
+    v = x * per + blockIdx.x / nx;
+    end = imin((x + 1) * per, units);
+    step = gridDim.x / nx;
+  }
+};
+
 // The prefix phase records its split count and the merge decision for this call's packed
 // count (one thread of workgroup 0), so the later attention kernels need not evaluate the
 // cost model again in every workgroup.  Without a prefix the phase is not launched and the
@@ -286,10 +305,9 @@ __global__ void __launch_bounds__(256, 2) attn_prefix_kernel(AttnParams p) {
   const T* pk = (const T*)p.pk;
   const T* pv = (const T*)p.pv;
 
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    // split fastest: the splits of one query tile run on different XCDs concurrently
-    const int s = u % ns, rest = u / ns;
-    const int qt = rest % qtiles, kvh = rest / qtiles;
+  for (PrefixWalk w(units); w.v < w.end; w.v += w.step) {
+    const int qt = w.v % qtiles, pair = w.v / qtiles;
+    const int s = pair % ns, kvh = pair / ns;
     const int r = qt * kQRows + wave * 16 + l16;
     const bool valid = r < K * g;
     const int rr = valid ? r : K * g - 1;
@@ -512,10 +530,9 @@ __global__ void __launch_bounds__(kTrWaves * 64, 1) attn_prefix_tr_kernel(AttnPa
   }
   const int wq = __builtin_amdgcn_readfirstlane(wave) * QI * 1024;   // wave's LDS slice
 
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    // split fastest: the splits of one query tile run on different XCDs concurrently
-    const int s = u % ns, rest = u / ns;
-    const int qt = rest % qtiles, kvh = rest / qtiles;
+  for (PrefixWalk w(units); w.v < w.end; w.v += w.step) {
+    const int qt = w.v % qtiles, pair = w.v / qtiles;
+    const int s = pair % ns, kvh = pair / ns;
     uint4 qf[2][KSQ];
     bool valid[2];
     int krow[2], hq[2];

@@ -370,7 +370,7 @@ __global__ void __launch_bounds__(kFinishThreads) oproj_finish_kernel(
   // device; slot s adds the projection of its packed row slot_row[s]
   if (by_row && K <= 0) return;
   const int rows = by_row ? K : S;
-  if (by_row) split = gemm_split(ceil_div(K, bm) * tiles_n, kiters);
+  if (by_row) split = gemm_split(ceil_div(K, gemm_bm_of(bm, S, K)) * tiles_n, kiters);
   const size_t plane = (size_t)rows * d;
   const size_t row = (size_t)s * d;
   const size_t prow = by_row ? (size_t)imin(imax(slot_row[s], 0), K - 1) * d : row;

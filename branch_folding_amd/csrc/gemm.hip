@@ -62,31 +62,41 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 
 constexpr int kGemmStages = 3;
 
-template <typename T, int EPI, int BN, int BM>
-__global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
+// Every unit of one GEMM call with BM x BN tiles, walked persistently by this workgroup.
+// The tile's NW waves, one per WTM x WTN wave tile, load and compute; in a launch with
+// more waves the others take part in the barriers only, so one launch can run either row
+// tile.  Stage buffers: A stages of at least BM rows, W stages of at least BN rows.
+// SPLIT = false keeps every unit on the whole K range (no partials, no reduction pass).
+template <typename T, int EPI, int BN, int BM, bool SPLIT = true, int WTM = 64, int WTN = 64,
+          int NWL = (BM / WTM) * (BN / WTN)>
+__device__ __forceinline__ void gemm_units(const GemmParams& p, int M, char* As0, char* As1,
+                                           char* As2, char* Ws0, char* Ws1, char* Ws2) {
   using G = GemmTile<T>;
-  constexpr int NT = BM * BN / 64;           // threads: one wave per 64 x 64 wave tile
-  constexpr int NW = NT / 64;                // waves
-  constexpr int WN = BN / 64;                // waves along N
+  constexpr int WN = BN / WTN;               // waves along N
+  constexpr int NW = (BM / WTM) * WN;        // waves of the tile
+  constexpr int TI = WTM / 16, TJ = WTN / 16;   // 16 x 16 MFMA tiles per wave
+  static_assert(EPI != kEpiArgmax || WTN == 64, "argmax partials assume 64-column wave tiles");
+  static_assert(EPI != kEpiSwiGLU || WTN % 32 == 0, "a wave holds whole gate/up pairs");
   constexpr int A_BYTES = BM * kGemmBKBytes;
   constexpr int W_BYTES = BN * kGemmBKBytes;
   constexpr int AQ = A_BYTES / 1024 / NW;    // A load instructions per wave per k-iteration
   constexpr int WQ = W_BYTES / 1024 / NW;    // W load instructions per wave per k-iteration
   constexpr int LPI = AQ + WQ;               // vector-memory ops per wave per k-iteration
   static_assert(AQ >= 1 && WQ >= 1 && A_BYTES % (1024 * NW) == 0, "tile/loader mismatch");
-  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
 
-  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
-  if (M <= 0) return;
   const int mb = ceil_div(M, BM), nt = ceil_div(p.N, BN);
   const int kiters = p.Kd / G::BK;
   const int tiles = mb * nt;
-  const int split = EPI == kEpiArgmax ? 1 : gemm_split(tiles, kiters);
+  const int split = (EPI == kEpiArgmax || !SPLIT) ? 1 : gemm_split(tiles, kiters);
   const int units = tiles * split;
   const int per_xcd = ceil_div(units, 8);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // NWL = waves in the launch; when the tile has them all, nothing is predicated (a
+  // predicated LDS DMA makes the compiler drain every load in flight before the LDS reads)
+  static_assert(NWL >= NW, "launch narrower than the tile");
+  const bool active = (NWL == NW) || wave < NW;
   const int wm = wave / WN, wn = wave % WN;
   const int g4 = lane >> 4, l16 = lane & 15;
   const char* Ab = (const char*)p.A;
@@ -129,6 +139,7 @@ __global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
     // Stage loads of k-iteration `it` (clamped to the unit's last one: cache hits, unused):
     // the weight tile and the A tile.
     auto issue_w = [&](char* ws, int it) {
+      if (!active) return;
       const size_t off = (size_t)imin(it, ke - 1) * kGemmBKBytes;
 #pragma unroll
       for (int q = 0; q < WQ; ++q)
@@ -136,6 +147,7 @@ __global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
                                          (lds_void_t*)(ws + (wave * WQ + q) * 1024), 16, 0, 0);
     };
     auto issue_a = [&](char* as, int it) {
+      if (!active) return;
       const size_t off = (size_t)imin(it, ke - 1) * kGemmBKBytes;
 #pragma unroll
       for (int q = 0; q < AQ; ++q)
@@ -143,12 +155,12 @@ __global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
                                          (lds_void_t*)(as + (wave * AQ + q) * 1024), 16, 0, 0);
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool rows_live = (m0 + wm * 64) < M;
+      for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool rows_live = active && (m0 + wm * WTM) < M;
 
     // One wave per SIMD, so LDS latency is hidden inside the wave: all operand fragments of
     // the k-iteration are read at once (the second k-step's reads land while the first
@@ -156,24 +168,24 @@ __global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
     auto compute = [&](const char* as, const char* ws) {
       if (!rows_live) return;
       constexpr int KS = kGemmBKBytes / 64;
-      uint4 af[KS][4], bfr[KS][4];
+      uint4 af[KS][TI], bfr[KS][TJ];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int c = ks * 4 + g4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[ks][i] = *reinterpret_cast<const uint4*>(as + swz(wm * 64 + i * 16 + l16, c));
+        for (int i = 0; i < TI; ++i)
+          af[ks][i] = *reinterpret_cast<const uint4*>(as + swz(wm * WTM + i * 16 + l16, c));
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfr[ks][j] = *reinterpret_cast<const uint4*>(ws + swz(wn * 64 + j * 16 + l16, c));
+        for (int j = 0; j < TJ; ++j)
+          bfr[ks][j] = *reinterpret_cast<const uint4*>(ws + swz(wn * WTN + j * 16 + l16, c));
       }
       __builtin_amdgcn_sched_barrier(0);   // keep every read ahead of the MFMAs
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < TJ; ++j)
             acc[i][j] = mma_kstep(af[ks][i], bfr[ks][j], acc[i][j], T());
     };
     // k-iteration i on stage (as, ws): once this wave's loads of i have landed (only the
@@ -204,18 +216,20 @@ __global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
     }
 
     // epilogue: lane holds rows (g4*4 + r) and column l16 of every 16x16 tile
-    if (EPI == kEpiArgmax) {
+    if (!active) {
+      // this wave holds no rows of the tile
+    } else if (EPI == kEpiArgmax) {
       // per row: the largest of this wave's 64 columns and its first column index (columns
       // ascend with j within a lane; across the 16 lanes of a row ties go to the lower one)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float bv = -__builtin_inff();
           int bi = 0x7fffffff;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 64 + j * 16 + l16;
+          for (int j = 0; j < TJ; ++j) {
+            const int col = n0 + wn * WTN + j * 16 + l16;
             const float v = acc[i][j][r];
             if (col < p.N && v > bv) {
               bv = v;
@@ -231,7 +245,7 @@ __global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
               bi = oi;
             }
           }
-          const int row = m0 + wm * 64 + i * 16 + g4 * 4 + r;
+          const int row = m0 + wm * WTM + i * 16 + g4 * 4 + r;
           if (l16 == 0 && row < M) {
             const size_t at = (size_t)row * p.arg_ld + ntile * WN + wn;
             p.arg_val[at] = bv;
@@ -242,13 +256,13 @@ __global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
       T* C = (T*)p.C;
       if (EPI == kEpiSwiGLU) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int col = ntile * (BN / 2) + (wn * 2 + jj) * 16 + l16;
+          for (int jj = 0; jj < TJ / 2; ++jj) {
+            const int col = ntile * (BN / 2) + (wn * (TJ / 2) + jj) * 16 + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int row = m0 + wm * 64 + i * 16 + g4 * 4 + r;
+              const int row = m0 + wm * WTM + i * 16 + g4 * 4 + r;
               if (row < M && col < p.ff) {
                 const float gv = acc[i][2 * jj][r], uv = acc[i][2 * jj + 1][r];
                 C[(size_t)row * p.ldc + col] = from_f32<T>(silu_f(gv) * uv);
@@ -258,13 +272,13 @@ __global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
       } else {
         const T* R = (const T*)p.R;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 64 + j * 16 + l16;
+          for (int j = 0; j < TJ; ++j) {
+            const int col = n0 + wn * WTN + j * 16 + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int row = m0 + wm * 64 + i * 16 + g4 * 4 + r;
+              const int row = m0 + wm * WTM + i * 16 + g4 * 4 + r;
               if (row < M && col < p.N) {
                 float x = acc[i][j][r];
                 if (EPI == kEpiResidual) x += to_f32(R[(size_t)row * p.ldr + col]);
@@ -276,19 +290,50 @@ __global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
     } else {
       float* part = p.partial + (size_t)s * M * p.N;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 64 + j * 16 + l16;
+        for (int j = 0; j < TJ; ++j) {
+          const int col = n0 + wn * WTN + j * 16 + l16;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int row = m0 + wm * 64 + i * 16 + g4 * 4 + r;
+            const int row = m0 + wm * WTM + i * 16 + g4 * 4 + r;
             if (row < M && col < p.N) part[(size_t)row * p.N + col] = acc[i][j][r];
           }
         }
     }
   }
+}
+
+template <typename T, int EPI, int BN, int BM>
+__global__ void __launch_bounds__(BM * BN / 64) gemm_kernel(GemmParams p) {
+  constexpr int A_BYTES = BM * kGemmBKBytes;
+  constexpr int W_BYTES = BN * kGemmBKBytes;
+  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
+  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
+  if (M <= 0) return;
+  gemm_units<T, EPI, BN, BM>(p, M, As0, As1, As2, Ws0, Ws1, Ws2);
   // no wave may end while its last (clamped) stage loads are still writing LDS
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+// Row tile chosen on the device (GemmParams::bm = kGemmTileAuto): eight waves, two per SIMD;
+// 256 x BN tiles on all of them from kGemmTallAutoFrom rows on, 128 x BN tiles on four below
+// (the other four take part in the barriers only).  A four-wave launch with 128 x 64 wave
+// tiles for the 256-row mode ran it 15-20% slower (3B layer, 1024 packed rows: QKV 56.6
+// against 47.2 us, down 77.3 against 67.7 us) and the 128-row mode no faster.
+template <typename T, int EPI, int BN>
+__global__ void __launch_bounds__(256 * BN / 64) gemm_auto_kernel(GemmParams p) {
+  constexpr int A_BYTES = 256 * kGemmBKBytes;
+  constexpr int W_BYTES = BN * kGemmBKBytes;
+  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
+  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
+  if (M <= 0) return;
+  if (gemm_bm(p, M) == 256)
+    gemm_units<T, EPI, BN, 256>(p, M, As0, As1, As2, Ws0, Ws1, Ws2);
+  else
+    gemm_units<T, EPI, BN, 128, true, 64, 64, 4 * BN / 64>(p, M, As0, As1, As2, Ws0, Ws1, Ws2);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
@@ -321,6 +366,8 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
   constexpr int LPI = R * AQ + WQ;
   const int kiters = p.Kd / G::BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the slab's four waves; a wider launch's other waves take part in the barriers only
+  const bool active = wave < 4;
   const int g4 = lane >> 4, l16 = lane & 15;
   const int lr = lane >> 3, lpc = lane & 7;
   const char* Ab = (const char*)p.A;
@@ -347,6 +394,7 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
   }
   // loads of k-iteration `it` into a stage: the weight chunk, and the A tile(s)
   auto issue_w = [&](char* ws, int it) {
+    if (!active) return;
     const size_t off = (size_t)imin(it, kiters - 1) * kGemmBKBytes;
 #pragma unroll
     for (int q = 0; q < WQ; ++q)
@@ -354,6 +402,7 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
                                        (lds_void_t*)(ws + (wave * WQ + q) * 1024), 16, 0, 0);
   };
   auto issue_a = [&](char* a0, char* a1, int it) {
+    if (!active) return;
     const size_t off = (size_t)imin(it, kiters - 1) * kGemmBKBytes;
 #pragma unroll
     for (int rt = 0; rt < R; ++rt) {
@@ -374,7 +423,7 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
       for (int j = 0; j < NB; ++j) acc[rt][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   bool live[R];
 #pragma unroll
-  for (int rt = 0; rt < R; ++rt) live[rt] = (m0 + rt * kGemmBM + wave * 32) < M;
+  for (int rt = 0; rt < R; ++rt) live[rt] = active && (m0 + rt * kGemmBM + wave * 32) < M;
   // One wave per SIMD, so LDS latency is hidden inside the wave: all operand fragments of
   // a k-iteration are read at once, then its MFMAs run (the weight fragments serve every
   // row tile).
@@ -436,6 +485,7 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
   }
 
   // epilogue: lane holds rows g4*4 + r of each 16-row block and column l16 of each block
+  if (!active) return;
   T* C = (T*)p.C;
 #pragma unroll
   for (int rt = 0; rt < R; ++rt)
@@ -455,16 +505,11 @@ __device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, in
       }
 }
 
+// Every slab unit of one SwiGLU call (rows M read on the device), walked persistently.
 template <typename T>
-__global__ void __launch_bounds__(kSlabThreads) swiglu_slab_kernel(GemmParams p, int slabs) {
-  constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
-  constexpr int W_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
-  // three stages of {A tile 0, A tile 1, W}: 3 x (16 + 16 + 20) KB = 156 KB
-  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Bs0[A_BYTES], Bs1[A_BYTES], Bs2[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
-  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
-  if (M <= 0) return;
+__device__ __forceinline__ void slab_units(const GemmParams& p, int M, int slabs, char* As0,
+                                           char* As1, char* As2, char* Bs0, char* Bs1,
+                                           char* Bs2, char* Ws0, char* Ws1, char* Ws2) {
   const int pairs = p.ff / 16;
   const int base = pairs / slabs, rem = pairs - base * slabs;
   const int mb = ceil_div(M, kGemmBM);
@@ -488,6 +533,45 @@ __global__ void __launch_bounds__(kSlabThreads) swiglu_slab_kernel(GemmParams p,
     }
 #undef SLAB_CASE
   }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kSlabThreads) swiglu_slab_kernel(GemmParams p, int slabs) {
+  constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
+  constexpr int W_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
+  // three stages of {A tile 0, A tile 1, W}: 3 x (16 + 16 + 20) KB = 156 KB
+  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Bs0[A_BYTES], Bs1[A_BYTES], Bs2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
+  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
+  if (M <= 0) return;
+  slab_units<T>(p, M, slabs, As0, As1, As2, Bs0, Bs1, Bs2, Ws0, Ws1, Ws2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+// SwiGLU gate/up with the row tile chosen on the device: up to 768 packed rows (three row
+// groups of the slabs, each streaming the weights once more) the column slabs, from there on
+// 256 x 128 tiles of the split-K GEMM body, each of the four waves on 128 x 64, with no
+// split (its SwiGLU epilogue needs whole sums).  3B layer, gate/up: 588 rows 91.5 us on
+// the slabs, 101.8 us on the tiles; 1024 rows 133.7 us on the slabs, 105.8 us on the tiles.
+// Four waves, one per SIMD: the slab body needs more registers than two waves per SIMD
+// leave.  Each stage is one X array (the slabs' two 128-row A tiles, or the 256-row A tile)
+// and one Y array (the slab's weight chunk, or the 128-row W tile): 3 x (32 + 20) KB.
+constexpr int kSwigluTallAutoFrom = 769;
+template <typename T>
+__global__ void __launch_bounds__(kSlabThreads) swiglu_auto_kernel(GemmParams p, int slabs) {
+  constexpr int X_BYTES = 2 * kGemmBM * kGemmBKBytes;
+  constexpr int Y_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
+  static_assert(X_BYTES >= 256 * kGemmBKBytes && Y_BYTES >= 128 * kGemmBKBytes, "stage sizes");
+  __shared__ __attribute__((aligned(1024))) char X0[X_BYTES], X1[X_BYTES], X2[X_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Y0[Y_BYTES], Y1[Y_BYTES], Y2[Y_BYTES];
+  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
+  if (M <= 0) return;
+  constexpr int H = kGemmBM * kGemmBKBytes;
+  if (M >= kSwigluTallAutoFrom)
+    gemm_units<T, kEpiSwiGLU, 128, 256, false, 128, 64>(p, M, X0, X1, X2, Y0, Y1, Y2);
+  else
+    slab_units<T>(p, M, slabs, X0, X1, X2, X0 + H, X1 + H, X2 + H, Y0, Y1, Y2);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
@@ -504,7 +588,7 @@ template <typename T, int EPI, int BN>
 __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
   const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
   if (M <= 0) return;
-  const int mb = ceil_div(M, gemm_bm(p)), nt = ceil_div(p.N, BN);
+  const int mb = ceil_div(M, gemm_bm(p, M)), nt = ceil_div(p.N, BN);
   const int kiters = p.Kd / (kGemmBKBytes / (int)sizeof(T));
   const int split = gemm_split(mb * nt, kiters);
   if (split == 1) return;
@@ -557,7 +641,7 @@ int gemm_tile_n(int) { return 128; }
 
 int gemm_host_split(int M, int N, int Kd, int elem_bytes, int bm) {
   const int BN = gemm_tile_n(N);
-  return gemm_split(ceil_div(M, bm) * ceil_div(N, BN),
+  return gemm_split(ceil_div(M, gemm_bm_of(bm, M, M)) * ceil_div(N, BN),
                     Kd / (kGemmBKBytes / elem_bytes));
 }
 
@@ -579,7 +663,9 @@ size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always)
 
 template <typename T, int EPI, int BN>
 static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st) {
-  if (gemm_bm(p) == 256)
+  if (p.bm == kGemmTileAuto)
+    gemm_auto_kernel<T, EPI, BN><<<num_cu, 256 * BN / 64, 0, st>>>(p);
+  else if (gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 256)
     gemm_kernel<T, EPI, BN, 256><<<num_cu, 256 * BN / 64, 0, st>>>(p);
   else
     gemm_kernel<T, EPI, BN, 128><<<num_cu, 128 * BN / 64, 0, st>>>(p);
@@ -596,7 +682,13 @@ static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st
 
 template <typename T, int EPI>
 static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t st) {
-  if (EPI == kEpiSwiGLU && gemm_bm(p) == 128) {
+  if (EPI == kEpiSwiGLU && p.bm == kGemmTileAuto) {
+    // slabs below kGemmTallAutoFrom rows, unsplit 256-row tiles above: no reduction pass
+    const int slabs = swiglu_slabs(p.ff, num_cu);
+    swiglu_auto_kernel<T><<<num_cu, kSlabThreads, 0, st>>>(p, slabs);
+    return hipGetLastError();
+  }
+  if (EPI == kEpiSwiGLU && gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 128) {
     const int slabs = swiglu_slabs(p.ff, num_cu);
     swiglu_slab_kernel<T><<<slabs, kSlabThreads, 0, st>>>(p, slabs);
     return hipGetLastError();

@@ -81,7 +81,8 @@ struct GemmParams {
   float* arg_val;
   int32_t* arg_idx;
   int arg_ld;
-  // row tile, 128 or 256 (gemm_tile_m); 0 = gemm_tile_m(m_cap)
+  // row tile: 128 or 256; 0 = gemm_tile_m(m_cap); kGemmTileAuto = chosen on the device from
+  // the row count (gemm_bm_of)
   int bm;
 };
 
@@ -97,9 +98,20 @@ constexpr int kGemmTallExactFrom = 512;
 __host__ __device__ inline int gemm_tile_m(int m_cap, bool exact = false) {
   return (m_cap >= kGemmTallFrom || (exact && m_cap >= kGemmTallExactFrom)) ? 256 : 128;
 }
-// the row tile a GEMM call runs with
-__host__ __device__ inline int gemm_bm(const GemmParams& p) {
-  return p.bm ? p.bm : gemm_tile_m(p.m_cap);
+// A row tile left to the device: calls whose row count is known only there (a folded
+// layer's packed rows) and may fall on either side of kGemmTallAutoFrom.  One launch of
+// eight waves runs 256-row tiles with all of them from kGemmTallAutoFrom rows on, and
+// 128-row tiles with four of them below (the other four only take part in the barriers).
+constexpr int kGemmTileAuto = -1;
+constexpr int kGemmTallAutoFrom = 512;
+// the row tile a GEMM call with M rows (read on the device) runs with; every kernel that
+// re-derives a GEMM's tiling or split uses this
+__host__ __device__ inline int gemm_bm_of(int bm, int m_cap, int M) {
+  if (bm == kGemmTileAuto) return M >= kGemmTallAutoFrom ? 256 : 128;
+  return bm ? bm : gemm_tile_m(m_cap);
+}
+__host__ __device__ inline int gemm_bm(const GemmParams& p, int M) {
+  return gemm_bm_of(p.bm, p.m_cap, M);
 }
 
 constexpr int kGemmBKBytes = 128;
@@ -137,8 +149,8 @@ int gemm_host_split(int M, int N, int Kd, int elem_bytes, int bm);
 // and for every packed slot s (packed_slot[slot_row[s]] == s) the FFN input
 // A2[slot_row[s]] = h[s] / sqrt(mean(h[s]^2) + eps) * g.  One workgroup per slot.
 // by_row: the partial planes hold the K packed rows (the GEMM's split re-derived on the
-// device from its row tile bm, tiles_n column tiles and kiters k-iterations) and slot s adds
-// row slot_row[s].
+// device from its row-tile setting bm (gemm_bm_of with K rows), tiles_n column tiles and
+// kiters k-iterations) and slot s adds row slot_row[s].
 template <typename T>
 hipError_t launch_oproj_finish(const float* partial, int split, const void* H, void* h, int S,
                                int d, const int32_t* slot_row, const int32_t* packed_slot,

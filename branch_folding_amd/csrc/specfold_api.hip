@@ -209,11 +209,17 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   const int dh = s->head_dim, nq = s->n_q_heads, nkv = s->n_kv_heads;
   const int qkvd = (nq + 2 * nkv) * dh, qd = nq * dh;
   const int cus = num_cus();
-  // row tile of the GEMMs: with tau < 0 every slot is packed, so the row count is S.  (The O
-  // projection always has S rows, but below 2048 slots its 256-row tiles would double the
-  // partial planes its finish reads for no gain: at the 7B layer -2 us in the GEMM, +2.5 us
-  // in the finish.)
-  const int bm = gemm_tile_m(S, !state_in && tau < 0.f);
+  // row tile of the packed GEMMs: with tau < 0 every slot is packed, so the row count is S.
+  // (The O projection always has S rows; at 512 slots its 256-row tiles double the partial
+  // planes its finish reads for no gain -- at the 7B layer -2 us in the GEMM, +2.5 us in
+  // the finish -- so it takes them from kOprojTallFrom slots.)
+  const bool exact = !state_in && tau < 0.f;
+  // From kGemmTallExactFrom to kGemmTallFrom slots a folded call's packed row count can fall
+  // on either side of kGemmTallAutoFrom, and only the device knows it: there the GEMMs pick
+  // their row tile on the device (a call at tau = 0 packs nearly every slot).
+  const int bm = (!exact && S >= kGemmTallExactFrom && S < kGemmTallFrom)
+                     ? kGemmTileAuto : gemm_tile_m(S, exact);
+  constexpr int kOprojTallFrom = 1024;
   // a failure left behind by some earlier, unrelated HIP call on this thread must not be
   // reported as a failure of these launches
   (void)hipGetLastError();
@@ -283,7 +289,10 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   gp = GemmParams{};
   gp.A = ATT; gp.lda = L.ld_q; gp.W = w->w_o; gp.ldw = qd; gp.C = nullptr; gp.ldc = d;
   gp.partial = gpart; gp.m_dev = reuse ? count : nullptr; gp.m_cap = S; gp.N = d; gp.Kd = qd;
-  gp.bm = bm;
+  // Without REUSE the O projection's row count is S on the host whatever tau decides, so
+  // from kOprojTallFrom slots it takes the 256-row tiles (3B layer, 1024 slots: 29.0 us
+  // against 34.6-38.0 us with 128-row tiles).
+  gp.bm = reuse ? bm : (S >= kOprojTallFrom ? 256 : (bm == kGemmTileAuto ? 128 : bm));
   if (reuse) {
     gp.a_rows = packed;
     gp.a_rows_cap = S;

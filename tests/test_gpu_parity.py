@@ -102,6 +102,19 @@ WIDE = [
 ]
 
 
+# 512 to 2047 slots: a folded call's packed row count is known only on the device, so the
+# GEMMs pick their row tile there (256-row tiles from 512 packed rows, 128-row tiles and the
+# SwiGLU column slabs below).  tau = 0 packs every slot (the 256-row path), 0.05 and 0.3 fewer.
+AUTO = [
+    custom_config(name="auto-f32", num_nodes=12, block=48, hidden=256, n_q=4, n_kv=2,
+                  head_dim=64, ffn=512, prefix=40, dtype="f32", graph="dag", reveal=(1, 2),
+                  seed=91),
+    custom_config(name="auto-bf16", num_nodes=20, block=40, hidden=384, n_q=6, n_kv=2,
+                  head_dim=64, ffn=640, prefix=70, dtype="bf16", graph="tree3",
+                  reveal=(1, 2), seed=92),
+]
+
+
 def _check_intermediates(dl, cfg, ref, K, L, tag, attn_slots=None):
     """Every intermediate the workspace keeps, element-wise against the oracle's, each to
     the output tolerance (max-abs-rel over the entries the oracle evaluated):
@@ -362,8 +375,9 @@ def test_budget_sweep_ends(n, tau):
 
 
 @pytest.mark.parametrize("cfg,tau", [(EDGE[2], 0.3), (EDGE[5], 0.05), (CONFIGS[0], 0.05),
-                                     (CONFIGS[1], 0.05)],
-                         ids=["ragged-bf16-dag", "star-f32", "tiny-f32", "7b-layer"])
+                                     (CONFIGS[1], 0.05), (AUTO[1], 0.0), (AUTO[0], 0.3)],
+                         ids=["ragged-bf16-dag", "star-f32", "tiny-f32", "7b-layer",
+                              "device-tile-bf16-tau0", "device-tile-f32"])
 def test_layer_reuse_attention(cfg, tau):
     """REUSE variant (SPECFOLD_FLAG_REUSE_ATTENTION): a folded slot takes its resolved
     source's attention output; the O projection runs on the packed rows only.  Compared
@@ -536,3 +550,15 @@ def test_gate_golden_cases(dtype):
         with np.errstate(invalid="ignore"):
             expect = ~(exact <= tau)
         np.testing.assert_array_equal(m[1], expect)
+
+
+@pytest.mark.parametrize("cfg", AUTO, ids=lambda c: c.name)
+@pytest.mark.parametrize("tau", [0.0, 0.05, 0.3])
+def test_layer_device_row_tile(cfg, tau):
+    """Folded layers whose GEMM row tile is chosen on the device from the packed count."""
+    L, DeviceLayer = _dev()
+    assert 512 <= cfg.slots < 2048
+    w = _workload(cfg)
+    _, gst, _ = _check_layer(cfg, w, tau, L, DeviceLayer)
+    if tau == 0.0:
+        assert gst["K"] >= 512            # the 256-row path ran
