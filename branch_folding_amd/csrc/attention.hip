@@ -376,17 +376,17 @@ constexpr int kTrWaves = 8;
 constexpr int kTrQRows = kTrWaves * 32;   // query rows per unit
 constexpr int kTrStages = 4;
 
-template <int DH>
+template <int DH, int NWV = kTrWaves>
 struct TrTile {
   static constexpr int ROWB = DH * 2;                   // bytes per K (or V) row
   static constexpr int TILEB = kKeys * ROWB;            // bytes per K (or V) tile
   static constexpr int RP = 256 / ROWB;                 // rows per 256 bytes (1 or 2)
   static constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
-  static constexpr int QI = TILEB / 1024 / kTrWaves;    // K (and V) loads per wave per tile
+  static constexpr int QI = TILEB / 1024 / NWV;         // K (and V) loads per wave per tile
   static constexpr int LPI = 2 * QI;                    // vector-memory ops per wave per tile
   static constexpr int KSQ = DH / 32;                   // 64-byte k-steps over dh
   static constexpr int NT = DH / 16;                    // 16-wide dh tiles of the output
-  static_assert(QI >= 1 && TILEB % (1024 * kTrWaves) == 0, "tile/loader mismatch");
+  static_assert(QI >= 1 && TILEB % (1024 * NWV) == 0, "tile/loader mismatch");
 };
 // physical 16-byte chunk = logical chunk ^ swizzle(row)
 template <int DH>
@@ -423,37 +423,37 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
 typedef short tr_v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) tr_v4s lds_tr_v4s;
 
-template <int DH>
+template <int DH, int NB = 2>
 __device__ __forceinline__ void tr_attend(const char* Ks, const char* Vs, int nkeys,
-                                          const uint4 (&qf)[2][TrTile<DH>::KSQ],
+                                          const uint4 (&qf)[NB][TrTile<DH>::KSQ],
                                           const int (&kofs)[TrTile<DH>::KSQ],
                                           const int (&vofs)[TrTile<DH>::NT], float scale_log2,
-                                          AttnState (&st)[2], f32x4 (&o)[2][TrTile<DH>::NT]) {
+                                          AttnState (&st)[NB], f32x4 (&o)[NB][TrTile<DH>::NT]) {
   using Tt = TrTile<DH>;
   // The two waves sharing a SIMD alternate between MFMA phases and the softmax; the MFMA
   // phases run at raised wave priority, so one wave's MFMAs issue ahead of the other's
   // softmax and the matrix pipe stays busy.
   __builtin_amdgcn_s_setprio(1);
   // S^T = K Q^T: sc[b][t][r] = key t*16 + g4*4 + r, query l16 of block b
-  f32x4 sc[2][4];
+  f32x4 sc[NB][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    sc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    sc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < NB; ++b) sc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < Tt::KSQ; ++ks) {
       const uint4 kf = *reinterpret_cast<const uint4*>(Ks + kofs[ks] + t * 16 * Tt::ROWB);
-      sc[0][t] = mma_kstep(kf, qf[0][ks], sc[0][t], bf16());
-      sc[1][t] = mma_kstep(kf, qf[1][ks], sc[1][t], bf16());
+#pragma unroll
+      for (int b = 0; b < NB; ++b) sc[b][t] = mma_kstep(kf, qf[b][ks], sc[b][t], bf16());
     }
   }
   __builtin_amdgcn_s_setprio(0);
-  softmax_tile<Tt::NT>(sc[0], nkeys, scale_log2, st[0], o[0]);
-  softmax_tile<Tt::NT>(sc[1], nkeys, scale_log2, st[1], o[1]);
-  // P^T as the B operand: k-step mu covers keys 32mu + 4*g4 + 0..3 and 32mu + 16 + 4*g4 + 0..3
-  uint4 pb[2][2];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < NB; ++b) softmax_tile<Tt::NT>(sc[b], nkeys, scale_log2, st[b], o[b]);
+  // P^T as the B operand: k-step mu covers keys 32mu + 4*g4 + 0..3 and 32mu + 16 + 4*g4 + 0..3
+  uint4 pb[NB][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int mu = 0; mu < 2; ++mu) {
       float pf[8];
@@ -477,8 +477,8 @@ __device__ __forceinline__ void tr_attend(const char* Ks, const char* Vs, int nk
           (lds_tr_v4s*)(Vs + vofs[nt] + (32 * mu + 16) * Tt::ROWB));
       const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
       const uint4 vf = make_uint4(l2.x, l2.y, h2.x, h2.y);
-      o[0][nt] = mma_kstep(vf, pb[0][mu], o[0][nt], bf16());
-      o[1][nt] = mma_kstep(vf, pb[1][mu], o[1][nt], bf16());
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b][nt] = mma_kstep(vf, pb[b][mu], o[b][nt], bf16());
     }
   __builtin_amdgcn_s_setprio(0);
 }
@@ -708,16 +708,19 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
   constexpr int VE = A::VE;
   __shared__ __attribute__((aligned(16))) T Ks[kKeys * A::LDK];
   __shared__ __attribute__((aligned(16))) T Vt[DH * A::LDV];
-  // the plan is loaded with the count (without a prefix it is not written and not used)
+  // the plan is loaded with the count (without a prefix phase it is not written and not used)
   const int plan_ns = p.plan[0], plan_merged = p.plan[1];
   const int K = imin(*p.count, p.cap);
   if (K <= 0) return;
   const int g = p.n_q / p.n_kv;
+  // a short prefix is streamed here, tile by tile, ahead of the block (no prefix phase ran)
+  const bool fused = attn_fused_prefix(p.P);
   // plane 0 holds all prefix splits when attn_merge_kernel merged them
-  const int ns = p.P <= 0 ? 0 : (plan_merged ? 1 : plan_ns);
+  const int ns = (p.P <= 0 || fused) ? 0 : (plan_merged ? 1 : plan_ns);
   const int qtiles = ceil_div(p.B * g, kQRows);
   const int units = p.N * p.n_kv * qtiles;
-  const int kchunks = ceil_div(p.B, kKeys);
+  const int pchunks = fused ? ceil_div(p.P, kKeys) : 0;
+  const int tiles = pchunks + ceil_div(p.B, kKeys);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g4 = lane >> 4, l16 = lane & 15;
   const T* qkv = (const T*)p.qkv;
   const long koff = (long)p.n_q * DH, voff = (long)(p.n_q + p.n_kv) * DH;
@@ -738,8 +741,25 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
     auto vp = [&](int key0) {
       return [=](int j) { return qkv + (size_t)row_of(n * p.B + key0 + j) * p.ld_qkv + voff + (size_t)kvh * DH; };
     };
+    // tile c < pchunks: prefix keys 64c.., through the caller's strided view; then the block
+    const T* pkb = (const T*)p.pk + (size_t)kvh * p.stride_head;
+    const T* pvb = (const T*)p.pv + (size_t)kvh * p.stride_head;
+    auto tile_keys = [&](int c) {
+      return c < pchunks ? imin(kKeys, p.P - c * kKeys) : imin(kKeys, p.B - (c - pchunks) * kKeys);
+    };
     KVRegs<T, DH> kv;
-    load_kv<T, DH>(kv, imin(kKeys, p.B), kp(0), vp(0));
+    auto load_tile = [&](int c) {
+      if (c < pchunks) {
+        const size_t key0 = (size_t)c * kKeys;
+        load_kv<T, DH>(kv, tile_keys(c),
+                       [=](int j) { return pkb + (key0 + j) * p.stride_tok; },
+                       [=](int j) { return pvb + (key0 + j) * p.stride_tok; });
+      } else {
+        const int key0 = (c - pchunks) * kKeys;
+        load_kv<T, DH>(kv, tile_keys(c), kp(key0), vp(key0));
+      }
+    };
+    load_tile(0);
     const T* qp = qkv + (size_t)k * p.ld_qkv + (size_t)h * DH;
     uint4 qf[A::KSTEPS_QK];
 #pragma unroll
@@ -788,16 +808,12 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
       }
     }
 
-    for (int c = 0; c < kchunks; ++c) {
-      const int key0 = c * kKeys;
-      const int nkeys = imin(kKeys, p.B - key0);
+    for (int c = 0; c < tiles; ++c) {
+      const int nkeys = tile_keys(c);
       __syncthreads();
       store_kv<T, DH>(Ks, Vt, kv);
       __syncthreads();
-      if (c + 1 < kchunks) {
-        const int key1 = key0 + kKeys;
-        load_kv<T, DH>(kv, imin(kKeys, p.B - key1), kp(key1), vp(key1));
-      }
+      if (c + 1 < tiles) load_tile(c + 1);
       attend_tile<T, DH>(Ks, Vt, nkeys, qf, p.scale_log2, st, o);
     }
     if (valid) {
@@ -809,6 +825,156 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
         for (int e = 0; e < 4; ++e) op[nt * 16 + g4 * 4 + e] = from_f32<T>(o[nt][e] * inv);
     }
   }
+}
+
+// ------------------------------------------------------------------------------------
+// Block phase with a short prefix streamed in, bf16 (attn_fused_prefix): a unit is 64 query
+// rows -- (position, head) pairs of one branch and KV head, 16 per wave -- that attend to
+// every prefix key, read through the caller's strided view, and then to the branch's own
+// block keys, gathered from the packed K/V rows through slot_row.  The tiles stream through
+// the same four-stage direct-to-LDS ring as the 256-query prefix kernel (three tiles in
+// flight, transposed V reads); the result is normalised and stored as the slot's attention
+// output, with no partials in between.
+// ------------------------------------------------------------------------------------
+constexpr int kSlotWaves = 4;
+constexpr int kSlotQRows = kSlotWaves * 16;
+
+template <int DH>
+__global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnParams p) {
+  using Tt = TrTile<DH, kSlotWaves>;
+  constexpr int QI = Tt::QI, LPI = Tt::LPI, KSQ = Tt::KSQ, NT = Tt::NT;
+  __shared__ __attribute__((aligned(1024))) char K0[Tt::TILEB], K1[Tt::TILEB], K2[Tt::TILEB],
+      K3[Tt::TILEB];
+  __shared__ __attribute__((aligned(1024))) char V0[Tt::TILEB], V1[Tt::TILEB], V2[Tt::TILEB],
+      V3[Tt::TILEB];
+  const int K = imin(*p.count, p.cap);
+  if (K <= 0) return;
+  const int g = p.n_q / p.n_kv;
+  const int rows = p.B * g;                       // query rows per (branch, KV head)
+  const int qtiles = ceil_div(rows, kSlotQRows);
+  const int units = p.N * p.n_kv * qtiles;
+  const int pch = p.P > 0 ? ceil_div(p.P, kKeys) : 0;
+  const int n = pch + ceil_div(p.B, kKeys);       // key tiles per unit
+  const int lane = threadIdx.x & 63, g4 = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* qkv = (const char*)p.qkv;
+  const long ldq = p.ld_qkv * 2, st_tok = p.stride_tok * 2, st_head = p.stride_head * 2;
+  auto row_of = [&](int slot) { return imin(imax(p.slot_row[slot], 0), K - 1); };
+
+  // LDS byte offsets of this lane's fragments (as in the prefix kernel)
+  int kofs[KSQ], vofs[NT];
+#pragma unroll
+  for (int ks = 0; ks < KSQ; ++ks)
+    kofs[ks] = l16 * Tt::ROWB + (((4 * ks + g4) ^ tr_kswz<DH>(l16)) << 4);
+  {
+    const int vr = 4 * g4 + (l16 >> 2);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      vofs[nt] = vr * Tt::ROWB + (((2 * nt + ((l16 & 3) >> 1)) ^ tr_vswz<DH>(vr)) << 4) +
+                 8 * (l16 & 1);
+  }
+  // loader geometry: load q of this wave fills LDS bytes (wave*QI + q)*1024 + 16*lane of a
+  // stage: key row lr[q] of the tile, physical chunk pc, fetching the matching logical chunk
+  int lr[QI];
+  uint32_t lkc[QI], lvc[QI];
+#pragma unroll
+  for (int q = 0; q < QI; ++q) {
+    const int byte = (wave * QI + q) * 1024 + 16 * lane;
+    const int r = byte / Tt::ROWB, pc = (byte % Tt::ROWB) >> 4;
+    lr[q] = r;
+    lkc[q] = (uint32_t)((pc ^ tr_kswz<DH>(r)) << 4);
+    lvc[q] = (uint32_t)((pc ^ tr_vswz<DH>(r)) << 4);
+  }
+  const int wq = wave * QI * 1024;                  // this wave's LDS slice of a stage
+
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int qt = u % qtiles, rest = u / qtiles;
+    const int kvh = rest % p.n_kv, nb = rest / p.n_kv;
+    const int r = qt * kSlotQRows + wave * 16 + l16;
+    const bool valid = r < rows;
+    const int rr = valid ? r : rows - 1;
+    const int i = rr / g, h = kvh * g + (rr - (rr / g) * g);
+    uint4 qf[1][KSQ];
+    {
+      const char* qp = qkv + (size_t)row_of(nb * p.B + i) * ldq + (size_t)h * DH * 2;
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) qf[0][ks] = ld16(qp + (4 * ks + g4) * 16);
+    }
+    AttnState st[1] = {{-__builtin_inff(), 0.f}};
+    f32x4 o[1][NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const char* kpre = (const char*)p.pk + (size_t)kvh * st_head;
+    const char* vpre = (const char*)p.pv + (size_t)kvh * st_head;
+    const char* kblk = qkv + ((size_t)p.n_q + kvh) * DH * 2;           // K heads of a row
+    const char* vblk = qkv + ((size_t)p.n_q + p.n_kv + kvh) * DH * 2;  // V heads of a row
+    // Every tile slot issues its loads, so the wait count stays a constant: slots past the
+    // unit's last tile load packed row 0's line; rows past the prefix (or the block) of a
+    // ragged tile reload its last row (finite values the softmax weights with 0).
+    auto issue = [&](char* Kd, char* Vd, int c) {
+      const uint32_t kl = lds_addr(Kd) + wq, vl = lds_addr(Vd) + wq;
+      const char* ks[QI];
+      const char* vs[QI];
+      if (c >= n) {
+#pragma unroll
+        for (int q = 0; q < QI; ++q) ks[q] = kblk, vs[q] = vblk;
+      } else if (c < pch) {
+        const int key0 = c * kKeys;
+#pragma unroll
+        for (int q = 0; q < QI; ++q) {
+          const long key = imin(key0 + lr[q], p.P - 1);
+          ks[q] = kpre + key * st_tok + lkc[q];
+          vs[q] = vpre + key * st_tok + lvc[q];
+        }
+      } else {
+        const int j0 = (c - pch) * kKeys;
+#pragma unroll
+        for (int q = 0; q < QI; ++q) {
+          const size_t prow = (size_t)row_of(nb * p.B + imin(j0 + lr[q], p.B - 1));
+          ks[q] = kblk + prow * ldq + lkc[q];
+          vs[q] = vblk + prow * ldq + lvc[q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < QI; ++q) {
+        dma16(ks[q], kl + q * 1024);
+        dma16(vs[q], vl + q * 1024);
+      }
+    };
+    auto body = [&](const char* Kc, const char* Vc, char* Kn, char* Vn, int c) {
+      if (c >= n) return;
+      __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm(2 * LPI));
+      __builtin_amdgcn_s_barrier();
+      const int nkeys = c < pch ? imin(kKeys, p.P - c * kKeys)
+                                : imin(kKeys, p.B - (c - pch) * kKeys);
+      tr_attend<DH, 1>(Kc, Vc, nkeys, qf, kofs, vofs, p.scale_log2, st, o);
+      issue(Kn, Vn, c + 3);
+    };
+    // the previous unit's loads and LDS reads and this unit's query loads are done before
+    // the ring is refilled
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+    issue(K0, V0, 0);
+    issue(K1, V1, 1);
+    issue(K2, V2, 2);
+    for (int it = 0; it < n; it += kTrStages) {
+      body(K0, V0, K3, V3, it);
+      body(K1, V1, K0, V0, it + 1);
+      body(K2, V2, K1, V1, it + 2);
+      body(K3, V3, K2, V2, it + 3);
+    }
+    if (valid) {
+      const float inv = 1.0f / st[0].l;
+      bf16* op = (bf16*)p.out + (size_t)(nb * p.B + i) * p.ld_out + (size_t)h * DH;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        st_part4(op + nt * 16 + g4 * 4, o[0][nt][0] * inv, o[0][nt][1] * inv,
+                 o[0][nt][2] * inv, o[0][nt][3] * inv);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
 }
 
 size_t attn_partial_rows(int S, int g, int n_kv, int P, int dh, int elem_bytes) {
@@ -839,7 +1005,8 @@ static bool merge_possible(int cap, int g, int n_kv, int P, int S, int dh, int e
 
 template <typename T>
 hipError_t launch_attn_prefix(const AttnParams& p, int num_cu, hipStream_t st) {
-  if (p.P <= 0) return hipSuccess;
+  // no prefix, or a short one that the block phase streams itself
+  if (p.P <= 0 || attn_fused_prefix(p.P)) return hipSuccess;
   const int mrows = ceil_div(p.cap * p.n_q, 4);
   const int mgrid = mrows < 4 * num_cu ? mrows : 4 * num_cu;   // grid-stride over rows
   const bool tr = attn_use_tr((int)sizeof(T), p.P);
@@ -861,6 +1028,15 @@ hipError_t launch_attn_prefix(const AttnParams& p, int num_cu, hipStream_t st) {
 template <typename T>
 hipError_t launch_attn_block(const AttnParams& p, int num_cu, hipStream_t st) {
   const int g = p.n_q / p.n_kv;
+  if (sizeof(T) == 2 && attn_fused_prefix(p.P)) {
+    // bf16 with a short prefix: one pass per slot over the prefix and the block
+    const int units = p.N * p.n_kv * ceil_div(p.B * g, kSlotQRows);
+    const int grid = units < num_cu ? units : num_cu;
+    if (p.dh == 128) attn_slot_tr_kernel<128><<<grid, kSlotWaves * 64, 0, st>>>(p);
+    else if (p.dh == 64) attn_slot_tr_kernel<64><<<grid, kSlotWaves * 64, 0, st>>>(p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   const int units = p.N * p.n_kv * ceil_div(p.B * g, kQRows);
   const int grid = units < 2 * num_cu ? units : 2 * num_cu;
   if (p.dh == 128) attn_block_kernel<T, 128><<<grid, 256, 0, st>>>(p);

@@ -218,6 +218,18 @@ struct AttnParams {
 };
 
 constexpr int kAttnMaxSplit = 32;
+// Prefixes of at most kAttnFusedMaxPrefix keys are not run as a separate per-packed-row
+// phase: every slot's query streams the prefix tiles (through the same zero-copy view) and
+// then its branch's block tiles in the block-phase kernel.  That recomputes the prefix
+// scores of a packed row once per slot that takes it, but the prefix stays L2-resident and
+// no split partials are written, re-read per slot and merged.  7B layer (512-key prefix):
+// 22.6 us for the fused pass against 12.5 + 16.0 us for the two phases (event probes).  A
+// fused unit walks its key tiles one after another (~1.5-2 us each), so longer prefixes
+// keep the split prefix phase.
+constexpr int kAttnFusedMaxPrefix = 512;
+__host__ __device__ inline bool attn_fused_prefix(int P) {
+  return P > 0 && P <= kAttnFusedMaxPrefix;
+}
 // Prefix-phase kernels: bf16 prefixes of at least kAttnTrMinPrefix keys run 256-query
 // units, one workgroup per CU (direct-to-LDS K/V ring, transposed V reads); shorter bf16
 // prefixes and fp32 run 64-query units, two workgroups per CU (K/V staged through

@@ -78,6 +78,23 @@ LONG_PREFIX = [
 ]
 
 
+# Prefixes up to 512 keys are streamed by the block phase itself, tile by tile ahead of the
+# branch's block; longer ones below the 256-query kernel's 2048 (bf16) or any length (fp32)
+# run the 64-query prefix phase with split partials: the last fused length, the first
+# unfused one and a ragged mid-length prefix, in both dtypes.
+MID_PREFIX = [
+    custom_config(name="midp-fused-bf16", num_nodes=7, block=20, hidden=256, n_q=4, n_kv=2,
+                  head_dim=128, ffn=256, prefix=512, dtype="bf16", graph="tree3",
+                  reveal=(1, 2), seed=93),
+    custom_config(name="midp-bf16", num_nodes=7, block=20, hidden=256, n_q=4, n_kv=2,
+                  head_dim=128, ffn=256, prefix=513, dtype="bf16", graph="tree3",
+                  reveal=(1, 2), seed=94),
+    custom_config(name="midp-f32", num_nodes=6, block=18, hidden=128, n_q=6, n_kv=2,
+                  head_dim=64, ffn=256, prefix=1500, dtype="f32", graph="dag",
+                  reveal=(1, 2), seed=95),
+]
+
+
 # 2048+ slots: the split-K GEMMs run 256-row tiles (8 waves); every slot compared, with
 # dense (2048 packed rows = 8 row tiles) and folded (a ragged last row tile) packings.
 TALL = [
@@ -562,3 +579,10 @@ def test_layer_device_row_tile(cfg, tau):
     _, gst, _ = _check_layer(cfg, w, tau, L, DeviceLayer)
     if tau == 0.0:
         assert gst["K"] >= 512            # the 256-row path ran
+
+
+@pytest.mark.parametrize("cfg", MID_PREFIX, ids=lambda c: c.name)
+@pytest.mark.parametrize("tau", [-1.0, 0.05])
+def test_layer_mid_prefix(cfg, tau):
+    L, DeviceLayer = _dev()
+    _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
