@@ -714,7 +714,7 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
   if (K <= 0) return;
   const int g = p.n_q / p.n_kv;
   // a short prefix is streamed here, tile by tile, ahead of the block (no prefix phase ran)
-  const bool fused = attn_fused_prefix(p.P);
+  const bool fused = p.fused != 0;
   // plane 0 holds all prefix splits when attn_merge_kernel merged them
   const int ns = (p.P <= 0 || fused) ? 0 : (plan_merged ? 1 : plan_ns);
   const int qtiles = ceil_div(p.B * g, kQRows);
@@ -828,7 +828,7 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
 }
 
 // ------------------------------------------------------------------------------------
-// Block phase with a short prefix streamed in, bf16 (attn_fused_prefix): a unit is 64 query
+// Block phase with a short prefix streamed in, bf16 (AttnParams::fused): a unit is 64 query
 // rows -- (position, head) pairs of one branch and KV head, 16 per wave -- that attend to
 // every prefix key, read through the caller's strided view, and then to the branch's own
 // block keys, gathered from the packed K/V rows through slot_row.  The tiles stream through
@@ -838,6 +838,7 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
 // ------------------------------------------------------------------------------------
 constexpr int kSlotWaves = 4;
 constexpr int kSlotQRows = kSlotWaves * 16;
+static_assert(kSlotQRows == kAttnSlotQRows, "unit size of the per-slot pass");
 
 template <int DH>
 __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnParams p) {
@@ -1006,7 +1007,7 @@ static bool merge_possible(int cap, int g, int n_kv, int P, int S, int dh, int e
 template <typename T>
 hipError_t launch_attn_prefix(const AttnParams& p, int num_cu, hipStream_t st) {
   // no prefix, or a short one that the block phase streams itself
-  if (p.P <= 0 || attn_fused_prefix(p.P)) return hipSuccess;
+  if (p.P <= 0 || p.fused) return hipSuccess;
   const int mrows = ceil_div(p.cap * p.n_q, 4);
   const int mgrid = mrows < 4 * num_cu ? mrows : 4 * num_cu;   // grid-stride over rows
   const bool tr = attn_use_tr((int)sizeof(T), p.P);
@@ -1028,7 +1029,7 @@ hipError_t launch_attn_prefix(const AttnParams& p, int num_cu, hipStream_t st) {
 template <typename T>
 hipError_t launch_attn_block(const AttnParams& p, int num_cu, hipStream_t st) {
   const int g = p.n_q / p.n_kv;
-  if (sizeof(T) == 2 && attn_fused_prefix(p.P)) {
+  if (sizeof(T) == 2 && p.fused) {
     // bf16 with a short prefix: one pass per slot over the prefix and the block
     const int units = p.N * p.n_kv * ceil_div(p.B * g, kSlotQRows);
     const int grid = units < num_cu ? units : num_cu;

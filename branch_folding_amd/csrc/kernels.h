@@ -215,6 +215,8 @@ struct AttnParams {
   // the packed count of this call.  The prefix phase writes it; the split merge and the block
   // phase load it next to the count instead of re-deriving both in every workgroup.
   int32_t* plan;
+  // nonzero: no prefix phase; the block phase streams the prefix itself (attn_fused_prefix)
+  int fused;
 };
 
 constexpr int kAttnMaxSplit = 32;
@@ -224,11 +226,15 @@ constexpr int kAttnMaxSplit = 32;
 // scores of a packed row once per slot that takes it, but the prefix stays L2-resident and
 // no split partials are written, re-read per slot and merged.  7B layer (512-key prefix):
 // 22.6 us for the fused pass against 12.5 + 16.0 us for the two phases (event probes).  A
-// fused unit walks its key tiles one after another (~1.5-2 us each), so longer prefixes
-// keep the split prefix phase.
+// fused unit walks its key tiles one after another (~1.5-2 us each), so longer prefixes keep
+// the split prefix phase, and so do calls whose units (64 query rows of one branch and KV
+// head) would need more than one round over the CUs: at 1 + 63 branches of the 7B layer the
+// fused pass (1024 units) made the layer 374 -> 404 us.
 constexpr int kAttnFusedMaxPrefix = 512;
-__host__ __device__ inline bool attn_fused_prefix(int P) {
-  return P > 0 && P <= kAttnFusedMaxPrefix;
+constexpr int kAttnSlotQRows = 64;
+inline bool attn_fused_prefix(int P, int N, int B, int n_q, int n_kv, int num_cu) {
+  const long units = (long)N * n_kv * ((B * (n_q / n_kv) + kAttnSlotQRows - 1) / kAttnSlotQRows);
+  return P > 0 && P <= kAttnFusedMaxPrefix && units <= num_cu;
 }
 // Prefix-phase kernels: bf16 prefixes of at least kAttnTrMinPrefix keys run 256-query
 // units, one workgroup per CU (direct-to-LDS K/V ring, transposed V reads); shorter bf16

@@ -276,6 +276,7 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   ap.part_o = ws + L.part_o; ap.part_lse = (float*)(ws + L.part_lse);
   ap.plan = (int32_t*)(ws + L.plan);
   ap.S = S; ap.slot_row = slot_row; ap.N = N; ap.B = B; ap.out = ATT; ap.ld_out = L.ld_q;
+  ap.fused = attn_fused_prefix(s->prefix_len, N, B, nq, nkv, cus) ? 1 : 0;
   HIP_CHECK(mark(SPECFOLD_STEP_ATTN_PREFIX, true));
   HIP_CHECK(launch_attn_prefix<T>(ap, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_ATTN_PREFIX, false));
