@@ -150,25 +150,25 @@ __device__ __forceinline__ float4 ld_part4(const bf16* p) {
   return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
 }
 
-// Online-softmax update of one 64-key tile for the lane's query: sc[t][r] holds the raw
-// score of key t*16 + (lane/16)*4 + r and becomes its unnormalised weight
-// 2^(score * scale_log2 - m).  Keys >= nkeys (a ragged last tile) get weight 0.  The
-// running output is rescaled only when some lane's running maximum moved.
-template <int NT>
-__device__ __forceinline__ void softmax_tile(f32x4 (&sc)[4], int nkeys, float scale_log2,
+// Online-softmax update of one tile of KC x 16 keys (64 by default) for the lane's query:
+// sc[t][r] holds the raw score of key t*16 + (lane/16)*4 + r and becomes its unnormalised
+// weight 2^(score * scale_log2 - m).  Keys >= nkeys (a ragged last tile) get weight 0;
+// nkeys >= 1.  The running output is rescaled only when some lane's running maximum moved.
+template <int NT, int KC = 4>
+__device__ __forceinline__ void softmax_tile(f32x4 (&sc)[KC], int nkeys, float scale_log2,
                                              AttnState& st, f32x4 (&o)[NT]) {
-  if (nkeys < kKeys) {   // uniform branch, ragged tiles only
+  if (nkeys < KC * 16) {   // uniform branch, ragged tiles only
     // key t*16 + g4*4 + r is past the end iff t*16 + r >= nkeys - g4*4
     const int th = nkeys - ((threadIdx.x & 63) >> 4) * 4;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < KC; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (t * 16 + r >= th) sc[t][r] = -__builtin_inff();
   }
   float mloc = sc[0][0];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < KC; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[t][r]);
   mloc = group4_max(mloc);
@@ -176,7 +176,7 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&sc)[4], int nkeys, float sc
   const float alpha = fast_exp2(st.m - m_new);           // st.m = -inf -> 0
   float lsum = 0.f;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < KC; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float pv = fast_exp2(fmaf(sc[t][r], scale_log2, -m_new));
@@ -423,21 +423,24 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
 typedef short tr_v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) tr_v4s lds_tr_v4s;
 
-template <int DH, int NB = 2>
+// KC x 16 keys starting at the stage rows Ks / Vs point at (a whole 64-key tile, or half of
+// one with KC = 2); nkeys >= 1 of them are live.
+template <int DH, int NB = 2, int KC = 4>
 __device__ __forceinline__ void tr_attend(const char* Ks, const char* Vs, int nkeys,
                                           const uint4 (&qf)[NB][TrTile<DH>::KSQ],
                                           const int (&kofs)[TrTile<DH>::KSQ],
                                           const int (&vofs)[TrTile<DH>::NT], float scale_log2,
                                           AttnState (&st)[NB], f32x4 (&o)[NB][TrTile<DH>::NT]) {
   using Tt = TrTile<DH>;
+  static_assert(KC == 2 || KC == 4, "whole or half tiles");
   // The two waves sharing a SIMD alternate between MFMA phases and the softmax; the MFMA
   // phases run at raised wave priority, so one wave's MFMAs issue ahead of the other's
   // softmax and the matrix pipe stays busy.
   __builtin_amdgcn_s_setprio(1);
   // S^T = K Q^T: sc[b][t][r] = key t*16 + g4*4 + r, query l16 of block b
-  f32x4 sc[NB][4];
+  f32x4 sc[NB][KC];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < KC; ++t) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) sc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -449,13 +452,14 @@ __device__ __forceinline__ void tr_attend(const char* Ks, const char* Vs, int nk
   }
   __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-  for (int b = 0; b < NB; ++b) softmax_tile<Tt::NT>(sc[b], nkeys, scale_log2, st[b], o[b]);
+  for (int b = 0; b < NB; ++b) softmax_tile<Tt::NT, KC>(sc[b], nkeys, scale_log2, st[b], o[b]);
   // P^T as the B operand: k-step mu covers keys 32mu + 4*g4 + 0..3 and 32mu + 16 + 4*g4 + 0..3
-  uint4 pb[NB][2];
+  constexpr int MU = KC / 2;
+  uint4 pb[NB][MU];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int mu = 0; mu < 2; ++mu) {
+    for (int mu = 0; mu < MU; ++mu) {
       float pf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -468,7 +472,7 @@ __device__ __forceinline__ void tr_attend(const char* Ks, const char* Vs, int nk
   // two key quads per lane group as the P^T operand above
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-  for (int mu = 0; mu < 2; ++mu)
+  for (int mu = 0; mu < MU; ++mu)
 #pragma unroll
     for (int nt = 0; nt < Tt::NT; ++nt) {
       const tr_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -829,25 +833,33 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
 
 // ------------------------------------------------------------------------------------
 // Block phase with a short prefix streamed in, bf16 (AttnParams::fused): a unit is 64 query
-// rows -- (position, head) pairs of one branch and KV head, 16 per wave -- that attend to
-// every prefix key, read through the caller's strided view, and then to the branch's own
-// block keys, gathered from the packed K/V rows through slot_row.  The tiles stream through
-// the same four-stage direct-to-LDS ring as the 256-query prefix kernel (three tiles in
-// flight, transposed V reads); the result is normalised and stored as the slot's attention
-// output, with no partials in between.
+// rows -- (position, head) pairs of one branch and KV head -- that attend to every prefix
+// key, read through the caller's strided view, and then to the branch's own block keys,
+// gathered from the packed K/V rows through slot_row.  The tiles stream through the same
+// four-stage direct-to-LDS ring as the 256-query prefix kernel (three tiles in flight,
+// transposed V reads).  Eight waves, two per SIMD: the waves w and w + 4 hold the same 16
+// query rows and take the first and the second 32 keys of every tile, each with its own
+// online-softmax state, so each SIMD runs two independent MFMA/softmax chains (with one
+// wave per SIMD the chain's latency set the time).  The two states of a row are merged
+// through LDS at the end, and the result is stored as the slot's attention output, with
+// no partials in HBM.
 // ------------------------------------------------------------------------------------
-constexpr int kSlotWaves = 4;
-constexpr int kSlotQRows = kSlotWaves * 16;
+constexpr int kSlotWaves = 8;
+constexpr int kSlotQRows = 64;
 static_assert(kSlotQRows == kAttnSlotQRows, "unit size of the per-slot pass");
+static_assert(kSlotQRows == (kSlotWaves / 2) * 16, "a wave pair per 16 query rows");
 
 template <int DH>
 __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnParams p) {
   using Tt = TrTile<DH, kSlotWaves>;
   constexpr int QI = Tt::QI, LPI = Tt::LPI, KSQ = Tt::KSQ, NT = Tt::NT;
+  constexpr int HALF = kKeys / 2;                  // keys per wave per tile
   __shared__ __attribute__((aligned(1024))) char K0[Tt::TILEB], K1[Tt::TILEB], K2[Tt::TILEB],
       K3[Tt::TILEB];
   __shared__ __attribute__((aligned(1024))) char V0[Tt::TILEB], V1[Tt::TILEB], V2[Tt::TILEB],
       V3[Tt::TILEB];
+  // after a unit's last tile, stage K<rg> holds the second-half state of row group rg
+  static_assert((NT * 4 + 2) * 64 * 4 <= Tt::TILEB, "merge slot of a row group");
   const int K = imin(*p.count, p.cap);
   if (K <= 0) return;
   const int g = p.n_q / p.n_kv;
@@ -858,9 +870,11 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
   const int n = pch + ceil_div(p.B, kKeys);       // key tiles per unit
   const int lane = threadIdx.x & 63, g4 = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = wave & 3, half = wave >> 2;      // row group; first or second 32 keys
   const char* qkv = (const char*)p.qkv;
   const long ldq = p.ld_qkv * 2, st_tok = p.stride_tok * 2, st_head = p.stride_head * 2;
   auto row_of = [&](int slot) { return imin(imax(p.slot_row[slot], 0), K - 1); };
+  float* mslot = (float*)(rg == 0 ? K0 : rg == 1 ? K1 : rg == 2 ? K2 : K3);
 
   // LDS byte offsets of this lane's fragments (as in the prefix kernel)
   int kofs[KSQ], vofs[NT];
@@ -887,11 +901,12 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
     lvc[q] = (uint32_t)((pc ^ tr_vswz<DH>(r)) << 4);
   }
   const int wq = wave * QI * 1024;                  // this wave's LDS slice of a stage
+  const int hofs = half * HALF * Tt::ROWB;          // this wave's keys inside a stage
 
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int qt = u % qtiles, rest = u / qtiles;
     const int kvh = rest % p.n_kv, nb = rest / p.n_kv;
-    const int r = qt * kSlotQRows + wave * 16 + l16;
+    const int r = qt * kSlotQRows + rg * 16 + l16;
     const bool valid = r < rows;
     const int rr = valid ? r : rows - 1;
     const int i = rr / g, h = kvh * g + (rr - (rr / g) * g);
@@ -901,6 +916,11 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks) qf[0][ks] = ld16(qp + (4 * ks + g4) * 16);
     }
+    // packed rows of the first block tile's keys, read with the queries: looked up inside
+    // the ring, the index loads would make the wave wait for every tile in flight
+    int brow[QI];
+#pragma unroll
+    for (int q = 0; q < QI; ++q) brow[q] = row_of(nb * p.B + imin(lr[q], p.B - 1));
     AttnState st[1] = {{-__builtin_inff(), 0.f}};
     f32x4 o[1][NT];
 #pragma unroll
@@ -928,6 +948,12 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
           ks[q] = kpre + key * st_tok + lkc[q];
           vs[q] = vpre + key * st_tok + lvc[q];
         }
+      } else if (c == pch) {
+#pragma unroll
+        for (int q = 0; q < QI; ++q) {
+          ks[q] = kblk + (size_t)brow[q] * ldq + lkc[q];
+          vs[q] = vblk + (size_t)brow[q] * ldq + lvc[q];
+        }
       } else {
         const int j0 = (c - pch) * kKeys;
 #pragma unroll
@@ -949,7 +975,9 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
       __builtin_amdgcn_s_barrier();
       const int nkeys = c < pch ? imin(kKeys, p.P - c * kKeys)
                                 : imin(kKeys, p.B - (c - pch) * kKeys);
-      tr_attend<DH, 1>(Kc, Vc, nkeys, qf, kofs, vofs, p.scale_log2, st, o);
+      const int nk = nkeys - half * HALF;           // this wave's live keys (wave-uniform)
+      if (nk > 0)
+        tr_attend<DH, 1, 2>(Kc + hofs, Vc + hofs, nk, qf, kofs, vofs, p.scale_log2, st, o);
       issue(Kn, Vn, c + 3);
     };
     // the previous unit's loads and LDS reads and this unit's query loads are done before
@@ -966,13 +994,35 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
       body(K2, V2, K1, V1, it + 2);
       body(K3, V3, K2, V2, it + 3);
     }
-    if (valid) {
-      const float inv = 1.0f / st[0].l;
-      bf16* op = (bf16*)p.out + (size_t)(nb * p.B + i) * p.ld_out + (size_t)h * DH;
+    // merge the wave pair's states: every wave's ring loads (the unused trailing ones too)
+    // have landed and every tile has been read before the second halves are written
+    __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
+    __syncthreads();
+    if (half) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        st_part4(op + nt * 16 + g4 * 4, o[0][nt][0] * inv, o[0][nt][1] * inv,
-                 o[0][nt][2] * inv, o[0][nt][3] * inv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mslot[(nt * 4 + e) * 64 + lane] = o[0][nt][e];
+      mslot[NT * 4 * 64 + lane] = st[0].m;
+      mslot[(NT * 4 + 1) * 64 + lane] = st[0].l;
+    }
+    __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
+    __syncthreads();
+    if (!half && valid) {
+      // the first half always holds a live key, so m0 is finite
+      const float m1 = mslot[NT * 4 * 64 + lane], l1 = mslot[(NT * 4 + 1) * 64 + lane];
+      const float m = fmaxf(st[0].m, m1);
+      const float a0 = fast_exp2(st[0].m - m), a1 = fast_exp2(m1 - m);   // m1 = -inf -> 0
+      const float inv = 1.0f / (st[0].l * a0 + l1 * a1);
+      bf16* op = (bf16*)p.out + (size_t)(nb * p.B + i) * p.ld_out + (size_t)h * DH;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = (o[0][nt][e] * a0 + mslot[(nt * 4 + e) * 64 + lane] * a1) * inv;
+        st_part4(op + nt * 16 + g4 * 4, v[0], v[1], v[2], v[3]);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
