@@ -485,8 +485,37 @@ __global__ void __launch_bounds__(256) qkv_rope_bias_kernel(
 }
 
 // ------------------------------------------------------------------------------------
+// Draft-graph check (debug builds of a call): node 0 is the root (fold_src = -1) and every
+// other node folds onto an earlier one (0 <= fold_src[n] < n), the topological numbering
+// the provenance steps rely on.  One workgroup; out[0] = first offending node or -1,
+// out[1] = its fold_src entry.
+// ------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) check_fold_src_kernel(const int32_t* __restrict__ fs,
+                                                              int N, int32_t* out) {
+  __shared__ int first;
+  if (threadIdx.x == 0) first = 0x7fffffff;
+  __syncthreads();
+  for (int n = threadIdx.x; n < N; n += blockDim.x) {
+    const int v = fs[n];
+    const bool bad = n == 0 ? v != -1 : (v < 0 || v >= n);
+    if (bad) atomicMin(&first, n);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int f = first;
+    out[0] = f == 0x7fffffff ? -1 : f;
+    out[1] = f == 0x7fffffff ? 0 : fs[f];
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Host launchers.
 // ------------------------------------------------------------------------------------
+hipError_t launch_check_fold_src(const int32_t* fold_src, int N, int32_t* out, hipStream_t st) {
+  check_fold_src_kernel<<<1, 256, 0, st>>>(fold_src, N, out);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int d, float tau,
                        float* ratio, uint8_t* recompute, const uint8_t* rec_given,

@@ -47,6 +47,9 @@ hipError_t launch_resolve_pack(const uint8_t* recompute, const int32_t* fold_src
 template <typename T>
 hipError_t launch_combine(const void* h, const void* F, const int32_t* slot_row,
                           const int32_t* count, int cap, int S, int d, void* y, hipStream_t st);
+// Draft-graph check: out[0] = first node n with fold_src[n] outside its range ([0, n), -1
+// for the root) or -1; out[1] = that entry.
+hipError_t launch_check_fold_src(const int32_t* fold_src, int N, int32_t* out, hipStream_t st);
 
 // ---------------------------------------------------------------------------------------
 // GEMM  C[M, N] = A[M, Kd] . W[N, Kd]^T  (both operands K-contiguous), M read on the

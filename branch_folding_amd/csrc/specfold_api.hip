@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -29,6 +30,8 @@ using namespace specfold;
 // compilation from dropping it, since no kernel names it.
 static_assert(SPECFOLD_STATIC_WORKSPACE_BYTES % 256 == 0, "static workspace granularity");
 __device__ __align__(256) __attribute__((used)) char specfold_scratch[SPECFOLD_STATIC_WORKSPACE_BYTES];
+// Result of the draft-graph check (debug mode only): first offending node, its entry.
+__device__ __align__(16) __attribute__((used)) int32_t specfold_debug_result[2];
 
 namespace {
 
@@ -60,6 +63,13 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int elem_bytes(const specfold_shape* s) { return s->dtype == SPECFOLD_BF16 ? 2 : 4; }
 
+// Largest supported model dimensions (well above today's largest open models).
+constexpr int kMaxHidden = 32768;
+constexpr int kMaxFfn = 131072;
+constexpr int kMaxHeads = 256;
+constexpr int kMaxPrefix = 1 << 24;
+constexpr int kMaxVocab = 1 << 24;
+
 specfold_status check_graph_shape(const specfold_shape* s) {
   if (!s) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "shape is NULL");
   if (s->num_nodes < 1 || s->block < 1)
@@ -81,18 +91,31 @@ specfold_status check_shape(const specfold_shape* s, bool layer) {
   if (s->hidden < 128 || s->hidden % 128 != 0)
     return fail(SPECFOLD_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 128",
                 s->hidden);
+  // upper limits keep every size and index the kernels form in 32-bit range
+  if (s->hidden > kMaxHidden)
+    return fail(SPECFOLD_ERR_UNSUPPORTED, "hidden %d > %d is not supported", s->hidden,
+                kMaxHidden);
+  if (!(s->rms_eps >= 0.f) || s->rms_eps == __builtin_inff())
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "rms_eps must be finite and >= 0");
   if (!layer) return SPECFOLD_OK;
   if (s->ffn < 128 || s->ffn % 128 != 0)
     return fail(SPECFOLD_ERR_UNSUPPORTED, "ffn %d must be a positive multiple of 128", s->ffn);
+  if (s->ffn > kMaxFfn)
+    return fail(SPECFOLD_ERR_UNSUPPORTED, "ffn %d > %d is not supported", s->ffn, kMaxFfn);
   if (s->head_dim != 64 && s->head_dim != 128)
     return fail(SPECFOLD_ERR_UNSUPPORTED, "head_dim %d must be 64 or 128", s->head_dim);
   if (s->n_q_heads < 1 || s->n_kv_heads < 1)
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "head counts must be >= 1");
+  if (s->n_q_heads > kMaxHeads)
+    return fail(SPECFOLD_ERR_UNSUPPORTED, "n_q_heads %d > %d is not supported", s->n_q_heads,
+                kMaxHeads);
   if (s->n_q_heads % s->n_kv_heads != 0)
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "n_q_heads %d is not a multiple of n_kv_heads %d",
                 s->n_q_heads, s->n_kv_heads);
   if (s->prefix_len < 0) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "prefix_len < 0");
-  if (!(s->rms_eps >= 0.f)) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "rms_eps must be >= 0");
+  if (s->prefix_len > kMaxPrefix)
+    return fail(SPECFOLD_ERR_UNSUPPORTED, "prefix_len %d > %d is not supported", s->prefix_len,
+                kMaxPrefix);
   if (!(s->rope_theta >= 0.f) || s->rope_theta == __builtin_inff())
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "rope_theta must be finite and >= 0");
   return SPECFOLD_OK;
@@ -469,6 +492,36 @@ specfold_status static_workspace(char** out) {
   return SPECFOLD_OK;
 }
 
+// Optional check of the draft graph before a call's kernels run (SPECFOLD_DEBUG set to
+// anything but "" or "0" in the environment): a one-workgroup kernel looks for a node whose
+// fold_src entry breaks the topological numbering and the call returns
+// SPECFOLD_ERR_INVALID_ARGUMENT naming it.  Without the check, such entries are clamped on
+// the device (wrong results, no out-of-range access).  The check waits for the caller's
+// stream, so a call in debug mode cannot be captured into a graph.
+bool debug_checks() {
+  const char* e = getenv("SPECFOLD_DEBUG");   // read on every call: a process may toggle it
+  return e && *e && strcmp(e, "0") != 0;
+}
+
+std::mutex g_debug_mu;
+
+specfold_status debug_check_fold_src(const int32_t* fold_src, int N, hipStream_t s) {
+  if (!debug_checks() || !fold_src) return SPECFOLD_OK;
+  std::lock_guard<std::mutex> lock(g_debug_mu);
+  (void)hipGetLastError();
+  void* res = nullptr;
+  HIP_CHECK(hipGetSymbolAddress(&res, HIP_SYMBOL(specfold_debug_result)));
+  HIP_CHECK(launch_check_fold_src(fold_src, N, (int32_t*)res, s));
+  int32_t host[2] = {0, 0};
+  HIP_CHECK(hipMemcpyAsync(host, res, sizeof host, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  if (host[0] >= 0)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
+                "fold_src[%d] = %d: the root needs -1 and node n a fold source in [0, n) "
+                "(SPECFOLD_DEBUG check)", host[0], host[1]);
+  return SPECFOLD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -484,6 +537,7 @@ specfold_status specfold_gate(const specfold_shape* shape, const void* hidden,
   hipStream_t s = (hipStream_t)stream;
   const specfold_shape* sh = shape;
   (void)hipGetLastError();   // do not report an earlier, unrelated failure
+  if ((st = debug_check_fold_src(fold_src, sh->num_nodes, s)) != SPECFOLD_OK) return st;
   if (sh->dtype == SPECFOLD_BF16) {
     HIP_CHECK(launch_gate<bf16>(hidden, fold_src, sh->num_nodes, sh->block, sh->hidden, tau,
                                 ratio, recompute, nullptr, nullptr, 0.f, nullptr, 0, s));
@@ -501,6 +555,8 @@ specfold_status specfold_resolve(const specfold_shape* shape, const uint8_t* rec
   if (!recompute || !fold_src || !src_node)
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "recompute, fold_src and src_node are required");
   (void)hipGetLastError();
+  st = debug_check_fold_src(fold_src, shape->num_nodes, (hipStream_t)stream);
+  if (st != SPECFOLD_OK) return st;
   HIP_CHECK(launch_resolve_pack(recompute, fold_src, nullptr, shape->num_nodes, shape->block,
                                 kResolve, src_node, nullptr, nullptr, nullptr, nullptr, 0, 0,
                                 (hipStream_t)stream));
@@ -574,6 +630,8 @@ specfold_status specfold_layer_forward_probed(const specfold_shape* shape,
   if (state_in && (st = check_state_in(state, -1)) != SPECFOLD_OK) return st;
   const Layout L = layout_of(shape);
   if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SPECFOLD_OK) return st;
+  if ((st = debug_check_fold_src(fold_src, shape->num_nodes, (hipStream_t)stream)) != SPECFOLD_OK)
+    return st;
   return launch_layer(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, state,
                       state_in, (char*)workspace, L, (hipStream_t)stream, probe, false, nullptr,
                       nullptr, (flags & SPECFOLD_FLAG_REUSE_ATTENTION) != 0);
@@ -603,6 +661,8 @@ specfold_status specfold_layer_forward_static(const specfold_shape* shape,
                 L.total, (size_t)SPECFOLD_STATIC_WORKSPACE_BYTES);
   char* ws = nullptr;
   if ((st = static_workspace(&ws)) != SPECFOLD_OK) return st;
+  if ((st = debug_check_fold_src(fold_src, shape->num_nodes, (hipStream_t)stream)) != SPECFOLD_OK)
+    return st;
   // nothing in the workspace has to start at zero: every launch writes what a later
   // launch of the same call reads
   return launch_layer(shape, weights, prefix, hidden_in, hidden_out, fold_src, tau, state,
@@ -658,6 +718,8 @@ specfold_status specfold_stack_forward(const specfold_shape* shape, int32_t num_
   // spare hidden buffer, so consecutive layers never alias and the last writes hidden_out
   // With fold states made on the device, layer l's combine also runs layer l+1's gate on the
   // output it writes (same results, one launch and one pass over the hidden states fewer).
+  if ((st = debug_check_fold_src(fold_src, shape->num_nodes, (hipStream_t)stream)) != SPECFOLD_OK)
+    return st;
   const bool fuse = !state_in && combine_gate_fits(shape->hidden, (int)elem_bytes(shape));
   const void* x = hidden_in;
   for (int l = 0; l < num_layers; ++l) {
@@ -676,8 +738,8 @@ specfold_status specfold_stack_forward(const specfold_shape* shape, int32_t num_
 
 size_t specfold_lm_head_workspace_bytes(const specfold_shape* shape, int32_t vocab) {
   if (check_shape(shape, false) != SPECFOLD_OK) return 0;
-  if (vocab < 1) {
-    fail(SPECFOLD_ERR_INVALID_ARGUMENT, "vocab must be >= 1");
+  if (vocab < 1 || vocab > kMaxVocab) {
+    fail(SPECFOLD_ERR_INVALID_ARGUMENT, "vocab must be in [1, %d]", kMaxVocab);
     return 0;
   }
   g_last_error.clear();
@@ -692,7 +754,8 @@ specfold_status specfold_lm_head_argmax(const specfold_shape* shape, int32_t voc
                                         void* workspace, size_t workspace_bytes, void* stream) {
   specfold_status st = check_shape(shape, false);
   if (st != SPECFOLD_OK) return st;
-  if (vocab < 1) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "vocab must be >= 1");
+  if (vocab < 1 || vocab > kMaxVocab)
+    return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "vocab must be in [1, %d]", kMaxVocab);
   if (!rms_final || !w_lm || !hidden || !packed_slot || !slot_row || !packed_count ||
       !row_token || !token)
     return fail(SPECFOLD_ERR_INVALID_ARGUMENT,

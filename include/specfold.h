@@ -36,6 +36,11 @@
  *     unrelated HIP call on the calling thread is cleared on entry, not reported.
  *   - Device-side index inputs (fold_src, masks, provenance, packed rows) are clamped
  *     before use, so malformed values give wrong results but never out-of-bounds access.
+ *     With SPECFOLD_DEBUG set in the environment (to anything but "" or "0"), calls that
+ *     take fold_src first check it on the device (fold_src[0] = -1, 0 <= fold_src[n] < n)
+ *     and fail with SPECFOLD_ERR_INVALID_ARGUMENT naming the first offending node before
+ *     any of their kernels run; that check waits for the stream, so such calls cannot be
+ *     captured into a graph.
  *
  * Layouts (row-major, elements of `dtype` unless noted):
  *   hidden states H      [N, B, d]         N = num_nodes (node 0 = parent/root), B = block
@@ -74,8 +79,9 @@ typedef enum specfold_dtype {
 } specfold_dtype;
 
 /* Shape of one verify layer.  Supported: num_nodes >= 1, 1 <= block <= 1024,
- * num_nodes * block <= 16384, hidden and ffn multiples of 128, head_dim 64 or 128,
- * n_q_heads a multiple of n_kv_heads, prefix_len >= 0, rms_eps >= 0, rope_theta >= 0.
+ * num_nodes * block <= 16384, hidden and ffn multiples of 128 (hidden <= 32768,
+ * ffn <= 131072), head_dim 64 or 128, n_q_heads <= 256 and a multiple of n_kv_heads,
+ * 0 <= prefix_len <= 2^24, rms_eps finite and >= 0, rope_theta finite and >= 0.
  * rope_theta > 0 turns on the rotary position embedding (rotate-half form, as in the
  * Llama / Qwen model families): after the QKV projection, the Q and K heads of the packed
  * row of block position i are rotated at absolute position prefix_len + i, the pair
@@ -335,9 +341,9 @@ size_t specfold_lm_head_workspace_bytes(const specfold_shape* shape, int32_t voc
  *   row_token:   int32 [N*B] capacity, first K written (-1 if a row has no finite logit)
  *   row_logit:   float [N*B] capacity or NULL;  token: int32 [N, B]
  *   workspace:   specfold_lm_head_workspace_bytes(shape, vocab) bytes, 256-byte aligned
- * Errors: SPECFOLD_ERR_INVALID_ARGUMENT for NULL / misaligned pointers or vocab < 1,
- * SPECFOLD_ERR_UNSUPPORTED for unsupported shapes, SPECFOLD_ERR_WORKSPACE for a short
- * workspace, SPECFOLD_ERR_HIP if a launch fails. */
+ * Errors: SPECFOLD_ERR_INVALID_ARGUMENT for NULL / misaligned pointers or vocab outside
+ * [1, 2^24], SPECFOLD_ERR_UNSUPPORTED for unsupported shapes, SPECFOLD_ERR_WORKSPACE for a
+ * short workspace, SPECFOLD_ERR_HIP if a launch fails. */
 specfold_status specfold_lm_head_argmax(const specfold_shape* shape, int32_t vocab,
                                         const void* rms_final, const void* w_lm,
                                         const void* hidden, const int32_t* packed_slot,
