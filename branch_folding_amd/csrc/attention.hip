@@ -153,7 +153,12 @@ __device__ __forceinline__ float4 ld_part4(const bf16* p) {
 // Online-softmax update of one tile of KC x 16 keys (64 by default) for the lane's query:
 // sc[t][r] holds the raw score of key t*16 + (lane/16)*4 + r and becomes its unnormalised
 // weight 2^(score * scale_log2 - m).  Keys >= nkeys (a ragged last tile) get weight 0;
-// nkeys >= 1.  The running output is rescaled only when some lane's running maximum moved.
+// nkeys >= 1.  The reference point m is the running maximum only up to a slack: a lane
+// moves it only when the tile's maximum exceeds it by more than kSoftmaxSlack (log2
+// units), so the weights stay below 2^kSoftmaxSlack, and the running output (m, l and o
+// stay consistent, the normalised result is the same) is rescaled only when some lane
+// moved it -- after the first tiles, rarely.
+constexpr float kSoftmaxSlack = 8.0f;
 template <int NT, int KC = 4>
 __device__ __forceinline__ void softmax_tile(f32x4 (&sc)[KC], int nkeys, float scale_log2,
                                              AttnState& st, f32x4 (&o)[NT]) {
@@ -172,7 +177,8 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&sc)[KC], int nkeys, float s
 #pragma unroll
     for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[t][r]);
   mloc = group4_max(mloc);
-  const float m_new = fmaxf(st.m, mloc * scale_log2);   // scale_log2 > 0
+  const float cand = mloc * scale_log2;                  // scale_log2 > 0
+  const float m_new = cand > st.m + kSoftmaxSlack ? cand : st.m;   // st.m = -inf: cand
   const float alpha = fast_exp2(st.m - m_new);           // st.m = -inf -> 0
   float lsum = 0.f;
 #pragma unroll
@@ -844,22 +850,30 @@ __global__ void __launch_bounds__(256, 2) attn_block_kernel(AttnParams p) {
 // through LDS at the end, and the result is stored as the slot's attention output, with
 // no partials in HBM.
 // ------------------------------------------------------------------------------------
-constexpr int kSlotWaves = 8;
+#ifndef SPECFOLD_SLOT_BLOCKS
+#define SPECFOLD_SLOT_BLOCKS 1
+#endif
+constexpr int kSlotBlocks = SPECFOLD_SLOT_BLOCKS;   // 16-row query blocks per wave
 constexpr int kSlotQRows = 64;
+constexpr int kSlotGroups = kSlotQRows / (16 * kSlotBlocks);   // row groups of a unit
+constexpr int kSlotWaves = 2 * kSlotGroups;                     // a wave pair per group
 static_assert(kSlotQRows == kAttnSlotQRows, "unit size of the per-slot pass");
-static_assert(kSlotQRows == (kSlotWaves / 2) * 16, "a wave pair per 16 query rows");
+static_assert(kSlotBlocks == 1 || kSlotBlocks == 2, "one or two query blocks per wave");
 
 template <int DH>
 __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnParams p) {
   using Tt = TrTile<DH, kSlotWaves>;
   constexpr int QI = Tt::QI, LPI = Tt::LPI, KSQ = Tt::KSQ, NT = Tt::NT;
+  constexpr int NBQ = kSlotBlocks, RG = kSlotGroups;
   constexpr int HALF = kKeys / 2;                  // keys per wave per tile
   __shared__ __attribute__((aligned(1024))) char K0[Tt::TILEB], K1[Tt::TILEB], K2[Tt::TILEB],
       K3[Tt::TILEB];
   __shared__ __attribute__((aligned(1024))) char V0[Tt::TILEB], V1[Tt::TILEB], V2[Tt::TILEB],
       V3[Tt::TILEB];
-  // after a unit's last tile, stage K<rg> holds the second-half state of row group rg
-  static_assert((NT * 4 + 2) * 64 * 4 <= Tt::TILEB, "merge slot of a row group");
+  // after a unit's last tile, stage K<rg*NBQ + b> holds the second-half state of block b of
+  // row group rg
+  static_assert((NT * 4 + 2) * 64 * 4 <= Tt::TILEB, "merge slot of a query block");
+  static_assert(RG * NBQ == 4, "four merge slots");
   const int K = imin(*p.count, p.cap);
   if (K <= 0) return;
   const int g = p.n_q / p.n_kv;
@@ -870,11 +884,14 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
   const int n = pch + ceil_div(p.B, kKeys);       // key tiles per unit
   const int lane = threadIdx.x & 63, g4 = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = wave & 3, half = wave >> 2;      // row group; first or second 32 keys
+  const int rg = wave % RG, half = wave / RG;     // row group; first or second 32 keys
   const char* qkv = (const char*)p.qkv;
   const long ldq = p.ld_qkv * 2, st_tok = p.stride_tok * 2, st_head = p.stride_head * 2;
   auto row_of = [&](int slot) { return imin(imax(p.slot_row[slot], 0), K - 1); };
-  float* mslot = (float*)(rg == 0 ? K0 : rg == 1 ? K1 : rg == 2 ? K2 : K3);
+  auto mslot_of = [&](int b) {
+    const int m = rg * NBQ + b;
+    return (float*)(m == 0 ? K0 : m == 1 ? K1 : m == 2 ? K2 : K3);
+  };
 
   // LDS byte offsets of this lane's fragments (as in the prefix kernel)
   int kofs[KSQ], vofs[NT];
@@ -906,25 +923,33 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int qt = u % qtiles, rest = u / qtiles;
     const int kvh = rest % p.n_kv, nb = rest / p.n_kv;
-    const int r = qt * kSlotQRows + rg * 16 + l16;
-    const bool valid = r < rows;
-    const int rr = valid ? r : rows - 1;
-    const int i = rr / g, h = kvh * g + (rr - (rr / g) * g);
-    uint4 qf[1][KSQ];
-    {
-      const char* qp = qkv + (size_t)row_of(nb * p.B + i) * ldq + (size_t)h * DH * 2;
+    bool valid[NBQ];
+    int qi[NBQ], qh[NBQ];
+    uint4 qf[NBQ][KSQ];
 #pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) qf[0][ks] = ld16(qp + (4 * ks + g4) * 16);
+    for (int b = 0; b < NBQ; ++b) {
+      const int r = qt * kSlotQRows + (rg * NBQ + b) * 16 + l16;
+      valid[b] = r < rows;
+      const int rr = valid[b] ? r : rows - 1;
+      qi[b] = rr / g;
+      qh[b] = kvh * g + (rr - (rr / g) * g);
+      const char* qp = qkv + (size_t)row_of(nb * p.B + qi[b]) * ldq + (size_t)qh[b] * DH * 2;
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) qf[b][ks] = ld16(qp + (4 * ks + g4) * 16);
     }
     // packed rows of the first block tile's keys, read with the queries: looked up inside
     // the ring, the index loads would make the wave wait for every tile in flight
     int brow[QI];
 #pragma unroll
     for (int q = 0; q < QI; ++q) brow[q] = row_of(nb * p.B + imin(lr[q], p.B - 1));
-    AttnState st[1] = {{-__builtin_inff(), 0.f}};
-    f32x4 o[1][NT];
+    AttnState st[NBQ];
+    f32x4 o[NBQ][NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NBQ; ++b) {
+      st[b] = AttnState{-__builtin_inff(), 0.f};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[b][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const char* kpre = (const char*)p.pk + (size_t)kvh * st_head;
     const char* vpre = (const char*)p.pv + (size_t)kvh * st_head;
@@ -977,7 +1002,7 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
                                 : imin(kKeys, p.B - (c - pch) * kKeys);
       const int nk = nkeys - half * HALF;           // this wave's live keys (wave-uniform)
       if (nk > 0)
-        tr_attend<DH, 1, 2>(Kc + hofs, Vc + hofs, nk, qf, kofs, vofs, p.scale_log2, st, o);
+        tr_attend<DH, NBQ, 2>(Kc + hofs, Vc + hofs, nk, qf, kofs, vofs, p.scale_log2, st, o);
       issue(Kn, Vn, c + 3);
     };
     // the previous unit's loads and LDS reads and this unit's query loads are done before
@@ -1000,27 +1025,34 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
     __syncthreads();
     if (half) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int b = 0; b < NBQ; ++b) {
+        float* ms = mslot_of(b);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mslot[(nt * 4 + e) * 64 + lane] = o[0][nt][e];
-      mslot[NT * 4 * 64 + lane] = st[0].m;
-      mslot[(NT * 4 + 1) * 64 + lane] = st[0].l;
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ms[(nt * 4 + e) * 64 + lane] = o[b][nt][e];
+        ms[NT * 4 * 64 + lane] = st[b].m;
+        ms[(NT * 4 + 1) * 64 + lane] = st[b].l;
+      }
     }
     __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
     __syncthreads();
-    if (!half && valid) {
-      // the first half always holds a live key, so m0 is finite
-      const float m1 = mslot[NT * 4 * 64 + lane], l1 = mslot[(NT * 4 + 1) * 64 + lane];
-      const float m = fmaxf(st[0].m, m1);
-      const float a0 = fast_exp2(st[0].m - m), a1 = fast_exp2(m1 - m);   // m1 = -inf -> 0
-      const float inv = 1.0f / (st[0].l * a0 + l1 * a1);
-      bf16* op = (bf16*)p.out + (size_t)(nb * p.B + i) * p.ld_out + (size_t)h * DH;
+#pragma unroll
+    for (int b = 0; b < NBQ; ++b) {
+      if (half || !valid[b]) continue;
+      // the first half always holds a live key, so its maximum is finite
+      const float* ms = mslot_of(b);
+      const float m1 = ms[NT * 4 * 64 + lane], l1 = ms[(NT * 4 + 1) * 64 + lane];
+      const float m = fmaxf(st[b].m, m1);
+      const float a0 = fast_exp2(st[b].m - m), a1 = fast_exp2(m1 - m);   // m1 = -inf -> 0
+      const float inv = 1.0f / (st[b].l * a0 + l1 * a1);
+      bf16* op = (bf16*)p.out + (size_t)(nb * p.B + qi[b]) * p.ld_out + (size_t)qh[b] * DH;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          v[e] = (o[0][nt][e] * a0 + mslot[(nt * 4 + e) * 64 + lane] * a1) * inv;
+          v[e] = (o[b][nt][e] * a0 + ms[(nt * 4 + e) * 64 + lane] * a1) * inv;
         st_part4(op + nt * 16 + g4 * 4, v[0], v[1], v[2], v[3]);
       }
     }
