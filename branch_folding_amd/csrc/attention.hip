@@ -1060,6 +1060,192 @@ __global__ void __launch_bounds__(kSlotWaves * 64, 1) attn_slot_tr_kernel(AttnPa
   __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
 }
 
+// ------------------------------------------------------------------------------------
+// Block phase after a separate prefix phase, bf16: a unit is 128 query rows -- (position,
+// head) pairs of one branch and KV head, 16 per wave -- whose state starts from the prefix
+// partials of each row's packed row (one plane when the split merge ran, else every split's)
+// and then attends the branch's own block keys, gathered from the packed K/V rows through
+// slot_row.  The block tiles arrive by direct-to-LDS loads into a two-stage ring (V read
+// transposed, as in the prefix kernel); at the usual block sizes there is one tile.  The
+// normalised result is the slot's attention output.
+// ------------------------------------------------------------------------------------
+#ifndef SPECFOLD_BLOCK_TR
+#define SPECFOLD_BLOCK_TR 1
+#endif
+constexpr bool kAttnBlockTr = SPECFOLD_BLOCK_TR != 0;
+constexpr int kBlkWaves = 8;
+constexpr int kBlkQRows = kBlkWaves * 16;
+static_assert(kBlkQRows == kAttnBlockQRows, "unit size of the block phase");
+
+template <int DH>
+__global__ void __launch_bounds__(kBlkWaves * 64, 1) attn_block_tr_kernel(AttnParams p) {
+  using Tt = TrTile<DH, kBlkWaves>;
+  constexpr int QI = Tt::QI, LPI = Tt::LPI, KSQ = Tt::KSQ, NT = Tt::NT;
+  __shared__ __attribute__((aligned(1024))) char K0[Tt::TILEB], K1[Tt::TILEB];
+  __shared__ __attribute__((aligned(1024))) char V0[Tt::TILEB], V1[Tt::TILEB];
+  // the plan is loaded with the count (without a prefix there are no partials)
+  const int plan_ns = p.plan[0], plan_merged = p.plan[1];
+  const int K = imin(*p.count, p.cap);
+  if (K <= 0) return;
+  const int ns = p.P <= 0 ? 0 : (plan_merged ? 1 : plan_ns);
+  const int g = p.n_q / p.n_kv;
+  const int rows = p.B * g;
+  const int qtiles = ceil_div(rows, kBlkQRows);
+  const int units = p.N * p.n_kv * qtiles;
+  const int n = ceil_div(p.B, kKeys);             // block tiles per unit
+  const int lane = threadIdx.x & 63, g4 = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* qkv = (const char*)p.qkv;
+  const long ldq = p.ld_qkv * 2;
+  auto row_of = [&](int slot) { return imin(imax(p.slot_row[slot], 0), K - 1); };
+
+  int kofs[KSQ], vofs[NT];
+#pragma unroll
+  for (int ks = 0; ks < KSQ; ++ks)
+    kofs[ks] = l16 * Tt::ROWB + (((4 * ks + g4) ^ tr_kswz<DH>(l16)) << 4);
+  {
+    const int vr = 4 * g4 + (l16 >> 2);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      vofs[nt] = vr * Tt::ROWB + (((2 * nt + ((l16 & 3) >> 1)) ^ tr_vswz<DH>(vr)) << 4) +
+                 8 * (l16 & 1);
+  }
+  int lr[QI];
+  uint32_t lkc[QI], lvc[QI];
+#pragma unroll
+  for (int q = 0; q < QI; ++q) {
+    const int byte = (wave * QI + q) * 1024 + 16 * lane;
+    const int r = byte / Tt::ROWB, pc = (byte % Tt::ROWB) >> 4;
+    lr[q] = r;
+    lkc[q] = (uint32_t)((pc ^ tr_kswz<DH>(r)) << 4);
+    lvc[q] = (uint32_t)((pc ^ tr_vswz<DH>(r)) << 4);
+  }
+  const int wq = wave * QI * 1024;
+
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int qt = u % qtiles, rest = u / qtiles;
+    const int kvh = rest % p.n_kv, nb = rest / p.n_kv;
+    const int r = qt * kBlkQRows + wave * 16 + l16;
+    const bool valid = r < rows;
+    const int rr = valid ? r : rows - 1;
+    const int i = rr / g, h = kvh * g + (rr - (rr / g) * g);
+    const int k = row_of(nb * p.B + i);
+    // packed rows of the first block tile's keys, with the queries and the partials
+    int brow[QI];
+#pragma unroll
+    for (int q = 0; q < QI; ++q) brow[q] = row_of(nb * p.B + imin(lr[q], p.B - 1));
+    uint4 qf[1][KSQ];
+    {
+      const char* qp = qkv + (size_t)k * ldq + (size_t)h * DH * 2;
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) qf[0][ks] = ld16(qp + (4 * ks + g4) * 16);
+    }
+    const char* kblk = qkv + ((size_t)p.n_q + kvh) * DH * 2;
+    const char* vblk = qkv + ((size_t)p.n_q + p.n_kv + kvh) * DH * 2;
+    // Every tile slot issues its loads (past the last tile: packed row 0's line), so the
+    // wait count stays a constant; rows past the block reload its last row.
+    auto issue = [&](char* Kd, char* Vd, int c) {
+      const uint32_t kl = lds_addr(Kd) + wq, vl = lds_addr(Vd) + wq;
+      const char* ks[QI];
+      const char* vs[QI];
+      if (c >= n) {
+#pragma unroll
+        for (int q = 0; q < QI; ++q) ks[q] = kblk, vs[q] = vblk;
+      } else if (c == 0) {
+#pragma unroll
+        for (int q = 0; q < QI; ++q) {
+          ks[q] = kblk + (size_t)brow[q] * ldq + lkc[q];
+          vs[q] = vblk + (size_t)brow[q] * ldq + lvc[q];
+        }
+      } else {
+        const int j0 = c * kKeys;
+#pragma unroll
+        for (int q = 0; q < QI; ++q) {
+          const size_t prow = (size_t)row_of(nb * p.B + imin(j0 + lr[q], p.B - 1));
+          ks[q] = kblk + prow * ldq + lkc[q];
+          vs[q] = vblk + prow * ldq + lvc[q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < QI; ++q) {
+        dma16(ks[q], kl + q * 1024);
+        dma16(vs[q], vl + q * 1024);
+      }
+    };
+    // the previous unit's loads and LDS reads and this unit's query and index loads are
+    // done before the ring is refilled
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+    issue(K0, V0, 0);
+
+    // the state starts from the prefix partials of packed row k (while the tile loads fly)
+    AttnState st[1] = {{-__builtin_inff(), 0.f}};
+    f32x4 o[1][NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ns; s0 += 2) {
+      float ls[2];
+      float4 po[2][NT];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int sb = imin(s0 + b, ns - 1);
+        const size_t prow = ((size_t)sb * K + k) * p.n_q + h;
+        ls[b] = (s0 + b < ns) ? p.part_lse[prow] : -__builtin_inff();
+        const bf16* pp = (const bf16*)p.part_o + prow * DH;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) po[b][nt] = ld_part4(pp + nt * 16 + g4 * 4);
+      }
+      float mb = st[0].m;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) mb = fmaxf(mb, ls[b]);
+      if (mb > -__builtin_inff()) {
+        const float alpha = fast_exp2(st[0].m - mb);   // st.m = -inf -> 0
+        st[0].l *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[0][nt] *= alpha;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const float w = fast_exp2(ls[b] - mb);       // 0 for an empty or absent split
+          st[0].l += w;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            o[0][nt][0] += w * po[b][nt].x;
+            o[0][nt][1] += w * po[b][nt].y;
+            o[0][nt][2] += w * po[b][nt].z;
+            o[0][nt][3] += w * po[b][nt].w;
+          }
+        }
+        st[0].m = mb;
+      }
+    }
+
+    // tile c: landed (c + 1 may be in flight) and every wave past tile c - 1, whose stage
+    // takes the loads of c + 1 after the tile is attended
+    auto body = [&](const char* Kc, const char* Vc, char* Kn, char* Vn, int c) {
+      if (c >= n) return;
+      __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm(0));
+      __builtin_amdgcn_s_barrier();
+      issue(Kn, Vn, c + 1);
+      tr_attend<DH, 1>(Kc, Vc, imin(kKeys, p.B - c * kKeys), qf, kofs, vofs, p.scale_log2, st,
+                       o);
+    };
+    for (int it = 0; it < n; it += 2) {
+      body(K0, V0, K1, V1, it);
+      body(K1, V1, K0, V0, it + 1);
+    }
+    if (valid) {
+      const float inv = 1.0f / st[0].l;
+      bf16* op = (bf16*)p.out + (size_t)(nb * p.B + i) * p.ld_out + (size_t)h * DH;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        st_part4(op + nt * 16 + g4 * 4, o[0][nt][0] * inv, o[0][nt][1] * inv,
+                 o[0][nt][2] * inv, o[0][nt][3] * inv);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(tr_waitcnt_vm_lgkm0(0));
+}
+
 size_t attn_partial_rows(int S, int g, int n_kv, int P, int dh, int elem_bytes) {
   size_t best = 0;
   for (int K = 1; K <= S; ++K) {
@@ -1117,6 +1303,15 @@ hipError_t launch_attn_block(const AttnParams& p, int num_cu, hipStream_t st) {
     const int grid = units < num_cu ? units : num_cu;
     if (p.dh == 128) attn_slot_tr_kernel<128><<<grid, kSlotWaves * 64, 0, st>>>(p);
     else if (p.dh == 64) attn_slot_tr_kernel<64><<<grid, kSlotWaves * 64, 0, st>>>(p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  if (sizeof(T) == 2 && kAttnBlockTr) {
+    // bf16 after a separate prefix phase (or none): 128-query units, direct-to-LDS tiles
+    const int units = p.N * p.n_kv * ceil_div(p.B * g, kBlkQRows);
+    const int grid = units < num_cu ? units : num_cu;
+    if (p.dh == 128) attn_block_tr_kernel<128><<<grid, kBlkWaves * 64, 0, st>>>(p);
+    else if (p.dh == 64) attn_block_tr_kernel<64><<<grid, kBlkWaves * 64, 0, st>>>(p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }

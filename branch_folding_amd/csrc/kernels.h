@@ -235,6 +235,7 @@ constexpr int kAttnMaxSplit = 32;
 // fused pass (1024 units) made the layer 374 -> 404 us.
 constexpr int kAttnFusedMaxPrefix = 512;
 constexpr int kAttnSlotQRows = 64;
+constexpr int kAttnBlockQRows = 128;   // query rows of a block-phase unit (bf16)
 inline bool attn_fused_prefix(int P, int N, int B, int n_q, int n_kv, int num_cu) {
   const long units = (long)N * n_kv * ((B * (n_q / n_kv) + kAttnSlotQRows - 1) / kAttnSlotQRows);
   return P > 0 && P <= kAttnFusedMaxPrefix && units <= num_cu;
