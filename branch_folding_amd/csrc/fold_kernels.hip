@@ -98,7 +98,9 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
                                                    const T* __restrict__ g, float eps,
                                                    T* __restrict__ An, int ld_an) {
   const int lane = threadIdx.x & 63;
-  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the slot is wave-uniform, so its fold source comes through a scalar load, which the
+  // parent row's loads wait for without waiting for the child row's vector loads
+  const int slot = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (slot >= N * B) return;
   const int n = slot / B, i = slot - n * B;
   const bool decide = (ratio != nullptr) || (recompute != nullptr);
@@ -147,7 +149,8 @@ __global__ void __launch_bounds__(256) combine_gate_kernel(
     float* __restrict__ ratio, uint8_t* __restrict__ recompute, const T* __restrict__ g,
     float eps, T* __restrict__ An, int ld_an) {
   const int lane = threadIdx.x & 63;
-  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform slot: the fold source, count and packed-row indices come through scalar loads
+  const int slot = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (slot >= N * B) return;
   const int n = slot / B, i = slot - n * B;
   constexpr int VE = Pack16<T>::kElems;
