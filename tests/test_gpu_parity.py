@@ -62,6 +62,10 @@ EDGE = [
     custom_config(name="edge-star-f32", num_nodes=17, block=16, hidden=256, n_q=4, n_kv=4,
                   head_dim=128, ffn=256, prefix=129, dtype="f32", graph="star",
                   reveal=(1, 1), seed=35),
+    # bf16 without a prefix: the block phase alone, two key tiles (100 keys)
+    custom_config(name="edge-noprefix-bf16", num_nodes=6, block=100, hidden=256, n_q=4, n_kv=2,
+                  head_dim=128, ffn=256, prefix=0, dtype="bf16", graph="tree3",
+                  reveal=(1, 2), seed=39),
 ]
 
 
@@ -92,6 +96,10 @@ MID_PREFIX = [
     custom_config(name="midp-f32", num_nodes=6, block=18, hidden=128, n_q=6, n_kv=2,
                   head_dim=64, ffn=256, prefix=1500, dtype="f32", graph="dag",
                   reveal=(1, 2), seed=95),
+    # bf16 block phase after a prefix phase with three key tiles (130 keys, ragged), dh 64
+    custom_config(name="midp-longblock-bf16", num_nodes=5, block=130, hidden=256, n_q=4,
+                  n_kv=1, head_dim=64, ffn=256, prefix=600, dtype="bf16", graph="chain",
+                  reveal=(1, 2), seed=96),
 ]
 
 
