@@ -29,8 +29,10 @@
  *     enqueued; device faults surface at the caller's next synchronisation.
  *   - Integer results (masks, provenance, packing) are exact; floating-point results are
  *     deterministic (bit-identical between runs, no floating-point atomics).
- *   - There is no global mutable state: calls on different streams are safe when they
- *     use different output and workspace buffers.
+ *   - Calls on different streams are safe when they use different output and workspace
+ *     buffers.  The only global device state is the array behind
+ *     specfold_layer_forward_static (its calls on one device share it) and the result slot
+ *     of the SPECFOLD_DEBUG graph check (whose use is serialised on the host).
  *   - On failure a status other than SPECFOLD_OK is returned and specfold_last_error()
  *     returns a message (per host thread).  A HIP error left pending by an earlier,
  *     unrelated HIP call on the calling thread is cleared on entry, not reported.
