@@ -404,28 +404,6 @@ __device__ __forceinline__ int tr_vswz(int r) {
   return 2 * ((r / TrTile<DH>::RP) & (8 / TrTile<DH>::RP - 1));
 }
 
-// Direct-to-LDS 16-byte load (global_load_lds_dwordx4: lane i writes LDS bytes
-// [lds_base + 16 i, lds_base + 16 i + 16); lds_base must be wave-uniform).  Issued from
-// inline asm so that the compiler's wait-count pass does not see an LDS write: the
-// transposed V reads below carry no alias information, and against a tracked LDS DMA the
-// pass would drain every load in flight before each of them.  The kernel orders these
-// loads itself (s_waitcnt vmcnt + s_barrier before a stage is read); M0 is restored.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %[sv], m0\n\t"
-      "s_mov_b32 m0, %[b]\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %[g], off\n\t"
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : [g] "v"(g), [b] "s"(lds_base)
-      : "memory");
-}
-
 typedef short tr_v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) tr_v4s lds_tr_v4s;
 

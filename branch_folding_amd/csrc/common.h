@@ -127,6 +127,29 @@ __device__ __forceinline__ f32x4 mma_kstep(const uint4& a, const uint4& b, f32x4
   return c;
 }
 
+// Direct-to-LDS 16-byte load (global_load_lds_dwordx4: lane i writes LDS bytes
+// [lds_base + 16 i, lds_base + 16 i + 16); lds_base must be wave-uniform).  Issued from
+// inline asm so that the compiler's wait-count pass does not see an LDS write: reads it
+// cannot tell apart from the stage being filled (the attention's transposed V reads carry no
+// alias information), or loads issued by only some of a workgroup's waves, would make it
+// drain every load in flight before each LDS read.  A kernel using it orders these loads
+// itself (s_waitcnt vmcnt + s_barrier before a stage is read); M0 is restored.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[b]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[g], off\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [g] "v"(g), [b] "s"(lds_base)
+      : "memory");
+}
+
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -348,6 +348,8 @@ __global__ void __launch_bounds__(256 * BN / 64) gemm_auto_kernel(GemmParams p) 
 // load count (and with it the s_waitcnt immediate) is a compile-time constant.
 // ---------------------------------------------------------------------------------------
 constexpr int kSlabMaxPairs = 5;
+// calls of this many slots or more can reach the tiled SwiGLU path (see swiglu_auto_kernel)
+constexpr int kSwigluTallAutoFrom = 769;
 constexpr int kSlabThreads = 256;
 
 // One slab unit over R row tiles (R = 1 or 2) of 128 rows starting at m0.  With R = 2 each
@@ -535,6 +537,178 @@ __device__ __forceinline__ void slab_units(const GemmParams& p, int M, int slabs
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// SwiGLU slabs on eight waves, for calls of fewer than kSwigluTallAutoFrom slots (the row
+// count cannot reach the tiled path, which the host knows from the slot count).  A pass
+// covers 128 rows (R = 1, 16 per wave) or 256 (R = 2, 32 per wave), every wave on every
+// block of the slab; waves 0-3 also load the weight chunk.  Two waves per SIMD keep more
+// loads in flight per CU than the four-wave slab: 7B layer gate/up 65.1-65.2 -> 62.6-63.4
+// us (probes, same box).  The loads are the untracked dma16: only some waves load weights,
+// and with the tracked builtin the compiler drained the ring before every LDS read.
+// ---------------------------------------------------------------------------------------
+constexpr int kSlab8Threads = 512;
+
+template <typename T, int P, int R>
+__device__ __forceinline__ void slab8_unit(const GemmParams& p, int M, int m0, int pair0,
+                                           char* As0, char* As1, char* As2, char* Bs0,
+                                           char* Bs1, char* Bs2, char* Ws0, char* Ws1,
+                                           char* Ws2) {
+  using G = GemmTile<T>;
+  static_assert(R == 1 || R == 2, "one or two row tiles per pass");
+  constexpr int NB = 2 * P;                               // gate_0, up_0, gate_1, ...
+  constexpr int AQ = kGemmBM * kGemmBKBytes / 1024 / 8;   // A loads per wave per row tile
+  constexpr int WQ = NB * 16 * kGemmBKBytes / 1024 / 4;   // W loads of each of waves 0-3
+  constexpr int LA = R * AQ, LW = LA + WQ;                // loads per k-iteration (4-7, 0-3)
+  const int kiters = p.Kd / G::BK;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool wl = wave < 4;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int lr = lane >> 3, lpc = lane & 7;
+  // this wave's rows: R = 1, rows 16w.. of the tile; R = 2, rows 32(w%4).. of tile w/4
+  const int tile = R == 2 ? wave >> 2 : 0;
+  const int lb = R == 2 ? (wave & 3) * 32 : wave * 16;
+  const char* Ab = (const char*)p.A;
+  const char* Wb = (const char*)p.W;
+
+  const char* a_src[R][AQ];
+  const char* w_src[WQ];
+#pragma unroll
+  for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int r = (wave * AQ + q) * 8 + lr;
+      const int c = lpc ^ ((r >> 1) & 7);
+      a_src[rt][q] = Ab + (size_t)imin(m0 + rt * kGemmBM + r, M - 1) * p.lda * sizeof(T) + c * 16;
+    }
+  const int ww = wl ? wave : 0;
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) {
+    const int r = (ww * WQ + q) * 8 + lr;               // stage row: block r/16, row r%16
+    const int c = lpc ^ ((r >> 1) & 7);
+    const int b = r >> 4;
+    const int j = (pair0 + (b >> 1)) * 16 + (r & 15);
+    const int wr = (b & 1) ? p.ff + j : j;
+    w_src[q] = Wb + (size_t)wr * p.ldw * sizeof(T) + c * 16;
+  }
+  // loads of k-iteration `it` into a stage: the weight chunk (waves 0-3) and the A tile(s)
+  auto issue = [&](char* a0, char* a1, char* ws, int it) {
+    const size_t off = (size_t)imin(it, kiters - 1) * kGemmBKBytes;
+    if (wl) {
+#pragma unroll
+      for (int q = 0; q < WQ; ++q) dma16(w_src[q] + off, lds_addr(ws) + (wave * WQ + q) * 1024);
+    }
+#pragma unroll
+    for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+      for (int q = 0; q < AQ; ++q)
+        dma16(a_src[rt][q] + off, lds_addr(rt == 0 ? a0 : a1) + (wave * AQ + q) * 1024);
+  };
+
+  f32x4 acc[R][NB];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool live = (m0 + tile * kGemmBM + lb) < M;
+  auto compute = [&](const char* a0, const char* a1, const char* ws) {
+    if (!live) return;
+    constexpr int KS = kGemmBKBytes / 64;
+    const char* as = tile == 0 ? a0 : a1;
+    uint4 af[KS][R], bfr[KS][NB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks * 4 + g4;
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        af[ks][i] = *reinterpret_cast<const uint4*>(as + swz(lb + i * 16 + l16, c));
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        bfr[ks][j] = *reinterpret_cast<const uint4*>(ws + swz(j * 16 + l16, c));
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep every read ahead of the MFMAs
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i][j] = mma_kstep(af[ks][i], bfr[ks][j], acc[i][j], T());
+  };
+  // three stages, two k-iterations in flight: once this wave's loads of i have landed (its
+  // loads of i + 1 may still be pending) and every wave has passed the barrier, stage i is
+  // read and the loads of i + 2 go into the stage i - 1 left
+  auto body = [&](char* a0, char* a1, char* ws, char* n0, char* n1, char* nw, int i) {
+    if (wl) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LW));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(LA));
+    __builtin_amdgcn_s_barrier();
+    if (i < kiters) compute(a0, a1, ws);
+    issue(n0, n1, nw, i + 2);
+  };
+  // every wave is done with the previous unit's stages and its loads have landed
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_barrier();
+  issue(As0, Bs0, Ws0, 0);
+  issue(As1, Bs1, Ws1, 1);
+  for (int it = 0; it < kiters; it += kGemmStages) {
+    body(As0, Bs0, Ws0, As2, Bs2, Ws2, it);
+    body(As1, Bs1, Ws1, As0, Bs0, Ws0, it + 1);
+    body(As2, Bs2, Ws2, As1, Bs1, Ws1, it + 2);
+  }
+
+  // epilogue: lane holds rows g4*4 + r of each 16-row block and column l16 of each block
+  T* C = (T*)p.C;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int pr = 0; pr < P; ++pr) {
+      const int col = (pair0 + pr) * 16 + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + tile * kGemmBM + lb + i * 16 + g4 * 4 + r;
+        if (row < M) {
+          const float gv = acc[i][2 * pr][r], uv = acc[i][2 * pr + 1][r];
+          C[(size_t)row * p.ldc + col] = from_f32<T>(silu_f(gv) * uv);
+        }
+      }
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kSlab8Threads) swiglu_slab8_kernel(GemmParams p, int slabs) {
+  constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
+  constexpr int W_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
+  // three stages of {A tile 0, A tile 1, W}: 3 x (16 + 16 + 20) KB = 156 KB
+  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Bs0[A_BYTES], Bs1[A_BYTES], Bs2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
+  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
+  if (M <= 0) return;
+  const int pairs = p.ff / 16;
+  const int base = pairs / slabs, rem = pairs - base * slabs;
+  const int mb = ceil_div(M, kGemmBM);
+  const int R = mb > 1 ? 2 : 1;                 // pairs of row tiles share every weight chunk
+  const int groups = ceil_div(mb, R);
+  for (int u = blockIdx.x; u < groups * slabs; u += gridDim.x) {
+    const int mg = u / slabs, sl = u - mg * slabs;
+    const int np = base + (sl < rem ? 1 : 0);
+    const int pair0 = sl * base + imin(sl, rem);
+    const int m0 = mg * R * kGemmBM;
+#define SLAB8_CASE(PP)                                                                      \
+  case PP:                                                                                  \
+    if (R == 1) slab8_unit<T, PP, 1>(p, M, m0, pair0, As0, As1, As2, Bs0, Bs1, Bs2, Ws0,    \
+                                     Ws1, Ws2);                                             \
+    else slab8_unit<T, PP, 2>(p, M, m0, pair0, As0, As1, As2, Bs0, Bs1, Bs2, Ws0, Ws1, Ws2); \
+    break;
+    switch (np) {
+      SLAB8_CASE(1) SLAB8_CASE(2) SLAB8_CASE(3) SLAB8_CASE(4) SLAB8_CASE(5)
+      default: break;          // the host never makes slabs wider than kSlabMaxPairs
+    }
+#undef SLAB8_CASE
+  }
+  // no wave may end while its last (clamped) stage loads are still writing LDS
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
 template <typename T>
 __global__ void __launch_bounds__(kSlabThreads) swiglu_slab_kernel(GemmParams p, int slabs) {
   constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
@@ -557,7 +731,6 @@ __global__ void __launch_bounds__(kSlabThreads) swiglu_slab_kernel(GemmParams p,
 // Four waves, one per SIMD: the slab body needs more registers than two waves per SIMD
 // leave.  Each stage is one X array (the slabs' two 128-row A tiles, or the 256-row A tile)
 // and one Y array (the slab's weight chunk, or the 128-row W tile): 3 x (32 + 20) KB.
-constexpr int kSwigluTallAutoFrom = 769;
 template <typename T>
 __global__ void __launch_bounds__(kSlabThreads) swiglu_auto_kernel(GemmParams p, int slabs) {
   constexpr int X_BYTES = 2 * kGemmBM * kGemmBKBytes;
@@ -682,6 +855,13 @@ static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st
 
 template <typename T, int EPI>
 static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t st) {
+  if (EPI == kEpiSwiGLU && p.m_cap < kSwigluTallAutoFrom &&
+      (p.bm == kGemmTileAuto || gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 128)) {
+    // too few slots for the tiled path: the eight-wave slabs, whatever the row count
+    const int slabs = swiglu_slabs(p.ff, num_cu);
+    swiglu_slab8_kernel<T><<<slabs, kSlab8Threads, 0, st>>>(p, slabs);
+    return hipGetLastError();
+  }
   if (EPI == kEpiSwiGLU && p.bm == kGemmTileAuto) {
     // slabs below kGemmTallAutoFrom rows, unsplit 256-row tiles above: no reduction pass
     const int slabs = swiglu_slabs(p.ff, num_cu);
