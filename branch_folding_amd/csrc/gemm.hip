@@ -546,6 +546,9 @@ __device__ __forceinline__ void slab_units(const GemmParams& p, int M, int slabs
 // us (probes, same box).  The loads are the untracked dma16: only some waves load weights,
 // and with the tracked builtin the compiler drained the ring before every LDS read.
 // ---------------------------------------------------------------------------------------
+#ifndef SPECFOLD_AUTO8
+#define SPECFOLD_AUTO8 1
+#endif
 constexpr int kSlab8Threads = 512;
 
 template <typename T, int P, int R>
@@ -673,16 +676,12 @@ __device__ __forceinline__ void slab8_unit(const GemmParams& p, int M, int m0, i
     }
 }
 
+// Every eight-wave slab unit of one SwiGLU call (rows M read on the device), walked
+// persistently.  Stage s holds {As_s, Bs_s, Ws_s}.
 template <typename T>
-__global__ void __launch_bounds__(kSlab8Threads) swiglu_slab8_kernel(GemmParams p, int slabs) {
-  constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
-  constexpr int W_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
-  // three stages of {A tile 0, A tile 1, W}: 3 x (16 + 16 + 20) KB = 156 KB
-  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Bs0[A_BYTES], Bs1[A_BYTES], Bs2[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
-  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
-  if (M <= 0) return;
+__device__ __forceinline__ void slab8_units(const GemmParams& p, int M, int slabs, char* As0,
+                                            char* As1, char* As2, char* Bs0, char* Bs1,
+                                            char* Bs2, char* Ws0, char* Ws1, char* Ws2) {
   const int pairs = p.ff / 16;
   const int base = pairs / slabs, rem = pairs - base * slabs;
   const int mb = ceil_div(M, kGemmBM);
@@ -705,6 +704,19 @@ __global__ void __launch_bounds__(kSlab8Threads) swiglu_slab8_kernel(GemmParams 
     }
 #undef SLAB8_CASE
   }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kSlab8Threads) swiglu_slab8_kernel(GemmParams p, int slabs) {
+  constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
+  constexpr int W_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
+  // three stages of {A tile 0, A tile 1, W}: 3 x (16 + 16 + 20) KB = 156 KB
+  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Bs0[A_BYTES], Bs1[A_BYTES], Bs2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
+  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
+  if (M <= 0) return;
+  slab8_units<T>(p, M, slabs, As0, As1, As2, Bs0, Bs1, Bs2, Ws0, Ws1, Ws2);
   // no wave may end while its last (clamped) stage loads are still writing LDS
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
@@ -745,6 +757,28 @@ __global__ void __launch_bounds__(kSlabThreads) swiglu_auto_kernel(GemmParams p,
     gemm_units<T, kEpiSwiGLU, 128, 256, false, 128, 64>(p, M, X0, X1, X2, Y0, Y1, Y2);
   else
     slab_units<T>(p, M, slabs, X0, X1, X2, X0 + H, X1 + H, X2 + H, Y0, Y1, Y2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+// The device-chosen SwiGLU on eight waves: below kSwigluTallAutoFrom packed rows the
+// eight-wave slabs, from there on 256 x 128 tiles of the split-K GEMM body with eight 64 x 64
+// wave tiles and no split.  Each stage is one X array (the slabs' two 128-row A tiles, or the
+// 256-row A tile) and one Y array (the slab's weight chunk, or the 128-row W tile).  The slab
+// path's loads are untracked, so its two A tiles may share an array.
+template <typename T>
+__global__ void __launch_bounds__(kSlab8Threads) swiglu_auto8_kernel(GemmParams p, int slabs) {
+  constexpr int X_BYTES = 2 * kGemmBM * kGemmBKBytes;
+  constexpr int Y_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
+  static_assert(X_BYTES >= 256 * kGemmBKBytes && Y_BYTES >= 128 * kGemmBKBytes, "stage sizes");
+  __shared__ __attribute__((aligned(1024))) char X0[X_BYTES], X1[X_BYTES], X2[X_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Y0[Y_BYTES], Y1[Y_BYTES], Y2[Y_BYTES];
+  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
+  if (M <= 0) return;
+  constexpr int H = kGemmBM * kGemmBKBytes;
+  if (M >= kSwigluTallAutoFrom)
+    gemm_units<T, kEpiSwiGLU, 128, 256, false>(p, M, X0, X1, X2, Y0, Y1, Y2);
+  else
+    slab8_units<T>(p, M, slabs, X0, X1, X2, X0 + H, X1 + H, X2 + H, Y0, Y1, Y2);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
@@ -865,7 +899,11 @@ static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t s
   if (EPI == kEpiSwiGLU && p.bm == kGemmTileAuto) {
     // slabs below kGemmTallAutoFrom rows, unsplit 256-row tiles above: no reduction pass
     const int slabs = swiglu_slabs(p.ff, num_cu);
+#if SPECFOLD_AUTO8
+    swiglu_auto8_kernel<T><<<num_cu, kSlab8Threads, 0, st>>>(p, slabs);
+#else
     swiglu_auto_kernel<T><<<num_cu, kSlabThreads, 0, st>>>(p, slabs);
+#endif
     return hipGetLastError();
   }
   if (EPI == kEpiSwiGLU && gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 128) {
