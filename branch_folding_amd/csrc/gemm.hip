@@ -342,213 +342,19 @@ __global__ void __launch_bounds__(256 * BN / 64) gemm_auto_kernel(GemmParams p) 
 // dealt out in contiguous ranges of P or P+1 pairs, one unit per CU, so every CU streams an
 // equal share of the weights with no split-K partials: a fixed 256-column tiling leaves
 // ~40% of the CUs idle at the 7B shape, and one CU cannot pull much more than ~30 GB/s
-// from HBM on its own.  A unit has 4 waves; each covers 32 rows and every block of the
-// slab, so both halves of an output element land in the same lane.  The main loop is the
-// same direct-to-LDS three-stage ring as gemm_kernel, templated on P so that the per-wave
-// load count (and with it the s_waitcnt immediate) is a compile-time constant.
+// from HBM on its own.  A unit has eight waves, two per SIMD; a pass covers 128 rows (R = 1,
+// 16 per wave) or 256 (R = 2, 32 per wave), every wave on every block of the slab, so both
+// halves of an output element land in the same lane, and waves 0-3 also load the weight
+// chunk.  The main loop is a direct-to-LDS three-stage ring like gemm_kernel's, templated on
+// P so that the per-wave load counts (and with them the s_waitcnt immediates) are
+// compile-time constants.  Eight waves keep more loads in flight per CU than the earlier
+// four (one per SIMD, 32 rows each): 7B layer gate/up 65.5-66.0 -> 63.9-64.4 us (probes,
+// same box).  The loads are the untracked dma16: only some waves load weights, and with the
+// tracked builtin the compiler drained the ring before every LDS read.
 // ---------------------------------------------------------------------------------------
 constexpr int kSlabMaxPairs = 5;
-// calls of this many slots or more can reach the tiled SwiGLU path (see swiglu_auto_kernel)
+// calls of this many slots or more can reach the tiled SwiGLU path (swiglu_auto8_kernel)
 constexpr int kSwigluTallAutoFrom = 769;
-constexpr int kSlabThreads = 256;
-
-// One slab unit over R row tiles (R = 1 or 2) of 128 rows starting at m0.  With R = 2 each
-// weight chunk is loaded once for both row tiles (the slab is streamed once for up to 256
-// packed rows); stage s then holds {As_s, Bs_s, Ws_s} instead of {As_s, Ws_s}.
-template <typename T, int P, int R>
-__device__ __forceinline__ void slab_unit(const GemmParams& p, int M, int m0, int pair0,
-                                          char* As0, char* As1, char* As2, char* Bs0,
-                                          char* Bs1, char* Bs2, char* Ws0, char* Ws1,
-                                          char* Ws2) {
-  using G = GemmTile<T>;
-  static_assert(R == 1 || R == 2, "one or two row tiles per pass");
-  constexpr int NB = 2 * P;                  // 16-column blocks: gate_0, up_0, gate_1, ...
-  constexpr int AQ = kGemmBM * kGemmBKBytes / 1024 / 4;   // A loads per wave per row tile (4)
-  constexpr int WQ = NB * 16 * kGemmBKBytes / 1024 / 4;   // W loads per wave (P)
-  constexpr int LPI = R * AQ + WQ;
-  const int kiters = p.Kd / G::BK;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // the slab's four waves; a wider launch's other waves take part in the barriers only
-  const bool active = wave < 4;
-  const int g4 = lane >> 4, l16 = lane & 15;
-  const int lr = lane >> 3, lpc = lane & 7;
-  const char* Ab = (const char*)p.A;
-  const char* Wb = (const char*)p.W;
-
-  const char* a_src[R][AQ];
-  const char* w_src[WQ];
-#pragma unroll
-  for (int rt = 0; rt < R; ++rt)
-#pragma unroll
-    for (int q = 0; q < AQ; ++q) {
-      const int r = (wave * AQ + q) * 8 + lr;
-      const int c = lpc ^ ((r >> 1) & 7);
-      a_src[rt][q] = Ab + (size_t)imin(m0 + rt * kGemmBM + r, M - 1) * p.lda * sizeof(T) + c * 16;
-    }
-#pragma unroll
-  for (int q = 0; q < WQ; ++q) {
-    const int r = (wave * WQ + q) * 8 + lr;           // stage row: block r/16, row r%16
-    const int c = lpc ^ ((r >> 1) & 7);
-    const int b = r >> 4;
-    const int j = (pair0 + (b >> 1)) * 16 + (r & 15);
-    const int wr = (b & 1) ? p.ff + j : j;
-    w_src[q] = Wb + (size_t)wr * p.ldw * sizeof(T) + c * 16;
-  }
-  // loads of k-iteration `it` into a stage: the weight chunk, and the A tile(s)
-  auto issue_w = [&](char* ws, int it) {
-    if (!active) return;
-    const size_t off = (size_t)imin(it, kiters - 1) * kGemmBKBytes;
-#pragma unroll
-    for (int q = 0; q < WQ; ++q)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(w_src[q] + off),
-                                       (lds_void_t*)(ws + (wave * WQ + q) * 1024), 16, 0, 0);
-  };
-  auto issue_a = [&](char* a0, char* a1, int it) {
-    if (!active) return;
-    const size_t off = (size_t)imin(it, kiters - 1) * kGemmBKBytes;
-#pragma unroll
-    for (int rt = 0; rt < R; ++rt) {
-      char* as = rt == 0 ? a0 : a1;
-#pragma unroll
-      for (int q = 0; q < AQ; ++q)
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[rt][q] + off),
-                                         (lds_void_t*)(as + (wave * AQ + q) * 1024), 16, 0, 0);
-    }
-  };
-
-  f32x4 acc[R][2][NB];
-#pragma unroll
-  for (int rt = 0; rt < R; ++rt)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[rt][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool live[R];
-#pragma unroll
-  for (int rt = 0; rt < R; ++rt) live[rt] = active && (m0 + rt * kGemmBM + wave * 32) < M;
-  // One wave per SIMD, so LDS latency is hidden inside the wave: all operand fragments of
-  // a k-iteration are read at once, then its MFMAs run (the weight fragments serve every
-  // row tile).
-  auto compute = [&](const char* a0, const char* a1, const char* ws) {
-    if (!live[0]) return;
-    constexpr int KS = kGemmBKBytes / 64;
-    uint4 af[R][KS][2], bfr[KS][NB];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int c = ks * 4 + g4;
-#pragma unroll
-      for (int rt = 0; rt < R; ++rt)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[rt][ks][i] = *reinterpret_cast<const uint4*>((rt == 0 ? a0 : a1) +
-                                                          swz(wave * 32 + i * 16 + l16, c));
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        bfr[ks][j] = *reinterpret_cast<const uint4*>(ws + swz(j * 16 + l16, c));
-    }
-    __builtin_amdgcn_sched_barrier(0);   // keep every read ahead of the MFMAs
-#pragma unroll
-    for (int rt = 0; rt < R; ++rt) {
-      if (rt > 0 && !live[rt]) break;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            acc[rt][i][j] = mma_kstep(af[rt][ks][i], bfr[ks][j], acc[rt][i][j], T());
-    }
-  };
-
-  // three stages, two k-iterations in flight: once this wave's loads of i have landed
-  // (only the LPI loads of i + 1 may still be pending) and every wave has passed the
-  // barrier, the loads of i + 2 go into the stage freed by i - 1.  The weight chunk (HBM,
-  // long latency) is issued before the MFMAs of i, the A tiles (L2 hits) after them: a CU
-  // keeps only so many loads outstanding, and with a full stage in flight the issue of the
-  // whole next stage would stall the wave before its MFMAs (18% of the time at 129..256
-  // rows).
-  auto body = [&](char* a0, char* a1, char* ws, char* n0, char* n1, char* nw, int i) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPI));
-    __builtin_amdgcn_s_barrier();
-    issue_w(nw, i + 2);
-    if (i < kiters) compute(a0, a1, ws);
-    issue_a(n0, n1, i + 2);
-  };
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  __builtin_amdgcn_s_barrier();
-  issue_w(Ws0, 0);
-  issue_a(As0, Bs0, 0);
-  issue_w(Ws1, 1);
-  issue_a(As1, Bs1, 1);
-  for (int it = 0; it < kiters; it += kGemmStages) {
-    body(As0, Bs0, Ws0, As2, Bs2, Ws2, it);
-    body(As1, Bs1, Ws1, As0, Bs0, Ws0, it + 1);
-    body(As2, Bs2, Ws2, As1, Bs1, Ws1, it + 2);
-  }
-
-  // epilogue: lane holds rows g4*4 + r of each 16-row block and column l16 of each block
-  if (!active) return;
-  T* C = (T*)p.C;
-#pragma unroll
-  for (int rt = 0; rt < R; ++rt)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int pr = 0; pr < P; ++pr) {
-        const int col = (pair0 + pr) * 16 + l16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = m0 + rt * kGemmBM + wave * 32 + i * 16 + g4 * 4 + r;
-          if (row < M) {
-            const float gv = acc[rt][i][2 * pr][r], uv = acc[rt][i][2 * pr + 1][r];
-            C[(size_t)row * p.ldc + col] = from_f32<T>(silu_f(gv) * uv);
-          }
-        }
-      }
-}
-
-// Every slab unit of one SwiGLU call (rows M read on the device), walked persistently.
-template <typename T>
-__device__ __forceinline__ void slab_units(const GemmParams& p, int M, int slabs, char* As0,
-                                           char* As1, char* As2, char* Bs0, char* Bs1,
-                                           char* Bs2, char* Ws0, char* Ws1, char* Ws2) {
-  const int pairs = p.ff / 16;
-  const int base = pairs / slabs, rem = pairs - base * slabs;
-  const int mb = ceil_div(M, kGemmBM);
-  // more than one row tile: pairs of row tiles share every weight chunk
-  const int R = mb > 1 ? 2 : 1;
-  const int groups = ceil_div(mb, R);
-  for (int u = blockIdx.x; u < groups * slabs; u += gridDim.x) {
-    const int mg = u / slabs, sl = u - mg * slabs;
-    const int np = base + (sl < rem ? 1 : 0);
-    const int pair0 = sl * base + imin(sl, rem);
-    const int m0 = mg * R * kGemmBM;
-#define SLAB_CASE(PP)                                                                        \
-  case PP:                                                                                   \
-    if (R == 1) slab_unit<T, PP, 1>(p, M, m0, pair0, As0, As1, As2, Bs0, Bs1, Bs2, Ws0, Ws1,  \
-                                    Ws2);                                                    \
-    else slab_unit<T, PP, 2>(p, M, m0, pair0, As0, As1, As2, Bs0, Bs1, Bs2, Ws0, Ws1, Ws2);  \
-    break;
-    switch (np) {
-      SLAB_CASE(1) SLAB_CASE(2) SLAB_CASE(3) SLAB_CASE(4) SLAB_CASE(5)
-      default: break;          // the host never makes slabs wider than kSlabMaxPairs
-    }
-#undef SLAB_CASE
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-// SwiGLU slabs on eight waves, for calls of fewer than kSwigluTallAutoFrom slots (the row
-// count cannot reach the tiled path, which the host knows from the slot count).  A pass
-// covers 128 rows (R = 1, 16 per wave) or 256 (R = 2, 32 per wave), every wave on every
-// block of the slab; waves 0-3 also load the weight chunk.  Two waves per SIMD keep more
-// loads in flight per CU than the four-wave slab: 7B layer gate/up 65.1-65.2 -> 62.6-63.4
-// us (probes, same box).  The loads are the untracked dma16: only some waves load weights,
-// and with the tracked builtin the compiler drained the ring before every LDS read.
-// ---------------------------------------------------------------------------------------
-#ifndef SPECFOLD_AUTO8
-#define SPECFOLD_AUTO8 1
-#endif
 constexpr int kSlab8Threads = 512;
 
 template <typename T, int P, int R>
@@ -721,45 +527,6 @@ __global__ void __launch_bounds__(kSlab8Threads) swiglu_slab8_kernel(GemmParams 
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
-template <typename T>
-__global__ void __launch_bounds__(kSlabThreads) swiglu_slab_kernel(GemmParams p, int slabs) {
-  constexpr int A_BYTES = kGemmBM * kGemmBKBytes;
-  constexpr int W_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
-  // three stages of {A tile 0, A tile 1, W}: 3 x (16 + 16 + 20) KB = 156 KB
-  __shared__ __attribute__((aligned(1024))) char As0[A_BYTES], As1[A_BYTES], As2[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Bs0[A_BYTES], Bs1[A_BYTES], Bs2[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
-  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
-  if (M <= 0) return;
-  slab_units<T>(p, M, slabs, As0, As1, As2, Bs0, Bs1, Bs2, Ws0, Ws1, Ws2);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-}
-
-// SwiGLU gate/up with the row tile chosen on the device: up to 768 packed rows (three row
-// groups of the slabs, each streaming the weights once more) the column slabs, from there on
-// 256 x 128 tiles of the split-K GEMM body, each of the four waves on 128 x 64, with no
-// split (its SwiGLU epilogue needs whole sums).  3B layer, gate/up: 588 rows 91.5 us on
-// the slabs, 101.8 us on the tiles; 1024 rows 133.7 us on the slabs, 105.8 us on the tiles.
-// Four waves, one per SIMD: the slab body needs more registers than two waves per SIMD
-// leave.  Each stage is one X array (the slabs' two 128-row A tiles, or the 256-row A tile)
-// and one Y array (the slab's weight chunk, or the 128-row W tile): 3 x (32 + 20) KB.
-template <typename T>
-__global__ void __launch_bounds__(kSlabThreads) swiglu_auto_kernel(GemmParams p, int slabs) {
-  constexpr int X_BYTES = 2 * kGemmBM * kGemmBKBytes;
-  constexpr int Y_BYTES = 2 * kSlabMaxPairs * 16 * kGemmBKBytes;
-  static_assert(X_BYTES >= 256 * kGemmBKBytes && Y_BYTES >= 128 * kGemmBKBytes, "stage sizes");
-  __shared__ __attribute__((aligned(1024))) char X0[X_BYTES], X1[X_BYTES], X2[X_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Y0[Y_BYTES], Y1[Y_BYTES], Y2[Y_BYTES];
-  const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
-  if (M <= 0) return;
-  constexpr int H = kGemmBM * kGemmBKBytes;
-  if (M >= kSwigluTallAutoFrom)
-    gemm_units<T, kEpiSwiGLU, 128, 256, false, 128, 64>(p, M, X0, X1, X2, Y0, Y1, Y2);
-  else
-    slab_units<T>(p, M, slabs, X0, X1, X2, X0 + H, X1 + H, X2 + H, Y0, Y1, Y2);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-}
-
 // The device-chosen SwiGLU on eight waves: below kSwigluTallAutoFrom packed rows the
 // eight-wave slabs, from there on 256 x 128 tiles of the split-K GEMM body with eight 64 x 64
 // wave tiles and no split.  Each stage is one X array (the slabs' two 128-row A tiles, or the
@@ -889,26 +656,16 @@ static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st
 
 template <typename T, int EPI>
 static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t st) {
-  if (EPI == kEpiSwiGLU && p.m_cap < kSwigluTallAutoFrom &&
-      (p.bm == kGemmTileAuto || gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 128)) {
-    // too few slots for the tiled path: the eight-wave slabs, whatever the row count
+  if (EPI == kEpiSwiGLU && p.bm == kGemmTileAuto && p.m_cap >= kSwigluTallAutoFrom) {
+    // slabs below kSwigluTallAutoFrom rows, unsplit 256-row tiles above: no reduction pass
+    const int slabs = swiglu_slabs(p.ff, num_cu);
+    swiglu_auto8_kernel<T><<<num_cu, kSlab8Threads, 0, st>>>(p, slabs);
+    return hipGetLastError();
+  }
+  if (EPI == kEpiSwiGLU && (p.bm == kGemmTileAuto || gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 128)) {
+    // 128-row tiles, or too few slots for the tiled path: the slabs, whatever the row count
     const int slabs = swiglu_slabs(p.ff, num_cu);
     swiglu_slab8_kernel<T><<<slabs, kSlab8Threads, 0, st>>>(p, slabs);
-    return hipGetLastError();
-  }
-  if (EPI == kEpiSwiGLU && p.bm == kGemmTileAuto) {
-    // slabs below kGemmTallAutoFrom rows, unsplit 256-row tiles above: no reduction pass
-    const int slabs = swiglu_slabs(p.ff, num_cu);
-#if SPECFOLD_AUTO8
-    swiglu_auto8_kernel<T><<<num_cu, kSlab8Threads, 0, st>>>(p, slabs);
-#else
-    swiglu_auto_kernel<T><<<num_cu, kSlabThreads, 0, st>>>(p, slabs);
-#endif
-    return hipGetLastError();
-  }
-  if (EPI == kEpiSwiGLU && gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 128) {
-    const int slabs = swiglu_slabs(p.ff, num_cu);
-    swiglu_slab_kernel<T><<<slabs, kSlabThreads, 0, st>>>(p, slabs);
     return hipGetLastError();
   }
   return launch_gemm_bn<T, EPI, 128>(p, num_cu, st);
