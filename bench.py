@@ -123,7 +123,17 @@ def kernel_rooflines(cfg, K, kernels):
     return out
 
 
-def build_layer(cfg):
+# Copies of one layer's weights that successive calls take in turn.  In a model each layer's
+# weights are read once per verify step, with every other layer's weights streamed in
+# between, so none of them is still in the GPU's 256 MB memory-side cache when the layer comes
+# round again.  Timing one layer over and over with one set of weights would let the weights
+# that the FFN stream leaves in that cache (QKV, O and down, ~195 MB at the 7B shape) be hit on
+# the next call: 15 us per 7B layer faster than the model would run.  Three copies (1.4 GB at
+# the 7B shape) cycle through more than the cache holds.
+WEIGHT_COPIES = 3
+
+
+def build_layer(cfg, copies=WEIGHT_COPIES):
     import numpy as np  # noqa: F401
     from branch_folding_amd.runner import DeviceLayer
     from synth import make_workload
@@ -131,6 +141,15 @@ def build_layer(cfg):
     w = make_workload(cfg, layers=1)
     log(f"[bench] workload {cfg.name} drawn in {time.time() - t:.1f}s")
     dl = DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src)
+    if copies > 1:
+        sets = [dl.w] + [{k: v.clone() for k, v in dl.w.items()} for _ in range(copies - 1)]
+        base, turn = dl.forward, [0]
+
+        def forward(*a, **k):
+            dl.w = sets[turn[0] % len(sets)]
+            turn[0] += 1
+            return base(*a, **k)
+        dl.forward = forward
     return w, dl
 
 
@@ -265,6 +284,38 @@ def step_distribution(dl, tau, steps, ev, stream):
     def q(f):
         return per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
     return dict(p10=q(0.1), p50=q(0.5), p90=q(0.9), min=per[0], max=per[-1], n=len(per))
+
+
+def vendor_gemm(cfg, K, ev, stream):
+    """The same four products as the layer's GEMMs, through torch.matmul (hipBLASLt), each
+    timed alone: QKV and the FFN on the K packed rows, the O projection on all S slots.
+    Plain products only (no gather, SwiGLU, residual or split reduction); three weight
+    copies in turn, so that, as in the layer, the weights come from HBM and not from the
+    memory-side cache.  A reference point for the layer's kernels, not part of the step."""
+    import torch
+    d, ff, qd, S = cfg.hidden, cfg.ffn, cfg.n_q * cfg.head_dim, cfg.slots
+    shapes = {"qkv": (K, d, cfg.qkv_dim), "o_proj": (S, qd, d),
+              "ffn_gate_up": (K, d, 2 * ff), "ffn_down": (K, ff, d)}
+    out = {}
+    for name, (m, k, n) in shapes.items():
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+        ws = [torch.randn(n, k, device="cuda", dtype=torch.bfloat16) for _ in range(3)]
+        c = torch.empty(m, n, device="cuda", dtype=torch.bfloat16)
+        for i in range(6):
+            torch.matmul(a, ws[i % 3].t(), out=c)
+        t0, t1 = ev.create(2)
+        torch.cuda.synchronize()
+        ev.record(t0, stream)
+        reps = 30
+        for i in range(reps):
+            torch.matmul(a, ws[i % 3].t(), out=c)
+        ev.record(t1, stream)
+        torch.cuda.synchronize()
+        out[name] = ev.ms(t0, t1) * 1e3 / reps
+        ev.destroy([t0, t1])
+        del a, ws, c
+    torch.cuda.empty_cache()
+    return out
 
 
 def measured_peaks(ev, stream):
@@ -432,7 +483,8 @@ def main():
         "data": "synthetic (seeded; random-init weights of the named shape)",
         "config": {"workload": cfg.name, "nodes": cfg.num_nodes, "block": cfg.block,
                    "hidden": cfg.hidden, "heads": f"{cfg.n_q}q/{cfg.n_kv}kv x {cfg.head_dim}",
-                   "ffn": cfg.ffn, "prefix": cfg.prefix, "tau": tau, "graph": cfg.graph},
+                   "ffn": cfg.ffn, "prefix": cfg.prefix, "tau": tau, "graph": cfg.graph,
+                   "weight_copies": WEIGHT_COPIES},
         "us_per_verify_layer": ms * 1e3,
         "us_per_step_dist": dist,
         "packed_rows": K,
@@ -450,6 +502,10 @@ def main():
         result["measured_peaks"] = measured_peaks(ev, stream)
         log("[bench] on-box reference rates: " + ", ".join(
             f"{k}={v:.3g}" for k, v in result["measured_peaks"].items()))
+        if cfg.dtype == "bf16" and K > 0:
+            result["vendor_gemm_us"] = vendor_gemm(cfg, K, ev, stream)
+            log("[bench] the same GEMM shapes through torch.matmul (hipBLASLt), us: " + ", ".join(
+                f"{k}={v:.1f}" for k, v in result["vendor_gemm_us"].items()))
     if args.gate_sweep:
         report["gate_sweep"] = gate_sweep(ev, stream)
         result["gate_sweep"] = report["gate_sweep"]

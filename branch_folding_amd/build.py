@@ -10,7 +10,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libspecfold.so")
-SOURCES = ["specfold_api.hip", "fold_kernels.hip", "gemm.hip", "attention.hip", "lm_head.hip"]
+SOURCES = ["specfold_api.hip", "fold_kernels.hip", "gemm.hip", "gemm_stream.hip", "attention.hip",
+           "lm_head.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -150,6 +150,21 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
       : "memory");
 }
 
+// dma16 with the nontemporal hint: for data read once (streamed weights), so that its lines
+// do not displace data that other CUs are still re-reading from L2.
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[b]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[g], off nt\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [g] "v"(g), [b] "s"(lds_base)
+      : "memory");
+}
+
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -80,6 +80,12 @@ struct GemmParams {
   // [0, a_rows_cap)); nullptr = row m
   const int32_t* a_rows;
   int a_rows_cap;
+  // nonzero: the weight tiles are loaded with the nontemporal hint where each is read once
+  // (one row tile); for weights read once per call and not read ahead into the memory-side
+  // cache by an earlier kernel, the hint keeps them from displacing the activation tiles
+  // every CU re-reads from L2.  Honoured by the SwiGLU and kEpiStore launches.  (Placed in
+  // what would be padding, so the kernel argument block keeps its size.)
+  int w_stream;
   // kEpiArgmax outputs: [m_cap][arg_ld] partial maxima and their column indices
   float* arg_val;
   int32_t* arg_idx;
@@ -145,6 +151,9 @@ __host__ __device__ inline int gemm_split(int tiles, int kiters) {
 
 template <typename T>
 hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st);
+// the kEpiStore GEMM kernel with streamed weights (gemm_stream.hip; no reduction pass)
+template <typename T>
+void launch_gemm_store_stream(const GemmParams& p, int num_cu, hipStream_t st);
 // split-K factor the GEMM uses when the row count M is known on the host
 int gemm_host_split(int M, int N, int Kd, int elem_bytes, int bm);
 

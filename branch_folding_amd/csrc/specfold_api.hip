@@ -335,6 +335,9 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   gp.A = A2; gp.lda = L.ld_d; gp.W = w->w_gate_up; gp.ldw = d; gp.C = G; gp.ldc = L.ld_ff;
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = 2 * ff; gp.Kd = d; gp.ff = ff;
   gp.bm = bm;
+  // the FFN weights are read once per call and nothing reads them ahead: streamed loads
+  // (QKV and O weights are read ahead into the memory-side cache and keep the default)
+  gp.w_stream = 1;
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiSwiGLU, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, false));
@@ -342,6 +345,7 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   gp = GemmParams{};
   gp.A = G; gp.lda = L.ld_ff; gp.W = w->w_down; gp.ldw = ff; gp.C = F; gp.ldc = d;
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = d; gp.Kd = ff; gp.bm = bm;
+  gp.w_stream = 1;
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_DOWN, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
   HIP_CHECK(mark(SPECFOLD_STEP_FFN_DOWN, false));

@@ -10,7 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "branch_folding_amd", "csrc")
-SOURCES = ["specfold_api.hip", "fold_kernels.hip", "gemm.hip", "attention.hip", "lm_head.hip"]
+from branch_folding_amd.build import SOURCES  # noqa: E402  (the library's own source list)
 SANITIZE = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all",
             "-fno-omit-frame-pointer"]
 
