@@ -140,7 +140,13 @@ def build_layer(cfg, copies=WEIGHT_COPIES):
     t = time.time()
     w = make_workload(cfg, layers=1)
     log(f"[bench] workload {cfg.name} drawn in {time.time() - t:.1f}s")
-    dl = DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src)
+    dl = rotating(DeviceLayer(cfg, w.weights[0], w.cache, w.H, w.fold_src), copies)
+    return w, dl
+
+
+def rotating(dl, copies=WEIGHT_COPIES):
+    """Makes successive dl.forward calls take the layer's weights from `copies` copies in
+    turn (the first is dl's own)."""
     if copies > 1:
         sets = [dl.w] + [{k: v.clone() for k, v in dl.w.items()} for _ in range(copies - 1)]
         base, turn = dl.forward, [0]
@@ -150,7 +156,7 @@ def build_layer(cfg, copies=WEIGHT_COPIES):
             turn[0] += 1
             return base(*a, **k)
         dl.forward = forward
-    return w, dl
+    return dl
 
 
 def time_layer(dl, tau, steps, warmup, ev, stream, probe_step=None):
@@ -681,7 +687,7 @@ def budget_sweep(w1, ev, stream, steps, warmup):
     for n in BUDGETS:
         cfg = budget_config(n)
         wn = make_workload(cfg, layers=1, weights=False)
-        dl = DeviceLayer(cfg, w1.weights[0], w1.cache, wn.H, wn.fold_src)
+        dl = rotating(DeviceLayer(cfg, w1.weights[0], w1.cache, wn.H, wn.fold_src))
         for tau in (-1.0, cfg.tau):
             dl.forward(tau, stream=stream)
             torch.cuda.synchronize()
