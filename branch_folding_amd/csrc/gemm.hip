@@ -382,14 +382,18 @@ static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st
   // gemm_stream.hip; compiled here, next to these kernels, they made the compiler drain every
   // load in flight before the LDS reads of these (gemm_auto_kernel: QKV 21.4 -> 28.7 us at the
   // 3B layer)
-  if (EPI == kEpiStore && BN == 128 && p.w_stream)
+  if (EPI == kEpiStore && BN == 128 && p.w_stream) {
     launch_gemm_store_stream<T>(p, num_cu, st);
-  else if (p.bm == kGemmTileAuto)
-    gemm_auto_kernel<T, EPI, BN><<<num_cu, 256 * BN / 64, 0, st>>>(p);
-  else if (gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 256)
+  } else if (p.bm == kGemmTileAuto) {
+    // the device-chosen tile serves the store, partial and argmax epilogues; a SwiGLU call
+    // takes the slab or swiglu_auto8 launches, and nothing calls the residual epilogue here
+    if constexpr (EPI == kEpiSwiGLU || EPI == kEpiResidual) return hipErrorInvalidValue;
+    else gemm_auto_kernel<T, EPI, BN><<<num_cu, 256 * BN / 64, 0, st>>>(p);
+  } else if (gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 256) {
     gemm_kernel<T, EPI, BN, 256><<<num_cu, 256 * BN / 64, 0, st>>>(p);
-  else
+  } else {
     gemm_kernel<T, EPI, BN, 128><<<num_cu, 128 * BN / 64, 0, st>>>(p);
+  }
   // the reduction only runs when some row count could make the device choose split > 1
   if (EPI != kEpiPartial && EPI != kEpiArgmax &&
       gemm_split(ceil_div(p.N, BN), p.Kd / (kGemmBKBytes / (int)sizeof(T))) > 1) {

@@ -26,7 +26,8 @@ __global__ void __launch_bounds__(BM * BN / 64) gemm_nt_kernel(GemmParams p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
-// row tile chosen on the device (the nontemporal hint at one 128-row tile only)
+// row tile chosen on the device (the nontemporal hint at one row tile only; GemmParams::bm =
+// kGemmTileAuto with w_stream set)
 template <typename T, int EPI, int BN>
 __global__ void __launch_bounds__(256 * BN / 64) gemm_auto_nt_kernel(GemmParams p) {
   constexpr int A_BYTES = 256 * kGemmBKBytes;
@@ -35,7 +36,15 @@ __global__ void __launch_bounds__(256 * BN / 64) gemm_auto_nt_kernel(GemmParams 
   __shared__ __attribute__((aligned(1024))) char Ws0[W_BYTES], Ws1[W_BYTES], Ws2[W_BYTES];
   const int M = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
   if (M <= 0) return;
-  if (gemm_bm(p, M) == 256)
+  // Streamed calls run 256-row tiles from kGemmTallAutoStreamFrom (129) rows, so the last
+  // path (128-row tiles, default policy) is not taken with w_stream set.  It stays: without
+  // it the compiler drained every load in flight before the LDS reads of the 256-row
+  // streamed path (s_waitcnt vmcnt(0) ahead of its ds_reads; tests/test_gemm_asm.py checks
+  // the assembly for that).
+  if (gemm_bm(p, M) == 256 && M <= 256)
+    gemm_units<T, EPI, BN, 256, true, 64, 64, 4 * BN / 64, true>(p, M, As0, As1, As2, Ws0, Ws1,
+                                                                 Ws2);
+  else if (gemm_bm(p, M) == 256)
     gemm_units<T, EPI, BN, 256>(p, M, As0, As1, As2, Ws0, Ws1, Ws2);
   else if (M <= 128)
     gemm_units<T, EPI, BN, 128, true, 64, 64, 4 * BN / 64, true>(p, M, As0, As1, As2, Ws0, Ws1,
