@@ -23,6 +23,8 @@
 // Split-K partial sums (fp32) are reduced by a separate kernel in split order, so results
 // are deterministic and no device-scope fences are needed.
 // Wave tile 64 x 64 (4 x 4 MFMA 16x16 tiles); a k-iteration is 128 bytes of K.
+#include <hip/hip_ext.h>
+
 #include "gemm_units.h"
 
 namespace specfold {
@@ -406,35 +408,45 @@ static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st
 }
 
 template <typename T, int EPI>
-static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t st) {
+static hipError_t launch_gemm_epi(const GemmParams& p, int num_cu, hipStream_t st,
+                                  const KernelTimer* timer) {
+  // a single-kernel launch, through hipExtLaunchKernel when it is timed
+  auto one = [&](auto kernel, int grid, int slabs) {
+    if (timer)
+      hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kSlab8Threads), 0, st, timer->start,
+                            timer->stop, 0, p, slabs);
+    else
+      kernel<<<grid, kSlab8Threads, 0, st>>>(p, slabs);
+    return hipGetLastError();
+  };
   if (EPI == kEpiSwiGLU && p.bm == kGemmTileAuto && p.m_cap >= kSwigluTallAutoFrom) {
     // slabs below kSwigluTallAutoFrom rows, unsplit 256-row tiles above: no reduction pass
-    const int slabs = swiglu_slabs(p.ff, num_cu);
-    swiglu_auto8_kernel<T><<<num_cu, kSlab8Threads, 0, st>>>(p, slabs);
-    return hipGetLastError();
+    return one(swiglu_auto8_kernel<T>, num_cu, swiglu_slabs(p.ff, num_cu));
   }
-  if (EPI == kEpiSwiGLU && (p.bm == kGemmTileAuto || gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 128)) {
+  if (EPI == kEpiSwiGLU && swiglu_single_launch(p)) {
     // 128-row tiles, or too few slots for the tiled path: the slabs, whatever the row count
     const int slabs = swiglu_slabs(p.ff, num_cu);
-    swiglu_slab8_kernel<T><<<slabs, kSlab8Threads, 0, st>>>(p, slabs);
-    return hipGetLastError();
+    return one(swiglu_slab8_kernel<T>, slabs, slabs);
   }
   return launch_gemm_bn<T, EPI, 128>(p, num_cu, st);
 }
 
 template <typename T>
-hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st) {
+hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st,
+                       const KernelTimer* timer) {
   switch (epi) {
-    case kEpiStore: return launch_gemm_epi<T, kEpiStore>(p, num_cu, st);
-    case kEpiResidual: return launch_gemm_epi<T, kEpiResidual>(p, num_cu, st);
-    case kEpiSwiGLU: return launch_gemm_epi<T, kEpiSwiGLU>(p, num_cu, st);
-    case kEpiPartial: return launch_gemm_epi<T, kEpiPartial>(p, num_cu, st);
-    case kEpiArgmax: return launch_gemm_epi<T, kEpiArgmax>(p, num_cu, st);
+    case kEpiStore: return launch_gemm_epi<T, kEpiStore>(p, num_cu, st, nullptr);
+    case kEpiResidual: return launch_gemm_epi<T, kEpiResidual>(p, num_cu, st, nullptr);
+    case kEpiSwiGLU: return launch_gemm_epi<T, kEpiSwiGLU>(p, num_cu, st, timer);
+    case kEpiPartial: return launch_gemm_epi<T, kEpiPartial>(p, num_cu, st, nullptr);
+    case kEpiArgmax: return launch_gemm_epi<T, kEpiArgmax>(p, num_cu, st, nullptr);
     default: return hipErrorInvalidValue;
   }
 }
 
-template hipError_t launch_gemm<float>(const GemmParams&, int, int, hipStream_t);
-template hipError_t launch_gemm<bf16>(const GemmParams&, int, int, hipStream_t);
+template hipError_t launch_gemm<float>(const GemmParams&, int, int, hipStream_t,
+                                       const KernelTimer*);
+template hipError_t launch_gemm<bf16>(const GemmParams&, int, int, hipStream_t,
+                                      const KernelTimer*);
 
 }  // namespace specfold

@@ -156,8 +156,22 @@ __host__ __device__ inline int gemm_split(int tiles, int kiters) {
   return s < 1 ? 1 : s;
 }
 
+// Events that time one kernel launch from its start to its end (hipExtLaunchKernel records
+// them on the launch's stream at the kernel's start and completion), for a timing probe of
+// a step that is a single kernel.
+struct KernelTimer {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+// Whether a SwiGLU GEMM call is one kernel launch (the column slabs or the device-chosen
+// swiglu_auto8 launch); the 256-row tiles chosen on the host add a split reduction
+inline bool swiglu_single_launch(const GemmParams& p) {
+  return p.bm == kGemmTileAuto || gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 128;
+}
+// `timer` (may be null): taken by a SwiGLU call that is one launch (swiglu_single_launch)
 template <typename T>
-hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st);
+hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st,
+                       const KernelTimer* timer = nullptr);
 // the kEpiStore GEMM kernel with streamed weights (gemm_stream.hip; no reduction pass)
 template <typename T>
 void launch_gemm_store_stream(const GemmParams& p, int num_cu, hipStream_t st);

@@ -338,9 +338,15 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   // the FFN weights are read once per call and nothing reads them ahead: streamed loads
   // (QKV and O weights are read ahead into the memory-side cache and keep the default)
   gp.w_stream = 1;
-  HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, true));
-  HIP_CHECK(launch_gemm<T>(gp, kEpiSwiGLU, cus, st));
-  HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, false));
+  // a probe of this step times the kernel itself when the step is one launch (its events
+  // taken at the kernel's start and end, as a kernel trace does); else it brackets the launches
+  KernelTimer kt{};
+  const bool timed = probe && probe->step == SPECFOLD_STEP_FFN_GATE_UP && probe->start &&
+                     probe->stop && swiglu_single_launch(gp);
+  if (timed) kt = KernelTimer{(hipEvent_t)probe->start, (hipEvent_t)probe->stop};
+  if (!timed) HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, true));
+  HIP_CHECK(launch_gemm<T>(gp, kEpiSwiGLU, cus, st, timed ? &kt : nullptr));
+  if (!timed) HIP_CHECK(mark(SPECFOLD_STEP_FFN_GATE_UP, false));
 
   gp = GemmParams{};
   gp.A = G; gp.lda = L.ld_ff; gp.W = w->w_down; gp.ldw = ff; gp.C = F; gp.ldc = d;

@@ -291,7 +291,10 @@ typedef enum specfold_step {
 
 /* A timing probe: `start` is recorded on the stream right before the first launch of
  * step `step` and `stop` right after its last launch (both are hipEvent_t created by the
- * caller).  Nothing is recorded for a step that the call skips. */
+ * caller).  When the FFN gate/up step is a single kernel (the column slabs, or the tiles
+ * chosen on the device), its events are instead taken at that kernel's start and end
+ * (hipExtLaunchKernel), which leaves out the cost of recording two events around it.
+ * Nothing is recorded for a step that the call skips. */
 typedef struct specfold_probe {
   int32_t step;
   void* start;
