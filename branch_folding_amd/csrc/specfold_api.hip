@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -121,18 +122,20 @@ specfold_status check_shape(const specfold_shape* s, bool layer) {
   return SPECFOLD_OK;
 }
 
+// Compute units of the current device, cached per device (threads may race to fill an entry;
+// they all store the same value).
 int num_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kPlanCUs;
-  if (cache[dev] == 0) {
-    int v = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         v <= 0)
       v = kPlanCUs;
-    cache[dev] = v;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
