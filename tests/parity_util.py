@@ -4,6 +4,7 @@ import math
 import numpy as np
 
 from oracle import fold_state, layer
+from synth import custom_config
 
 # Tolerances on the layer output: max|y - y_ref| / max|y_ref|.
 TOL = {"f32": 1e-3, "bf16": 2e-2}
@@ -54,3 +55,41 @@ def assert_fold_state_equal(gpu, ora, tau, ratio_rtol=2e-5):
         np.testing.assert_array_equal(gpu["slot_row"], ora["slot_row"])
         return True
     return False
+
+
+# Seeded random shapes: every combination axis the layer takes (dtype, head_dim, GQA group,
+# KV heads, hidden and FFN widths, node count, ragged block length, prefix length across the
+# three prefix paths, graph kind, reveal pattern, rotary embedding and bias, tau), drawn
+# independently so that combinations no hand-picked case names get run.  Sizes are bounded
+# so that the oracle finishes each case in seconds.
+PREFIXES = [0, 1, 17, 64, 65, 300, 512, 513, 700, 2048, 2100]
+TAUS = [-1.0, 0.0, 0.02, 0.05, 0.1, 0.3, math.inf]
+
+
+def random_case(seed):
+    """(config, tau) of random case `seed`: a pure function of the seed."""
+    r = np.random.default_rng(9100 + seed)
+    dtype = ("f32", "bf16")[int(r.integers(2))]
+    dh = int(r.choice([64, 128]))
+    n_kv = int(r.choice([1, 2, 4]))
+    n_q = n_kv * int(r.choice([1, 2, 3, 4, 7]))
+    hidden = 128 * int(r.integers(1, 5))
+    ffn = 128 * int(r.integers(1, 6))
+    graph = str(r.choice(["chain", "star", "tree3", "dag", "dag_deep"]))
+    N = int(r.integers(1, 25))
+    B = int(r.integers(1, 81))
+    P = int(r.choice(PREFIXES))
+    while N > 1 and N * B * n_q * (P + B) * dh > 6e8:   # the oracle's attention work
+        N -= 1
+    lo = int(r.integers(1, 4))
+    hi = lo + int(r.integers(0, 4))
+    rope = float(r.choice([0.0, 0.0, 1.0e4, 1.0e6]))
+    bias = bool(r.integers(2))
+    tau = float(r.choice(TAUS))
+    name = (f"rand{seed}-{dtype}-N{N}B{B}-d{hidden}f{ffn}-q{n_q}kv{n_kv}dh{dh}-P{P}-{graph}"
+            + ("-rope" if rope else "") + ("-bias" if bias else ""))
+    cfg = custom_config(name=name, num_nodes=N, block=B, hidden=hidden, n_q=n_q, n_kv=n_kv,
+                        head_dim=dh, ffn=ffn, prefix=P, dtype=dtype, graph=graph,
+                        reveal=(lo, hi), seed=9200 + seed, max_depth=int(r.integers(2, 7)),
+                        rope_theta=rope, qkv_bias=bias)
+    return cfg, tau

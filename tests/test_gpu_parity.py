@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from parity_util import (TOL, assert_fold_state_equal, max_abs_rel, oracle_layer,
-                         oracle_state)
+                         oracle_state, random_case)
 from synth import CONFIGS, budget_config, custom_config, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -408,6 +408,13 @@ def test_layer_reuse_attention(cfg, tau):
     source's attention output; the O projection runs on the packed rows only.  Compared
     with the oracle's attn="reuse" layer, and on the GPU output itself the closed form
     y[n,i] - y[src,i] = H[n,i] - H[src,i] within the output tolerance."""
+    _check_reuse(cfg, tau, expect_difference=True)
+
+
+def _check_reuse(cfg, tau, expect_difference):
+    """expect_difference: the case folds slots next to recomputed keys, so the corrected
+    layer must differ from the reused one somewhere (not so where every folded slot's
+    branch keys are its source's own, e.g. at tau = inf)."""
     L, DeviceLayer = _dev()
     w = _workload(cfg)
     _say(f"[gpu] reuse layer {cfg.name} tau={tau}")
@@ -442,10 +449,11 @@ def test_layer_reuse_attention(cfg, tau):
                 worst = max(worst, float(np.max(np.abs(d))) / scale)
     assert worst <= tol, worst
     # the corrected and the reused layer differ once anything folds next to a recomputed key
-    dl.forward(tau)
-    torch.cuda.synchronize()
-    if (~st["recompute"]).any():
-        assert np.max(np.abs(dl.output_numpy() - y)) > 0
+    if expect_difference:
+        dl.forward(tau)
+        torch.cuda.synchronize()
+        if (~st["recompute"]).any():
+            assert np.max(np.abs(dl.output_numpy() - y)) > 0
 
 
 @pytest.mark.parametrize("cfg", TALL, ids=lambda c: c.name)
@@ -596,44 +604,8 @@ def test_layer_mid_prefix(cfg, tau):
     _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
 
 
-# Seeded random shapes: every combination axis the layer takes (dtype, head_dim, GQA group,
-# KV heads, hidden and FFN widths, node count, ragged block length, prefix length across the
-# three prefix paths, graph kind, reveal pattern, rotary embedding and bias, tau), drawn
-# independently so that combinations no hand-picked case names get run.  Sizes are bounded
-# so that the oracle finishes each case in seconds.
-_PREFIXES = [0, 1, 17, 64, 65, 300, 512, 513, 700, 2048, 2100]
-_TAUS = [-1.0, 0.0, 0.02, 0.05, 0.1, 0.3, math.inf]
-
-
-def _random_case(seed):
-    r = np.random.default_rng(9100 + seed)
-    dtype = ("f32", "bf16")[int(r.integers(2))]
-    dh = int(r.choice([64, 128]))
-    n_kv = int(r.choice([1, 2, 4]))
-    n_q = n_kv * int(r.choice([1, 2, 3, 4, 7]))
-    hidden = 128 * int(r.integers(1, 5))
-    ffn = 128 * int(r.integers(1, 6))
-    graph = str(r.choice(["chain", "star", "tree3", "dag", "dag_deep"]))
-    N = int(r.integers(1, 25))
-    B = int(r.integers(1, 81))
-    P = int(r.choice(_PREFIXES))
-    while N > 1 and N * B * n_q * (P + B) * dh > 6e8:   # the oracle's attention work
-        N -= 1
-    lo = int(r.integers(1, 4))
-    hi = lo + int(r.integers(0, 4))
-    rope = float(r.choice([0.0, 0.0, 1.0e4, 1.0e6]))
-    bias = bool(r.integers(2))
-    tau = float(r.choice(_TAUS))
-    name = (f"rand{seed}-{dtype}-N{N}B{B}-d{hidden}f{ffn}-q{n_q}kv{n_kv}dh{dh}-P{P}-{graph}"
-            + ("-rope" if rope else "") + ("-bias" if bias else ""))
-    cfg = custom_config(name=name, num_nodes=N, block=B, hidden=hidden, n_q=n_q, n_kv=n_kv,
-                        head_dim=dh, ffn=ffn, prefix=P, dtype=dtype, graph=graph,
-                        reveal=(lo, hi), seed=9200 + seed, max_depth=int(r.integers(2, 7)),
-                        rope_theta=rope, qkv_bias=bias)
-    return cfg, tau
-
-
-RANDOM = [_random_case(s) for s in range(32)]
+# Seeded random shapes (parity_util.random_case): combinations no hand-picked case names.
+RANDOM = [random_case(s) for s in range(32)]
 
 
 @pytest.mark.parametrize("case", RANDOM, ids=lambda c: f"{c[0].name}-tau{c[1]}")
@@ -641,3 +613,10 @@ def test_layer_random_shapes(case):
     cfg, tau = case
     L, DeviceLayer = _dev()
     _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
+
+
+@pytest.mark.parametrize("case", RANDOM[::2], ids=lambda c: f"{c[0].name}-tau{c[1]}")
+def test_layer_random_shapes_reuse(case):
+    """The REUSE variant on every other seeded random shape."""
+    cfg, tau = case
+    _check_reuse(cfg, tau, expect_difference=False)

@@ -30,7 +30,7 @@ import pytest
 import torch
 
 from oracle import stack
-from parity_util import TOL, assert_fold_state_equal, max_abs_rel
+from parity_util import TOL, assert_fold_state_equal, max_abs_rel, random_case
 from synth import CONFIGS, custom_config, iter_layers, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -250,6 +250,23 @@ SMALL = [
 @pytest.mark.parametrize("tau", [0.05, 0.3])
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_stack_small(cfg, tau):
+    L, runner = _dev()
+    _check_stack(cfg, cfg.layers, tau, L, runner)
+
+
+# Three-layer stacks on every fourth seeded random layer shape (rotary embedding and bias
+# off: the oracle's stack runs plain layers), mostly at thresholds where some slots fold
+# and others recompute in every layer.
+_STACK_TAUS = (0.05, 0.3, 0.02, 0.1, -1.0, math.inf, 0.05, 0.0)
+RANDOM_STACK = [
+    (c.with_(name=c.name.replace("-rope", "").replace("-bias", "") + "-x3", layers=3,
+             rope_theta=0.0, qkv_bias=False), _STACK_TAUS[i])
+    for i, (c, _) in enumerate(random_case(s) for s in range(1, 32, 4))]
+
+
+@pytest.mark.parametrize("case", RANDOM_STACK, ids=lambda c: f"{c[0].name}-tau{c[1]}")
+def test_stack_random_shapes(case):
+    cfg, tau = case
     L, runner = _dev()
     _check_stack(cfg, cfg.layers, tau, L, runner)
 
