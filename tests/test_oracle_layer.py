@@ -20,6 +20,7 @@ import torch
 import torch.nn.functional as Fn
 
 from oracle import fold_state, layer, serial_layer
+from parity_util import random_case
 from synth import CONFIGS, custom_config, make_workload
 
 
@@ -66,7 +67,15 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("cfg", SMALL + [CONFIGS[0]], ids=lambda c: c.name + str(c.seed))
+# Every fourth seeded random shape of the GPU parity sweep (GQA groups, head_dim 128,
+# prefixes up to 2100 keys, blocks up to 80, up to 24 nodes), without rotary embedding and
+# bias, which the textbook layer here does not have.
+RANDOM = [random_case(s)[0] for s in range(0, 32, 4)]
+RANDOM = [c.with_(name=c.name.replace("-rope", "").replace("-bias", ""), rope_theta=0.0,
+                  qkv_bias=False) for c in RANDOM]
+
+
+@pytest.mark.parametrize("cfg", SMALL + [CONFIGS[0]] + RANDOM, ids=lambda c: c.name + str(c.seed))
 def test_dense_equals_textbook_layer(cfg):
     w = make_workload(cfg)
     out = _run(w, -1.0)
@@ -79,7 +88,7 @@ def test_dense_equals_textbook_layer(cfg):
 
 
 @pytest.mark.parametrize("tau", [0.02, 0.05, 0.2, 1.0])
-@pytest.mark.parametrize("cfg", SMALL + [CONFIGS[0]], ids=lambda c: c.name + str(c.seed))
+@pytest.mark.parametrize("cfg", SMALL + [CONFIGS[0]] + RANDOM, ids=lambda c: c.name + str(c.seed))
 def test_folded_equals_textbook_on_substituted_input(cfg, tau):
     w = make_workload(cfg)
     out = _run(w, tau)
