@@ -620,3 +620,24 @@ def test_layer_random_shapes_reuse(case):
     """The REUSE variant on every other seeded random shape."""
     cfg, tau = case
     _check_reuse(cfg, tau, expect_difference=False)
+
+
+# The largest draft the boundary accepts: num_nodes * block = 16384 slots, as 256 nodes of
+# 64 positions and as 16 nodes of the longest block (1024 positions: 16 key tiles of the
+# branch's own block in the block phase), dense and folded.
+MAXIMUM = [
+    custom_config(name="max-slots-256x64-bf16", num_nodes=256, block=64, hidden=128, n_q=2,
+                  n_kv=1, head_dim=64, ffn=128, prefix=16, dtype="bf16", graph="dag",
+                  reveal=(1, 3), seed=95),
+    custom_config(name="max-block-16x1024-f32", num_nodes=16, block=1024, hidden=128, n_q=4,
+                  n_kv=2, head_dim=64, ffn=128, prefix=33, dtype="f32", graph="tree3",
+                  reveal=(1, 8), seed=96),
+]
+
+
+@pytest.mark.parametrize("cfg", MAXIMUM, ids=lambda c: c.name)
+@pytest.mark.parametrize("tau", [-1.0, 0.05])
+def test_layer_maximum_sizes(cfg, tau):
+    L, DeviceLayer = _dev()
+    assert cfg.slots == 16384
+    _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
