@@ -641,3 +641,27 @@ def test_layer_maximum_sizes(cfg, tau):
     L, DeviceLayer = _dev()
     assert cfg.slots == 16384
     _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
+
+
+# The widest shapes the boundary accepts, one dimension at a time: hidden 32768 (rows of 8192
+# fp32 chunks: the gate and the O finish loop over them), FFN 131072 (1639 SwiGLU slabs of
+# five pairs; a down GEMM over 131072), and 256 query heads over 8 KV heads (32 query heads
+# per KV head).
+MAX_WIDTH = [
+    custom_config(name="max-hidden-32768-f32", num_nodes=3, block=5, hidden=32768, n_q=2,
+                  n_kv=1, head_dim=64, ffn=128, prefix=20, dtype="f32", graph="chain",
+                  reveal=(1, 2), seed=97),
+    custom_config(name="max-ffn-131072-bf16", num_nodes=2, block=9, hidden=128, n_q=2, n_kv=1,
+                  head_dim=64, ffn=131072, prefix=20, dtype="bf16", graph="chain",
+                  reveal=(1, 2), seed=98),
+    custom_config(name="max-heads-256q8kv-bf16", num_nodes=3, block=6, hidden=256, n_q=256,
+                  n_kv=8, head_dim=64, ffn=128, prefix=40, dtype="bf16", graph="tree3",
+                  reveal=(1, 2), seed=99),
+]
+
+
+@pytest.mark.parametrize("cfg", MAX_WIDTH, ids=lambda c: c.name)
+@pytest.mark.parametrize("tau", [-1.0, 0.3])
+def test_layer_maximum_widths(cfg, tau):
+    L, DeviceLayer = _dev()
+    _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
