@@ -70,6 +70,7 @@ constexpr int kMaxFfn = 131072;
 constexpr int kMaxHeads = 256;
 constexpr int kMaxPrefix = 1 << 24;
 constexpr int kMaxVocab = 1 << 24;
+constexpr int64_t kMaxTokStrideBytes = 1LL << 26;   // 64 MB per prefix token
 
 specfold_status check_graph_shape(const specfold_shape* s) {
   if (!s) return fail(SPECFOLD_ERR_INVALID_ARGUMENT, "shape is NULL");
@@ -404,6 +405,12 @@ specfold_status check_layer_params(const specfold_shape* shape,
         (prefix->stride_head * eb) % 16 != 0)
       return fail(SPECFOLD_ERR_INVALID_ARGUMENT,
                   "prefix view pointers and strides must keep rows 16-byte aligned%s", at);
+    // the prefix kernels hold a lane's offset inside a 64-key tile in 32 bits
+    if (prefix->stride_tok * eb >= kMaxTokStrideBytes)
+      return fail(SPECFOLD_ERR_UNSUPPORTED,
+                  "prefix stride_tok of %lld elements is %lld bytes; token strides must stay "
+                  "below %lld bytes%s", (long long)prefix->stride_tok,
+                  (long long)(prefix->stride_tok * eb), (long long)kMaxTokStrideBytes, at);
   }
   return SPECFOLD_OK;
 }

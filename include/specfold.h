@@ -105,7 +105,8 @@ typedef struct specfold_shape {
 
 /* Zero-copy strided view of the shared prefix cache (SpecFold explainer: the shared cache
  * is referenced, never copied per branch).  Strides are in elements; the head_dim
- * elements of one (token, head) are contiguous; strides must keep rows 16-byte aligned. */
+ * elements of one (token, head) are contiguous; strides must keep rows 16-byte aligned,
+ * and stride_tok must stay below 64 MB per token (SPECFOLD_ERR_UNSUPPORTED otherwise). */
 typedef struct specfold_kv_view {
   const void* k;
   const void* v;

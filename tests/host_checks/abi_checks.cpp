@@ -164,6 +164,9 @@ void reject_calls() {
   specfold_kv_view neg{P(), P(), -1024, 128};
   fwd(SPECFOLD_ERR_INVALID_ARGUMENT, weights(), &neg, P(), P(1ull << 32), fs, 0, nullptr,
       P(1ull << 34), need, "negative prefix stride");
+  specfold_kv_view huge{P(), P(), 1ll << 40, 128};
+  fwd(SPECFOLD_ERR_UNSUPPORTED, weights(), &huge, P(), P(1ull << 32), fs, 0, nullptr,
+      P(1ull << 34), need, "token stride beyond the prefix kernels' reach");
   fwd(SPECFOLD_ERR_INVALID_ARGUMENT, weights(), &kv, P(), P(1ull << 32), nullptr, 0, nullptr,
       P(1ull << 34), need, "missing fold_src");
   fwd(SPECFOLD_ERR_INVALID_ARGUMENT, weights(), &kv, P(), P(1ull << 32), fs, 0x80, nullptr,

@@ -100,6 +100,11 @@ def test_forward_argument_errors():
     assert _fwd(sh, hidden_in=None)[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
     assert _fwd(sh, prefix=None)[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
     assert _fwd(sh, prefix=(FAKE, FAKE, 1001, 128))[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
+    # token strides the prefix kernels cannot address (bf16: 2^25 elements = 64 MB)
+    assert _fwd(sh, prefix=(FAKE, FAKE, 1 << 25, 128))[0] == L.SPECFOLD_ERR_UNSUPPORTED
+    # just below it the view passes, and the call fails on the next check (no fold_src)
+    st, msg = _fwd(sh, prefix=(FAKE, FAKE, (1 << 25) - 8, 128), fold_src=None)
+    assert st == L.SPECFOLD_ERR_INVALID_ARGUMENT and "fold_src" in msg
     assert _fwd(sh, fold_src=None)[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
     assert _fwd(sh, flags=4)[0] == L.SPECFOLD_ERR_INVALID_ARGUMENT
     assert _fwd(sh, flags=L.SPECFOLD_FLAG_FOLD_STATE_IN,
