@@ -665,3 +665,15 @@ MAX_WIDTH = [
 def test_layer_maximum_widths(cfg, tau):
     L, DeviceLayer = _dev()
     _check_layer(cfg, _workload(cfg), tau, L, DeviceLayer)
+
+
+def test_layer_million_key_prefix():
+    """A prefix of 2^20 + 37 keys (bf16; the 256-query prefix kernel over 16385 key tiles,
+    the last one ragged, split across units and merged), dense and folded."""
+    L, DeviceLayer = _dev()
+    cfg = custom_config(name="prefix-1048613-bf16", num_nodes=3, block=5, hidden=128, n_q=4,
+                        n_kv=1, head_dim=64, ffn=128, prefix=(1 << 20) + 37, dtype="bf16",
+                        graph="chain", reveal=(1, 2), seed=101)
+    w = _workload(cfg)
+    for tau in (-1.0, 0.3):
+        _check_layer(cfg, w, tau, L, DeviceLayer)
