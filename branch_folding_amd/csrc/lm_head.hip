@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(256) argmax_finish_kernel(const float* __restr
     if (t == 0) {
 #pragma unroll
       for (int w = 1; w < 4; ++w) argmax_take(bv, bi, sv[w], si[w]);
-      row_token[k] = (bi >= 0 && bi < V) ? bi : -1;   // -1: no finite logit in the row
+      row_token[k] = (bi >= 0 && bi < V) ? bi : -1;   // -1: no logit above -inf (all NaN)
       if (row_logit) row_logit[k] = bv;
     }
     __syncthreads();

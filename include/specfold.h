@@ -338,13 +338,15 @@ size_t specfold_lm_head_workspace_bytes(const specfold_shape* shape, int32_t voc
  *     a_k = hidden[slot] / sqrt(mean(hidden[slot]^2) + rms_eps) * rms_final
  *     logit[k, v] = a_k . w_lm[v]                      (fp32 accumulation)
  *     row_token[k] = the first v of the largest logit;  row_logit[k] = that logit
+ *                    (NaN logits never win)
  *   token[n, i] = row_token[slot_row[n, i]] for every slot.
  * The fold state (packed_slot, slot_row, packed_count) is the last layer's, as produced
  * by specfold_layer_forward / specfold_stack_forward; with every slot packed (tau < 0)
  * every slot gets its own prediction.  The logits are never stored.
  *   shape:       num_nodes, block, hidden, rms_eps, dtype are used (hidden % 128 == 0)
  *   rms_final:   [d] dtype;  w_lm: [vocab, d] dtype, row-major;  hidden: [N, B, d] dtype
- *   row_token:   int32 [N*B] capacity, first K written (-1 if a row has no finite logit)
+ *   row_token:   int32 [N*B] capacity, first K written (-1 if no logit of the row is above
+ *                -inf, e.g. all NaN; its row_logit is then -inf)
  *   row_logit:   float [N*B] capacity or NULL;  token: int32 [N, B]
  *   workspace:   specfold_lm_head_workspace_bytes(shape, vocab) bytes, 256-byte aligned
  * Errors: SPECFOLD_ERR_INVALID_ARGUMENT for NULL / misaligned pointers or vocab outside

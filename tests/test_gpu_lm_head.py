@@ -39,13 +39,12 @@ def _to_dev(x, dtype):
     return t.to(dtype).cuda()
 
 
-def _run(cfg, H, fold_src, tau, vocab, rows=None):
+def _gpu_lm_head(cfg, H, st, g, w, vocab):
+    """specfold_lm_head_argmax on hidden rows H with fold state st: (row_token, row_logit,
+    token) on the host."""
     L = _dev()
     from branch_folding_amd.runner import shape_of
-    print(f"[gpu] lm head {cfg.name} V={vocab} tau={tau}", flush=True)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    g, w = lm_head_weights(cfg, vocab)
-    st = fold_state(H, fold_src, tau)
     S, K = cfg.slots, st["K"]
     sh = shape_of(cfg)
     ws_bytes = L.specfold_lm_head_workspace_bytes(sh, vocab)
@@ -62,7 +61,15 @@ def _run(cfg, H, fold_src, tau, vocab, rows=None):
     tok = torch.full((S,), -7, dtype=torch.int32, device="cuda")
     L.specfold_lm_head_argmax(sh, vocab, gd, wd, hid, ps, sr, cnt, rt, rl, tok, ws, ws_bytes)
     torch.cuda.synchronize()
-    rt, rl, tok = rt.cpu().numpy(), rl.cpu().numpy(), tok.cpu().numpy().reshape(st["slot_row"].shape)
+    return rt.cpu().numpy(), rl.cpu().numpy(), tok.cpu().numpy().reshape(st["slot_row"].shape)
+
+
+def _run(cfg, H, fold_src, tau, vocab, rows=None):
+    print(f"[gpu] lm head {cfg.name} V={vocab} tau={tau}", flush=True)
+    g, w = lm_head_weights(cfg, vocab)
+    st = fold_state(H, fold_src, tau)
+    S, K = cfg.slots, st["K"]
+    rt, rl, tok = _gpu_lm_head(cfg, H, st, g, w, vocab)
     # the gather is exact
     np.testing.assert_array_equal(tok, rt[st["slot_row"]])
     ref = lm_head_argmax(H, g, w, st, eps=cfg.rms_eps, rows=rows)
@@ -79,7 +86,8 @@ def _run(cfg, H, fold_src, tau, vocab, rows=None):
     for r, k in enumerate(ks):
         t, gg = int(ref["row_token"][k]), int(rt[k])
         assert 0 <= gg < vocab, (k, gg)
-        top2 = np.partition(lg[r], -2)[-2:]
+        # with one token in the vocabulary there is no runner-up: the pick is forced
+        top2 = np.partition(lg[r], -2)[-2:] if vocab > 1 else np.array([-np.inf, lg[r, 0]])
         if top2[1] - top2[0] > 2 * e[r].max():
             assert gg == t, (k, gg, t)
             exact += 1
@@ -103,6 +111,41 @@ def test_lm_head_small_fp32():
                         graph="chain", seed=42)
     w = make_workload(cfg, weights=False)
     _run(cfg, w.H, w.fold_src, 0.05, vocab=333)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("vocab", [1, 17, 65])
+def test_lm_head_tiny_vocab(vocab, dtype):
+    """Vocabularies smaller than one wave's 64 columns (one token: every pick is token 0),
+    and one column past a wave."""
+    cfg = custom_config(name=f"lm-tiny-{dtype}", num_nodes=4, block=9, hidden=128, dtype=dtype,
+                        graph="tree3", seed=43)
+    w = make_workload(cfg, weights=False)
+    st = _run(cfg, w.H, w.fold_src, 0.05, vocab=vocab)
+    assert st["K"] > 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lm_head_row_without_finite_logit(dtype):
+    """A packed row whose hidden state is NaN has no logit above -inf: its token is -1 and
+    its logit -inf (the header's contract), and every other row's token and logit equal a
+    clean run's."""
+    cfg = custom_config(name=f"lm-nan-{dtype}", num_nodes=4, block=9, hidden=128, dtype=dtype,
+                        graph="tree3", seed=44)
+    w = make_workload(cfg, weights=False)
+    g, wl = lm_head_weights(cfg, 300)
+    st = fold_state(w.H, w.fold_src, 0.05)
+    assert st["packed_slot"][0] == 0                  # the root's first slot is packed row 0
+    rt0, rl0, tok0 = _gpu_lm_head(cfg, w.H, st, g, wl, 300)
+    Hn = w.H.copy()
+    Hn[0, 0, :] = np.nan
+    rt, rl, tok = _gpu_lm_head(cfg, Hn, st, g, wl, 300)
+    K = st["K"]
+    assert rt[0] == -1 and rl[0] == -np.inf
+    np.testing.assert_array_equal(rt[1:K], rt0[1:K])
+    np.testing.assert_array_equal(rl[1:K], rl0[1:K])
+    np.testing.assert_array_equal(tok, rt[st["slot_row"]])
+    assert np.all(tok[st["slot_row"] == 0] == -1)
 
 
 def test_lm_head_7b_full_vocab_sampled_rows():
