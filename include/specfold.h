@@ -156,7 +156,7 @@ typedef struct specfold_fold_state {
  * For every child n >= 1 and position i:
  *     r = ||H[n,i] - H[p,i]||_2 / ||H[p,i]||_2,  p = fold_src[n],
  * accumulated in fp32; recompute = !(r <= tau), so tau < 0 folds nothing, tau = +inf
- * folds every finite ratio, and NaN recomputes.  ||H[p,i]|| = 0 gives r = 0 when the
+ * folds every finite ratio, a NaN ratio recomputes and a NaN tau folds nothing.  ||H[p,i]|| = 0 gives r = 0 when the
  * rows are equal and +inf otherwise.  Root rows always recompute (r = +inf), and so
  * does any node whose fold_src entry is not in [0, n).
  *   hidden    [N, B, d] device, dtype = shape->dtype

@@ -549,8 +549,8 @@ def test_gate_golden_cases(dtype):
     exact rational to fp32 rounding, a zero-norm parent gives 0 (equal rows) or +inf, a
     NaN anywhere in either row gives NaN and recomputes, and the decision fold iff
     r <= tau holds at tau = 0 (identical rows fold), at tau equal to a case's exact
-    ratio (1 and 1/2 fold), between ratios, at +inf (every finite ratio folds) and below
-    zero (nothing folds).  The root's rows always recompute with r = +inf."""
+    ratio (1 and 1/2 fold), between ratios, at +inf (every finite ratio folds), below
+    zero and at a NaN tau (nothing folds).  The root's rows always recompute with r = +inf."""
     L, _ = _dev()
     from branch_folding_amd.runner import shape_of
     d = 128
@@ -563,7 +563,7 @@ def test_gate_golden_cases(dtype):
     fs = torch.tensor([-1, 0], dtype=torch.int32, device="cuda")
     exact = np.array([np.nan if r is None else (math.inf if r[1] == 0 else r[0] / r[1])
                       for r in want])
-    for tau in (1.0, 0.5, 0.0, 0.75, math.inf, -1.0):
+    for tau in (1.0, 0.5, 0.0, 0.75, math.inf, -1.0, math.nan):
         _say(f"[gpu] gate golden {dtype} tau={tau}")
         ratio = torch.empty(2 * B, device="cuda")
         rec = torch.empty(2 * B, dtype=torch.uint8, device="cuda")

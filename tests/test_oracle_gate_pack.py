@@ -70,6 +70,8 @@ def test_gate_special_thresholds():
     H[2, 5, 0] = np.nan
     _, _, rec_nan = gate(H, w.fold_src, math.inf)
     assert rec_nan[2, 5]                                        # NaN ratio recomputes
+    _, _, rec_nan_tau = gate(w.H, w.fold_src, math.nan)
+    assert rec_nan_tau.all()                                    # NaN tau: nothing folds
 
 
 def test_gate_ratio_peaks_at_revealed_positions():
