@@ -221,12 +221,15 @@ def measured_traffic(kernel, workload):
         return None
     if rec.get("kernel") != kernel or rec.get("workload") != workload:
         return None
-    src = os.path.join(ROOT, rec.get("source", ""))
+    # every source file of the kernel's translation unit, hashed in the listed order
+    h = hashlib.sha256()
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        for src in rec.get("sources", []):
+            h.update(open(os.path.join(ROOT, src), "rb").read())
     except OSError:
         return None
-    return rec.get("hbm_bytes_per_launch") if sha == rec.get("source_sha256") else None
+    ok = rec.get("sources") and h.hexdigest() == rec.get("sources_sha256")
+    return rec.get("hbm_bytes_per_launch") if ok else None
 
 
 def calibration_copy(reps=3):
