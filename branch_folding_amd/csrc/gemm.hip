@@ -380,12 +380,12 @@ size_t gemm_partial_elems(int m_cap, int N, int Kd, int elem_bytes, bool always)
 
 template <typename T, int EPI, int BN>
 static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st) {
-  // plain stores with streamed weights (the FFN down projection) run the kernels of
-  // gemm_stream.hip; compiled here, next to these kernels, they made the compiler drain every
-  // load in flight before the LDS reads of these (gemm_auto_kernel: QKV 21.4 -> 28.7 us at the
-  // 3B layer)
-  if (EPI == kEpiStore && BN == 128 && p.w_stream) {
-    launch_gemm_store_stream<T>(p, num_cu, st);
+  // plain stores and the argmax epilogue with streamed weights (the FFN down projection, the
+  // LM head) run the kernels of gemm_stream.hip; compiled here, next to these kernels, they
+  // made the compiler drain every load in flight before the LDS reads of these
+  // (gemm_auto_kernel: QKV 21.4 -> 28.7 us at the 3B layer)
+  if ((EPI == kEpiStore || EPI == kEpiArgmax) && BN == 128 && p.w_stream) {
+    launch_gemm_stream<T, EPI>(p, num_cu, st);
   } else if (p.bm == kGemmTileAuto) {
     // the device-chosen tile serves the store, partial and argmax epilogues; a SwiGLU call
     // takes the slab or swiglu_auto8 launches, and nothing calls the residual epilogue here

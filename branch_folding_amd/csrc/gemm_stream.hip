@@ -1,8 +1,9 @@
-// The FFN down projection's GEMM with streamed weights (GemmParams::w_stream): the kernels of
-// gemm.hip's plain-store path, except that at one row tile -- each weight tile then read
-// once -- the weight loads carry the nontemporal hint, so the weight stream does not push the
-// activation operand, which every CU re-reads, out of L2 (7B layer, 122 packed rows: down
-// 47.2 -> 44 us).  With more row tiles the weights are re-read and keep the default policy.
+// GEMMs with streamed weights (GemmParams::w_stream): the FFN down projection (plain stores)
+// and the LM head (argmax epilogue).  The kernels of gemm.hip's path for those epilogues,
+// except that at one row tile -- each weight tile then read once -- the weight loads carry
+// the nontemporal hint, so the weight stream does not push the activation operand, which
+// every CU re-reads, out of L2 (7B layer, 122 packed rows: down 47.2 -> 44 us).  With more
+// row tiles the weights are re-read and keep the default policy.
 // A translation unit of its own: compiled beside the plain kernels these made the compiler
 // drain every load in flight before the plain kernels' LDS reads.
 #include "gemm_units.h"
@@ -54,18 +55,20 @@ __global__ void __launch_bounds__(256 * BN / 64) gemm_auto_nt_kernel(GemmParams 
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
-template <typename T>
-void launch_gemm_store_stream(const GemmParams& p, int num_cu, hipStream_t st) {
+template <typename T, int EPI>
+void launch_gemm_stream(const GemmParams& p, int num_cu, hipStream_t st) {
   constexpr int BN = 128;
   if (p.bm == kGemmTileAuto)
-    gemm_auto_nt_kernel<T, kEpiStore, BN><<<num_cu, 256 * BN / 64, 0, st>>>(p);
+    gemm_auto_nt_kernel<T, EPI, BN><<<num_cu, 256 * BN / 64, 0, st>>>(p);
   else if (gemm_bm_of(p.bm, p.m_cap, p.m_cap) == 256)
-    gemm_nt_kernel<T, kEpiStore, BN, 256><<<num_cu, 256 * BN / 64, 0, st>>>(p);
+    gemm_nt_kernel<T, EPI, BN, 256><<<num_cu, 256 * BN / 64, 0, st>>>(p);
   else
-    gemm_nt_kernel<T, kEpiStore, BN, 128><<<num_cu, 128 * BN / 64, 0, st>>>(p);
+    gemm_nt_kernel<T, EPI, BN, 128><<<num_cu, 128 * BN / 64, 0, st>>>(p);
 }
 
-template void launch_gemm_store_stream<float>(const GemmParams&, int, hipStream_t);
-template void launch_gemm_store_stream<bf16>(const GemmParams&, int, hipStream_t);
+template void launch_gemm_stream<float, kEpiStore>(const GemmParams&, int, hipStream_t);
+template void launch_gemm_stream<bf16, kEpiStore>(const GemmParams&, int, hipStream_t);
+template void launch_gemm_stream<float, kEpiArgmax>(const GemmParams&, int, hipStream_t);
+template void launch_gemm_stream<bf16, kEpiArgmax>(const GemmParams&, int, hipStream_t);
 
 }  // namespace specfold

@@ -172,9 +172,10 @@ inline bool swiglu_single_launch(const GemmParams& p) {
 template <typename T>
 hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st,
                        const KernelTimer* timer = nullptr);
-// the kEpiStore GEMM kernel with streamed weights (gemm_stream.hip; no reduction pass)
-template <typename T>
-void launch_gemm_store_stream(const GemmParams& p, int num_cu, hipStream_t st);
+// the kEpiStore or kEpiArgmax GEMM kernel with streamed weights (gemm_stream.hip; no
+// reduction pass)
+template <typename T, int EPI>
+void launch_gemm_stream(const GemmParams& p, int num_cu, hipStream_t st);
 // split-K factor the GEMM uses when the row count M is known on the host
 int gemm_host_split(int M, int N, int Kd, int elem_bytes, int bm);
 

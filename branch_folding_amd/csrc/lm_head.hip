@@ -94,6 +94,7 @@ hipError_t launch_lm_head(const LmHeadParams& q, int num_cu, hipStream_t st) {
   gp.A = q.An; gp.lda = q.ld_an; gp.a_rows = q.packed_slot; gp.a_rows_cap = S;
   gp.W = q.w; gp.ldw = q.d; gp.m_dev = q.count; gp.m_cap = S; gp.N = q.V; gp.Kd = q.d;
   gp.arg_val = q.arg_val; gp.arg_idx = q.arg_idx; gp.arg_ld = gemm_argmax_partials(q.V);
+  gp.w_stream = 1;     // the head is read once per call: streamed weight loads
   if ((e = launch_gemm<T>(gp, kEpiArgmax, num_cu, st)) != hipSuccess) return e;
   const int fgrid = S < 4 * num_cu ? S : 4 * num_cu;
   argmax_finish_kernel<<<fgrid, 256, 0, st>>>(q.arg_val, q.arg_idx, gp.arg_ld, q.count, S, q.V,
