@@ -453,37 +453,73 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ h,
 // by ~1e-3 rad.
 // ------------------------------------------------------------------------------------
 template <typename T>
-__global__ void __launch_bounds__(256) qkv_rope_bias_kernel(
-    T* __restrict__ qkv, long ld, const int32_t* __restrict__ count, int cap,
-    const int32_t* __restrict__ packed_slot, int B, int P, int n_q, int n_kv, int dh,
-    const T* __restrict__ bias, float theta) {
-  const int K = imin(*count, cap);
-  const int half = dh / 2, heads = n_q + 2 * n_kv;
-  const long total = (long)K * heads * half;
+__global__ void __launch_bounds__(256) qkv_reduce_rope_bias_kernel(
+    GemmParams p, const int32_t* __restrict__ packed_slot, int B, int P, int n_q, int n_kv,
+    int dh, const T* __restrict__ bias, float theta) {
+  const int K = p.m_dev ? imin(*p.m_dev, p.m_cap) : p.m_cap;
+  if (K <= 0) return;
+  // the split the GEMM ran with, derived as its own reduction derives it
+  const int kiters = p.Kd / (kGemmBKBytes / (int)sizeof(T));
+  const int split = gemm_split(ceil_div(K, gemm_bm(p, K)) * ceil_div(p.N, kGemmTileN), kiters);
+  // one thread per (packed row, head, 4 consecutive j < dh/2): columns j..j+3 and their
+  // rotation partners j+dh/2..j+dh/2+3
+  const int half = dh / 2, q4 = half / 4, heads = n_q + 2 * n_kv;
+  const long total = (long)K * heads * q4;
+  const size_t plane = (size_t)K * p.N;
+  T* C = (T*)p.C;
   for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (long)gridDim.x * blockDim.x) {
-    const int k = (int)(idx / (heads * half));
-    const int rem = (int)(idx - (long)k * heads * half);
-    const int hd = rem / half, j = rem - hd * half;
-    T* row = qkv + (size_t)k * ld + (size_t)hd * dh;
-    float x1 = to_f32(row[j]), x2 = to_f32(row[j + half]);
+    const int k = (int)(idx / (heads * q4));
+    const int rem = (int)(idx - (long)k * heads * q4);
+    const int hd = rem / q4, j0 = (rem - hd * q4) * 4;
+    const int c1 = hd * dh + j0, c2 = c1 + half;
+    T* row = C + (size_t)k * p.ldc;
+    float x1[4], x2[4];
+    if (split > 1) {
+      // the partial planes summed in split order, as the plain reduction sums them
+      const float* pr = p.partial + (size_t)k * p.N;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      for (int sp = 0; sp < split; ++sp) {
+        const float4 u = *reinterpret_cast<const float4*>(pr + (size_t)sp * plane + c1);
+        const float4 v = *reinterpret_cast<const float4*>(pr + (size_t)sp * plane + c2);
+        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+        b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+      }
+      x1[0] = a.x; x1[1] = a.y; x1[2] = a.z; x1[3] = a.w;
+      x2[0] = b.x; x2[1] = b.y; x2[2] = b.z; x2[3] = b.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x1[e] = to_f32(row[c1 + e]);
+        x2[e] = to_f32(row[c2 + e]);
+      }
+    }
     if (bias) {
-      x1 += to_f32(bias[hd * dh + j]);
-      x2 += to_f32(bias[hd * dh + j + half]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x1[e] += to_f32(bias[c1 + e]);
+        x2[e] += to_f32(bias[c2 + e]);
+      }
     }
     if (theta > 0.f && hd < n_q + n_kv) {
-      const int ps = imin(imax(packed_slot[k], 0), cap - 1);
+      const int ps = imin(imax(packed_slot[k], 0), p.m_cap - 1);
       const double pos = (double)(P + ps % B);
-      const double ang = pos * pow((double)theta, -2.0 * j / dh);
-      double sn, cs;
-      sincos(ang, &sn, &cs);
-      const float c = (float)cs, s = (float)sn;
-      const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
-      x1 = y1;
-      x2 = y2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double ang = pos * pow((double)theta, -2.0 * (j0 + e) / dh);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        const float c = (float)cs, sv = (float)sn;
+        const float y1 = x1[e] * c - x2[e] * sv, y2 = x2[e] * c + x1[e] * sv;
+        x1[e] = y1;
+        x2[e] = y2;
+      }
     }
-    row[j] = from_f32<T>(x1);
-    row[j + half] = from_f32<T>(x2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      row[c1 + e] = from_f32<T>(x1[e]);
+      row[c2 + e] = from_f32<T>(x2[e]);
+    }
   }
 }
 
@@ -589,21 +625,21 @@ hipError_t launch_combine(const void* h, const void* F, const int32_t* slot_row,
 }
 
 template <typename T>
-hipError_t launch_qkv_rope_bias(void* qkv, long ld, const int32_t* count, int cap,
-                                const int32_t* packed_slot, int B, int P, int n_q, int n_kv,
-                                int dh, const void* bias, float theta, hipStream_t st) {
-  const long total = (long)cap * (n_q + 2 * n_kv) * (dh / 2);
+hipError_t launch_qkv_reduce_rope_bias(const GemmParams& gp, const int32_t* packed_slot, int B,
+                                       int P, int n_q, int n_kv, int dh, const void* bias,
+                                       float theta, hipStream_t st) {
+  const long total = (long)gp.m_cap * (n_q + 2 * n_kv) * (dh / 8);
   const long blocks = (total + 255) / 256;
-  qkv_rope_bias_kernel<T><<<(int)(blocks < 4096 ? blocks : 4096), 256, 0, st>>>(
-      (T*)qkv, ld, count, cap, packed_slot, B, P, n_q, n_kv, dh, (const T*)bias, theta);
+  qkv_reduce_rope_bias_kernel<T><<<(int)(blocks < 4096 ? blocks : 4096), 256, 0, st>>>(
+      gp, packed_slot, B, P, n_q, n_kv, dh, (const T*)bias, theta);
   return hipGetLastError();
 }
-template hipError_t launch_qkv_rope_bias<float>(void*, long, const int32_t*, int, const int32_t*,
-                                                int, int, int, int, int, const void*, float,
-                                                hipStream_t);
-template hipError_t launch_qkv_rope_bias<bf16>(void*, long, const int32_t*, int, const int32_t*,
-                                               int, int, int, int, int, const void*, float,
-                                               hipStream_t);
+template hipError_t launch_qkv_reduce_rope_bias<float>(const GemmParams&, const int32_t*, int,
+                                                       int, int, int, int, const void*, float,
+                                                       hipStream_t);
+template hipError_t launch_qkv_reduce_rope_bias<bf16>(const GemmParams&, const int32_t*, int,
+                                                      int, int, int, int, const void*, float,
+                                                      hipStream_t);
 
 template <typename T>
 hipError_t launch_oproj_finish(const float* partial, int split, const void* H, void* h, int S,

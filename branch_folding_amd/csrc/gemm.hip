@@ -354,7 +354,7 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
 
 // 128-column tiles: at one unit per CU the split-K partial planes cost more HBM traffic
 // than re-reading the (L2-resident) activation tile for twice as many column tiles.
-int gemm_tile_n(int) { return 128; }
+int gemm_tile_n(int) { return kGemmTileN; }
 
 int gemm_host_split(int M, int N, int Kd, int elem_bytes, int bm) {
   const int BN = gemm_tile_n(N);
@@ -397,7 +397,7 @@ static hipError_t launch_gemm_bn(const GemmParams& p, int num_cu, hipStream_t st
     gemm_kernel<T, EPI, BN, 128><<<num_cu, 128 * BN / 64, 0, st>>>(p);
   }
   // the reduction only runs when some row count could make the device choose split > 1
-  if (EPI != kEpiPartial && EPI != kEpiArgmax &&
+  if (EPI != kEpiPartial && EPI != kEpiArgmax && !p.defer_reduce &&
       gemm_split(ceil_div(p.N, BN), p.Kd / (kGemmBKBytes / (int)sizeof(T))) > 1) {
     const int Nout = (EPI == kEpiSwiGLU) ? p.ff : p.N;
     const long total = (long)p.m_cap * (Nout / 4);

@@ -29,13 +29,6 @@ hipError_t launch_combine_gate(const void* h, const void* F, const int32_t* slot
                                const int32_t* count, int cap, void* y, const int32_t* fold_src,
                                int N, int B, int d, float tau, float* ratio, uint8_t* recompute,
                                const void* g, float eps, void* An, int ld_an, hipStream_t st);
-// QKV bias (bias may be nullptr) and rotary embedding (theta > 0) on the K packed rows of
-// the Q|K|V buffer [cap, ld], in place; the packed row k sits at block position
-// packed_slot[k] % B, absolute position P + that.
-template <typename T>
-hipError_t launch_qkv_rope_bias(void* qkv, long ld, const int32_t* count, int cap,
-                                const int32_t* packed_slot, int B, int P, int n_q, int n_kv,
-                                int dh, const void* bias, float theta, hipStream_t st);
 size_t resolve_pack_lds_bytes(int S);
 // prefetch (may be nullptr): up to a fixed number of its bytes are read by otherwise idle
 // workgroups of the same launch, so the following kernel finds them in the memory-side cache.
@@ -93,6 +86,9 @@ struct GemmParams {
   // row tile: 128 or 256; 0 = gemm_tile_m(m_cap); kGemmTileAuto = chosen on the device from
   // the row count (gemm_bm_of)
   int bm;
+  // nonzero: the caller runs the split-K reduction itself (the QKV projection of a layer
+  // with a QKV bias or rotary embedding, launch_qkv_reduce_rope_bias); launch_gemm runs none
+  int defer_reduce;
 };
 
 constexpr int kGemmBM = 128;      // row tile of the SwiGLU slabs
@@ -131,6 +127,7 @@ __host__ __device__ inline int gemm_bm(const GemmParams& p, int M) {
 }
 
 constexpr int kGemmBKBytes = 128;
+constexpr int kGemmTileN = 128;   // columns per tile of the split-K GEMM (gemm_tile_n)
 constexpr int kGemmMaxSplit = 24;
 // Split-K keeps units >= this many k-iterations long, so a unit's fp32 partial plane stays
 // small next to the weight bytes it streams.
@@ -172,6 +169,16 @@ inline bool swiglu_single_launch(const GemmParams& p) {
 template <typename T>
 hipError_t launch_gemm(const GemmParams& p, int epi, int num_cu, hipStream_t st,
                        const KernelTimer* timer = nullptr);
+// The QKV projection's split-K reduction fused with its bias (bias may be nullptr) and
+// rotary embedding (theta > 0).  gp is the QKV GEMM's parameters, launched with
+// defer_reduce set: each of the K packed rows of the Q|K|V buffer gp.C gets the sum of the
+// GEMM's split partials (the split it chose on the device from K; with one split, the
+// GEMM's own output) plus the bias, then the Q and K heads are rotated; packed row k sits
+// at block position packed_slot[k] % B, absolute position P + that.
+template <typename T>
+hipError_t launch_qkv_reduce_rope_bias(const GemmParams& gp, const int32_t* packed_slot, int B,
+                                       int P, int n_q, int n_kv, int dh, const void* bias,
+                                       float theta, hipStream_t st);
 // the kEpiStore or kEpiArgmax GEMM kernel with streamed weights (gemm_stream.hip; no
 // reduction pass)
 template <typename T, int EPI>

@@ -286,11 +286,15 @@ specfold_status run_layer(const specfold_shape* s, const specfold_layer_weights*
   GemmParams gp{};
   gp.A = A2; gp.lda = L.ld_d; gp.a_rows = packed; gp.a_rows_cap = S; gp.W = w->w_qkv; gp.ldw = d; gp.C = QKV; gp.ldc = L.ld_qkv;
   gp.partial = gpart; gp.m_dev = count; gp.m_cap = S; gp.N = qkvd; gp.Kd = d; gp.bm = bm;
+  // with a QKV bias or rotary embedding the split-K reduction also adds the bias and rotates
+  // Q and K (one pass over the partial planes, one rounding to the model dtype)
+  const bool qkv_epilogue = w->b_qkv || s->rope_theta > 0.f;
+  gp.defer_reduce = qkv_epilogue ? 1 : 0;
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, true));
   HIP_CHECK(launch_gemm<T>(gp, kEpiStore, cus, st));
-  if (w->b_qkv || s->rope_theta > 0.f)
-    HIP_CHECK(launch_qkv_rope_bias<T>(QKV, L.ld_qkv, count, S, packed, B, s->prefix_len, nq,
-                                      nkv, dh, w->b_qkv, s->rope_theta, st));
+  if (qkv_epilogue)
+    HIP_CHECK(launch_qkv_reduce_rope_bias<T>(gp, packed, B, s->prefix_len, nq, nkv, dh,
+                                             w->b_qkv, s->rope_theta, st));
   HIP_CHECK(mark(SPECFOLD_STEP_QKV, false));
 
   AttnParams ap{};
