@@ -17,6 +17,12 @@ namespace specfold {
 // round of loads and kept in registers for the normalisation.
 // ------------------------------------------------------------------------------------
 constexpr int kGateU = 8;                    // 16-byte chunks per lane held in registers
+// Slots (one wave each) per workgroup of the gate passes: four, unless that leaves CUs
+// without a workgroup (512 slots: 256 workgroups of two instead of 128 of four; the 7B
+// layer's gate 8.2-8.5 -> 7.9-8.2 us, event probes).
+static int gate_slots_per_block(int S) {
+  return S >= 4 * kPlanCUs ? 4 : (S >= 2 * kPlanCUs ? 2 : 1);
+}
 
 // Everything of the gate after the rows are loaded: sums of squares over the chunks held in
 // registers (and, for rows longer than 64*kGateU chunks, the rest through tail_c / tail_p),
@@ -100,7 +106,7 @@ __global__ void __launch_bounds__(256) gate_kernel(const T* __restrict__ H,
   const int lane = threadIdx.x & 63;
   // the slot is wave-uniform, so its fold source comes through a scalar load, which the
   // parent row's loads wait for without waiting for the child row's vector loads
-  const int slot = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (slot >= N * B) return;
   const int n = slot / B, i = slot - n * B;
   const bool decide = (ratio != nullptr) || (recompute != nullptr);
@@ -150,7 +156,7 @@ __global__ void __launch_bounds__(256) combine_gate_kernel(
     float eps, T* __restrict__ An, int ld_an) {
   const int lane = threadIdx.x & 63;
   // wave-uniform slot: the fold source, count and packed-row indices come through scalar loads
-  const int slot = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (slot >= N * B) return;
   const int n = slot / B, i = slot - n * B;
   constexpr int VE = Pack16<T>::kElems;
@@ -562,7 +568,8 @@ hipError_t launch_gate(const void* H, const int32_t* fold_src, int N, int B, int
                        float* ratio, uint8_t* recompute, const uint8_t* rec_given,
                        const void* g, float eps, void* An, int ld_an, hipStream_t st) {
   const int S = N * B;
-  gate_kernel<T><<<ceil_div(S, 4), 256, 0, st>>>((const T*)H, fold_src, N, B, d, tau, ratio,
+  const int wpb = gate_slots_per_block(S);
+  gate_kernel<T><<<ceil_div(S, wpb), 64 * wpb, 0, st>>>((const T*)H, fold_src, N, B, d, tau, ratio,
                                                  recompute, rec_given, (const T*)g, eps,
                                                  (T*)An, ld_an);
   return hipGetLastError();
@@ -576,7 +583,8 @@ hipError_t launch_combine_gate(const void* h, const void* F, const int32_t* slot
                                int N, int B, int d, float tau, float* ratio, uint8_t* recompute,
                                const void* g, float eps, void* An, int ld_an, hipStream_t st) {
   if (!combine_gate_fits(d, (int)sizeof(T))) return hipErrorInvalidValue;
-  combine_gate_kernel<T><<<ceil_div(N * B, 4), 256, 0, st>>>(
+  const int wpb = gate_slots_per_block(N * B);
+  combine_gate_kernel<T><<<ceil_div(N * B, wpb), 64 * wpb, 0, st>>>(
       (const T*)h, (const T*)F, slot_row, count, cap, (T*)y, fold_src, N, B, d, tau, ratio,
       recompute, (const T*)g, eps, (T*)An, ld_an);
   return hipGetLastError();
